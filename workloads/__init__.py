@@ -1,0 +1,16 @@
+"""Seeded synthetic decode batches shared by the tests, the bench and the smoke check.
+
+This package only draws inputs (context lengths, block tables, Q/K/V values, poison
+fill).  It holds none of the decode method's arithmetic: no slot computation, no
+gather, no attention.  Both the HIP path and the CPU oracle consume what it makes.
+"""
+
+from .decode_batches import (  # noqa: F401
+    CONFIGS,
+    DecodeBatch,
+    build_batch,
+    make_config,
+    permute_physical_blocks,
+    poison_bits,
+    unshare_prefix_blocks,
+)
