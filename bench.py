@@ -1,0 +1,238 @@
+"""Benchmark of one PagedAttention decode step on one MI355X.
+
+A step is the whole hot path over one batch: slot mapping, cache write of every
+sequence's new token, the attention partition kernel, the log-sum-exp reduce.
+Inputs are seeded synthetic batches already resident in HBM.  The headline is the
+KV bytes the step must read (sum of context lengths x kv heads x head_dim x 2 x
+element size) per second, the same figure as a fraction of the 8 TB/s HBM peak, and
+sequences (tokens) per second.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config llama3_8b]
+                    [--partition-size 512] [--no-cpu-baseline]
+
+Prints one JSON line.  The fp64 CPU oracle is timed on a bounded sample of the same
+batch (first sequences), on one host thread, and its outputs are compared with the
+GPU's for those sequences.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "paged-attn decode KV HBM GB/s (% of peak) and tokens/s at batch×ctx, 1 GPU"
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="tokens per context partition (0: the workload's own, 512)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0,
+                    help="sequences the CPU oracle runs on (0: chosen for ~10-30 s)")
+    return ap.parse_args(argv)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
+                                   "has no multi-GPU mode (use --gpus 1)"}))
+        return 2
+
+    import torch
+    import paged_kv_cache_441_amd as pkv
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    b = make_config(args.config, device=dev)
+    spec = b.spec
+    P = args.partition_size or spec.partition_size
+    B, H, Hkv, D, BS, NB = (b.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim,
+                            spec.block_size, spec.num_blocks)
+    MB = b.max_blocks_per_seq
+    bt = torch.as_tensor(b.block_tables, device=dev)
+    cl = torch.as_tensor(b.context_lens, device=dev)
+    kc, vc = b.key_cache, b.value_cache
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    slots = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = pkv.alloc_workspace(b.query, bt, BS, P)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkv.slot_mapping(bt, cl, BS, NB, out=slots)
+        pkv.kv_cache_write(b.key, b.value, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        pkv.paged_attention_reduce(out, cl, ws, BS, MB, P)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / K
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_part = np.array([e[1].elapsed_time(e[2]) for e in events])
+    t_red = np.array([e[2].elapsed_time(e[3]) for e in events])
+    t_gpu = np.array([e[0].elapsed_time(e[3]) for e in events])
+
+    kv_bytes = b.kv_bytes()
+    tokens = int(b.context_lens.astype(np.int64).sum())
+    step_s = ms_step / 1e3
+    kv_gbs_step = kv_bytes / step_s / 1e9
+    part_ms = float(t_part.mean())
+    part_gbs = kv_bytes / (part_ms / 1e3) / 1e9
+    attn_ms = float((t_part + t_red).mean())
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs_step, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.kv_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "num_seqs": B, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": BS, "num_blocks": NB, "max_blocks_per_seq": MB,
+            "partition_size": P, "kv_dtype": spec.kv_dtype, "accumulate": "f32",
+            "out_dtype": "f32", "context": str(spec.ctx),
+            "context_sum": tokens, "context_mean": round(tokens / B, 1),
+            "context_max": int(b.context_lens.max()), "seed": spec.seed,
+        },
+        "pct_of_peak": round(100.0 * kv_gbs_step / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(B / step_s, 1),
+        "tokens_per_s_32_layers": round(B / (32 * step_s), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "attention_kv_gbs": round(kv_bytes / (attn_ms / 1e3) / 1e9, 1),
+        "kernel_ms": {
+            "slot_mapping+kv_cache_write": round(float(t_write.mean()), 5),
+            "attention_partition": round(part_ms, 5),
+            "attention_reduce": round(float(t_red.mean()), 5),
+            "step_events": round(float(t_gpu.mean()), 5),
+            "attention_partition_p10_p50_p90": [round(float(x), 5) for x in
+                                                np.percentile(t_part, [10, 50, 90])],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_partition_kernel",
+            "achieved": round(part_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "device": torch.cuda.get_device_name(dev),
+        "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "input_generation_s": round(gen_s, 2),
+    }
+
+    # ---- CPU oracle on a bounded sample, and a parity spot check -----------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_baseline(b, out, args.cpu_sample_seqs)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(b, gpu_out, n_sample):
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    B = b.num_seqs
+    n = n_sample or min(B, 64)
+    seqs = list(range(n))
+    bt = b.block_tables[:n]
+    ids = np.unique(bt[bt >= 0])
+    idx = torch.as_tensor(ids.astype(np.int64), device=b.key_cache.device)
+    kc = b.numpy_storage(b.key_cache.index_select(0, idx))
+    vc = b.numpy_storage(b.value_cache.index_select(0, idx))
+    tables = np.where(bt >= 0, np.searchsorted(ids, np.maximum(bt, 0)), -1).astype(np.int32)
+    q = b.numpy_storage(b.query)[:n]
+    k = b.numpy_storage(b.key)[:n]
+    v = b.numpy_storage(b.value)[:n]
+    ctx = b.context_lens[:n]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _, _, _, ref = oracle.decode_step(q, k, v, kc, vc, tables, ctx, b.scale, b.kv_dtype)
+        dt = time.perf_counter() - t0
+    sample_kv = int(ctx.astype(np.int64).sum()) * b.spec.num_kv_heads * b.spec.head_dim * 2 * \
+        (2 if b.kv_dtype == "bf16" else 4)
+    g = gpu_out[:n].float().cpu().numpy().astype(np.float64)
+    err = float(np.abs(g - ref).max())
+    base = {
+        "value": round(sample_kv / dt / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(n / dt, 2),
+        "seconds": round(dt, 3),
+        "cores": 1,
+        "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "host_cpus_visible": len(os.sched_getaffinity(0)),
+        "sample": f"first {n} of {B} sequences of the same batch (slot mapping, cache write "
+                  f"and fp64 attention for all {b.spec.num_heads} heads), one host thread",
+    }
+    parity = {"sequences": n, "max_abs_err_vs_oracle": err, "tolerance": 2e-3,
+              "ok": bool(err <= 2e-3)}
+    return base, parity
+
+
+if __name__ == "__main__":
+    sys.exit(main())

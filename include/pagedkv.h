@@ -1,0 +1,211 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: the PagedAttention decode step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The decode step of a batch of sequences, each with one new token:
+ *   1. pkv_slot_mapping            -- where each new token goes in the paged cache;
+ *   2. pkv_kv_cache_write          -- scatter the new tokens' K/V rows there
+ *                                     (reshape_and_cache);
+ *   3. pkv_paged_attention_decode  -- attention of each sequence's query over its
+ *                                     whole paged context, split into context
+ *                                     partitions that are merged by log-sum-exp
+ *                                     (= pkv_paged_attention_partition followed by
+ *                                     pkv_paged_attention_reduce).
+ *
+ * Cache layout (both key_cache and value_cache), row-major, no padding:
+ *     [num_blocks][block_size][num_kv_heads][head_dim]
+ * Viewed with the first two dimensions merged, every cache "slot"
+ * (= physical_block * block_size + offset) is one token's contiguous row of
+ * num_kv_heads * head_dim elements.  (Page "vllm源码剖析", section 一.2, the
+ * paragraph on why the cache is reshaped: [num_blocks, block_size, num_kv_heads,
+ * head_size] with the first two dimensions merged so that a token's data is
+ * contiguous.)
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named as device buffers are device (HBM) addresses owned by the
+ *    caller; the library never allocates, frees or retains them and keeps no
+ *    global state.  All entry points are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    only enqueued on it; no call synchronises the host.  Ordering (write before
+ *    attention) is the caller's, by using one stream.
+ *  - Integer tensors are int32, row-major.  Element types are pkv_dtype.
+ *  - Errors come back as a pkv_status, never as an abort or exception.  Every
+ *    argument check happens before any GPU work is enqueued, so a call that
+ *    returns an error other than PKV_ERR_HIP has touched nothing.
+ *  - A sequence's context length counts its new token: the new token sits at
+ *    0-based position context_len - 1.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, inconsistent shapes */
+  PKV_ERR_UNSUPPORTED = 2,  /* a valid combination this build has no kernel for */
+  PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  PKV_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,   /* IEEE binary32 */
+  PKV_BF16 = 1   /* bfloat16 (top 16 bits of a binary32) */
+} pkv_dtype;
+
+/* PKV_ABI_VERSION of the loaded library. */
+int32_t pkv_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* pkv_status_string(int32_t status);
+
+/*
+ * pkv_slot_mapping -- slot of each sequence's new token.
+ *
+ * Defines: position pos = context_lens[i] - 1 lies in logical block
+ * pos / block_size at offset pos % block_size; the block table maps the logical
+ * block to a physical one and
+ *     slot_mapping[i] = block_tables[i][pos / block_size] * block_size + pos % block_size.
+ * (Page "vllm源码剖析", section 一.3, the worked example of a token's offset:
+ * block size 4, tokens 1-4 in block 0 and 5-8 in block 1, offset by the modulus.)
+ *
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq], physical block ids
+ *   context_lens  device int32 [num_seqs]
+ *   slot_mapping  device int32 [num_seqs], written
+ *   num_blocks    pool size; used to recognise invalid ids
+ *
+ * A sequence whose context length is outside [1, max_blocks_per_seq*block_size],
+ * or whose target block id is outside [0, num_blocks), gets slot -1 (which
+ * pkv_kv_cache_write skips).  num_seqs == 0 is a no-op.
+ * block_size must be a power of two in [1, 1024].
+ */
+pkv_status pkv_slot_mapping(const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t* slot_mapping, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t block_size,
+                            int64_t num_blocks, void* stream);
+
+/*
+ * pkv_kv_cache_write -- reshape_and_cache: store each new token's K and V rows.
+ *
+ * For every token t with 0 <= slot_mapping[t] < num_blocks*block_size:
+ *     key_cache  [slot / block_size][slot % block_size][:][:] = key  [t][:][:]
+ *     value_cache[slot / block_size][slot % block_size][:][:] = value[t][:][:]
+ * as a bit copy.  Tokens with a negative slot are padding and are skipped; slots
+ * at or past the end of the pool are skipped as well (never written).  Two tokens
+ * with the same slot are a caller error (which one lands is unspecified).
+ * (Page "vllm源码剖析", section 一.2 on the reshaped cache; page "vLLM
+ * PagedAttention 原理与源码深度解析", section 3.3, writing a token into the
+ * sequence's last block.)
+ *
+ *   key, value              device [num_tokens][num_kv_heads][head_dim], kv_dtype
+ *   key_cache, value_cache  device [num_blocks][block_size][num_kv_heads][head_dim]
+ *   slot_mapping            device int32 [num_tokens]
+ *
+ * Any head_dim with num_kv_heads*head_dim*sizeof(kv_dtype) a multiple of 16 bytes
+ * is accepted.  num_tokens == 0 is a no-op.
+ */
+pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int32_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                              void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs (0 for invalid
+ * arguments).  The workspace holds one (max, sum, partial output) record per
+ * (sequence, query head, context partition):
+ *     num_seqs * num_heads * ceil(max_blocks_per_seq*block_size / P) * (head_dim + 2) * 4
+ * bytes, P being the effective partition size.  Its contents need no
+ * initialisation and are scratch between calls.
+ */
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int32_t partition_size);
+
+/*
+ * pkv_paged_attention_decode -- one query token per sequence attends to its
+ * whole paged context.
+ *
+ * For sequence i, query head h, kv head g = h / (num_heads / num_kv_heads), and
+ * context rows k_t, v_t (t < ctx = context_lens[i]) read through the block table
+ * (row t is row t % block_size of physical block block_tables[i][t / block_size]):
+ *     s_t = scale * <q_{i,h}, k_t>,   p_t = exp(s_t - max_u s_u),
+ *     out[i][h] = sum_t p_t v_t / sum_t p_t.
+ * (Page "vllm源码分析：我是如何一步步读懂PagedAttention核心实现的？", 第三讲: the
+ * logical-to-physical block indirection, then the usual softmax and weighted
+ * sum; page "vLLM PagedAttention 原理与源码深度解析", section 5.3: gather K/V
+ * through block_tables up to context_lens, scores divided by sqrt(head_dim),
+ * softmax, weighted sum of V.  The max subtraction and the partition merge below
+ * are not printed on the pages; they leave the result unchanged.)
+ *
+ * Long contexts are split into partitions of P = partition_size tokens, each
+ * giving (m_k, l_k, o_k); the partitions are merged as
+ *     M = max m_k,  w_k = l_k exp(m_k - M),  out = sum w_k o_k / sum w_k.
+ * A sequence with a single partition is written directly.
+ *
+ *   out           device [num_seqs][num_heads][head_dim], out_dtype (written)
+ *   query         device [num_seqs][num_heads][head_dim], kv_dtype
+ *   key_cache, value_cache  device caches as above, kv_dtype
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at or past
+ *                 ceil(ctx/block_size) are never read
+ *   context_lens  device int32 [num_seqs], 1 <= ctx <= max_blocks_per_seq*block_size
+ *   scale         multiplies q.k (1/sqrt(head_dim) for standard attention)
+ *   partition_size  P in tokens; 0 selects 512; must be a multiple of block_size
+ *                 and of 16
+ *   workspace     device buffer of at least pkv_paged_attention_workspace_bytes()
+ *
+ * Supported: kv_dtype in {PKV_F32, PKV_BF16}; out_dtype in {PKV_F32, PKV_BF16}
+ * (bf16 output is the fp32 result rounded to nearest even); head_dim in {64, 128};
+ * block_size in {16, 32}; num_heads / num_kv_heads in {1, 2, 4, 8}.  Other
+ * combinations return PKV_ERR_UNSUPPORTED.  Accumulation is fp32.
+ *
+ * Device-side contract: a sequence whose context length is out of range, or that
+ * lists a block id outside [0, num_blocks) within its context, gets NaN in every
+ * element of its output rows; no memory outside the listed blocks is read.
+ * num_seqs == 0 is a no-op.
+ */
+pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, float scale, int32_t partition_size,
+                                      pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of pkv_paged_attention_decode, for callers that want to place
+ * or time them separately.  Called back to back on one stream with the same
+ * arguments and workspace they produce exactly what pkv_paged_attention_decode
+ * produces.  The partition half writes single-partition sequences to `out` and
+ * every multi-partition sequence's per-partition records to the workspace; the
+ * reduce half merges those records into `out`.
+ */
+pkv_status pkv_paged_attention_partition(void* out, const void* query, const void* key_cache,
+                                         const void* value_cache, const int32_t* block_tables,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         float scale, int32_t partition_size,
+                                         pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t partition_size,
+                                      pkv_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,18 @@
+"""PagedAttention decode on AMD MI355X (gfx950): Python binding of libpagedkv.so.
+
+The hot path (slot mapping, cache write, paged attention with a log-sum-exp
+partition merge) runs in hand-written HIP kernels behind the C ABI of
+include/pagedkv.h; this package only marshals torch tensors into that ABI.
+"""
+
+from ._lib import LIB_PATH, PkvError, load_library, status_string  # noqa: F401
+from .ops import (  # noqa: F401
+    alloc_workspace,
+    decode_step,
+    kv_cache_write,
+    paged_attention_decode,
+    paged_attention_partition,
+    paged_attention_reduce,
+    slot_mapping,
+    workspace_bytes,
+)

@@ -1,0 +1,81 @@
+"""ctypes view of libpagedkv.so (the C ABI declared in include/pagedkv.h).
+
+Loading fails loudly when the library has not been built: there is no other
+implementation to fall back on.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_WORKSPACE = 3
+PKV_ERR_HIP = 4
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes), in the order of include/pagedkv.h
+SIGNATURES = {
+    "pkv_abi_version": (_i32, []),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_slot_mapping": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp]),
+    "pkv_kv_cache_write": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz,
+                                             _vp]),
+    "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                          _sz, _vp]),
+}
+
+ABI_VERSION = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"libpagedkv.so not found at {path}; build it first with "
+                "`python -m paged_kv_cache_441_amd.build_lib` (hipcc, gfx950)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.pkv_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libpagedkv ABI {lib.pkv_abi_version()} != {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pkv_status_string(int(status)).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, what)

@@ -1,0 +1,77 @@
+// Slot mapping and the cache write (reshape_and_cache) for gfx950.
+//
+// A token at 0-based position pos of a sequence lies in logical block
+// pos / block_size at offset pos % block_size; its cache slot is
+// physical_block * block_size + offset (page "vllm源码剖析", section 一.3, the
+// worked example of a token's offset).  With the cache viewed as
+// [num_blocks * block_size][num_kv_heads][head_dim] (same page, section 一.2 on
+// the reshaped cache), a token's K (or V) for all heads is one contiguous row at
+// slot * num_kv_heads * head_dim, so the write is a row copy per token.
+#include "pkv_device.hpp"
+#include "pkv_launch.hpp"
+
+namespace pkv {
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int32_t* __restrict__ slot_mapping, int num_seqs, int max_blocks_per_seq,
+    int block_shift, int64_t num_blocks) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= num_seqs) return;
+  const int ctx = context_lens[i];
+  const int block_size = 1 << block_shift;
+  int32_t slot = -1;
+  if (ctx >= 1 && ctx <= max_blocks_per_seq * block_size) {
+    const int pos = ctx - 1;
+    const int logical = pos >> block_shift;
+    const int offset = pos & (block_size - 1);
+    const int32_t physical = block_tables[(int64_t)i * max_blocks_per_seq + logical];
+    if (physical >= 0 && (int64_t)physical < num_blocks) slot = physical * block_size + offset;
+  }
+  slot_mapping[i] = slot;
+}
+
+// One workgroup per token: copy the token's K row and V row (num_kv_heads*head_dim
+// elements each, a multiple of 16 bytes) in 16-byte pieces.
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ slot_mapping, int chunks_per_row, int64_t num_slots) {
+  const int t = blockIdx.x;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int64_t src = (int64_t)t * chunks_per_row;
+  const int64_t dst = (int64_t)slot * chunks_per_row;
+  for (int c = threadIdx.x; c < 2 * chunks_per_row; c += blockDim.x) {
+    if (c < chunks_per_row) {
+      key_cache[dst + c] = key[src + c];
+    } else {
+      value_cache[dst + c - chunks_per_row] = value[src + c - chunks_per_row];
+    }
+  }
+}
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t* slot_mapping, int num_seqs, int max_blocks_per_seq,
+                               int block_shift, int64_t num_blocks, hipStream_t stream) {
+  const int threads = 256;
+  const int grid = (num_seqs + threads - 1) / threads;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(threads), 0, stream, block_tables,
+                     context_lens, slot_mapping, num_seqs, max_blocks_per_seq, block_shift,
+                     num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int32_t* slot_mapping, int num_tokens,
+                              int row_bytes, int64_t num_slots, hipStream_t stream) {
+  const int chunks = row_bytes / 16;
+  const int threads = chunks * 2 >= 256 ? 256 : ((chunks * 2 + 63) / 64) * 64;
+  hipLaunchKernelGGL(cache_write_kernel, dim3(num_tokens), dim3(threads), 0, stream,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                     static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache),
+                     slot_mapping, chunks, num_slots);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,246 @@
+// The extern "C" surface of libpagedkv: argument checks, workspace layout and
+// kernel dispatch.  Every check runs before anything is enqueued; no entry point
+// allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.hpp"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_exact(int64_t x) {
+  int s = 0;
+  while ((int64_t{1} << s) < x) ++s;
+  return s;
+}
+
+size_t elem_bytes(pkv_dtype t) { return t == PKV_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t t) { return t == PKV_F32 || t == PKV_BF16; }
+
+// Multiplication of non-negative sizes with an overflow check against a limit.
+bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > limit / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct AttnShape {
+  int64_t max_parts = 0;
+  int partition = 0;
+  size_t ws_bytes = 0;
+};
+
+// Shape checks common to every attention entry point; fills the derived sizes.
+pkv_status check_attention_shape(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq,
+                                 int32_t partition_size, AttnShape* s) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || partition_size < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
+  const int P = partition_size == 0 ? 512 : partition_size;
+  if (P % block_size != 0 || P % 16 != 0) return PKV_ERR_INVALID_ARG;
+  int64_t max_ctx = 0;
+  if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX, &max_ctx)) return PKV_ERR_INVALID_ARG;
+  s->partition = P;
+  s->max_parts = (max_ctx + P - 1) / P;
+  int64_t recs = 0, t = 0;
+  if (!mul_ok(num_seqs, num_heads, INT64_MAX / 8, &t) || !mul_ok(t, s->max_parts, INT64_MAX / 8, &recs))
+    return PKV_ERR_INVALID_ARG;
+  int64_t bytes = 0;
+  if (!mul_ok(recs, int64_t{head_dim} + 2, INT64_MAX / 8, &bytes)) return PKV_ERR_INVALID_ARG;
+  s->ws_bytes = static_cast<size_t>(bytes) * 4;
+  return PKV_OK;
+}
+
+pkv_status fill_attention_args(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                               int32_t partition_size, int32_t kv_dtype, int32_t out_dtype,
+                               void* workspace, size_t workspace_bytes, bool need_inputs,
+                               pkv::AttentionArgs* a) {
+  AttnShape s;
+  pkv_status st = check_attention_shape(num_seqs, num_heads, head_dim, block_size,
+                                        max_blocks_per_seq, partition_size, &s);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_INVALID_ARG;
+  if (need_inputs) {
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+    if (num_blocks <= 0 || !std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+    int64_t pool = 0;
+    if (!mul_ok(num_blocks, block_size, INT64_MAX / 4096, &pool) ||
+        !mul_ok(pool, int64_t{num_kv_heads} * head_dim, INT64_MAX / 8, &pool))
+      return PKV_ERR_INVALID_ARG;
+  }
+  if (num_seqs > 0) {
+    if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
+    if (need_inputs && (!query || !key_cache || !value_cache || !block_tables))
+      return PKV_ERR_INVALID_ARG;
+  }
+  if (need_inputs) {
+    const int G = num_heads / num_kv_heads;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PKV_ERR_UNSUPPORTED;
+  }
+  if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
+  if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (!workspace || workspace_bytes < s.ws_bytes)) return PKV_ERR_WORKSPACE;
+  if (s.max_parts * num_seqs * int64_t{num_kv_heads > 0 ? num_kv_heads : 1} > INT32_MAX)
+    return PKV_ERR_UNSUPPORTED;   // grid larger than one launch can hold
+
+  a->out = out;
+  a->query = query;
+  a->key_cache = key_cache;
+  a->value_cache = value_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->num_seqs = num_seqs;
+  a->num_heads = num_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->block_shift = log2_exact(block_size);
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->num_blocks = num_blocks;
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  a->partition_size = s.partition;
+  a->max_parts = static_cast<int>(s.max_parts);
+  a->kv_bf16 = kv_dtype == PKV_BF16;
+  a->out_bf16 = out_dtype == PKV_BF16;
+  const int64_t recs = int64_t{num_seqs} * num_heads * s.max_parts;
+  float* ws = static_cast<float*>(workspace);
+  a->ws_m = ws;
+  a->ws_l = ws ? ws + recs : nullptr;
+  a->ws_o = ws ? ws + 2 * recs : nullptr;
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or shape)";
+    case PKV_ERR_UNSUPPORTED: return "unsupported combination (head_dim, block_size, GQA group or dtype)";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+pkv_status pkv_slot_mapping(const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t* slot_mapping, int32_t num_seqs, int32_t max_blocks_per_seq,
+                            int32_t block_size, int64_t num_blocks, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
+  int64_t t = 0;
+  if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX, &t) ||
+      !mul_ok(num_blocks, block_size, INT32_MAX, &t))
+    return PKV_ERR_INVALID_ARG;   // slots are int32
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  return hip_status(pkv::launch_slot_mapping(block_tables, context_lens, slot_mapping, num_seqs,
+                                             max_blocks_per_seq, log2_exact(block_size),
+                                             num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, pkv_dtype kv_dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  int64_t row = 0, slots = 0;
+  if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row))
+    return PKV_ERR_INVALID_ARG;
+  if (!mul_ok(num_blocks, block_size, INT64_MAX / 4096, &slots)) return PKV_ERR_INVALID_ARG;
+  int64_t cache_bytes = 0;
+  if (!mul_ok(slots, row, INT64_MAX / 2, &cache_bytes)) return PKV_ERR_INVALID_ARG;
+  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  return hip_status(pkv::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
+                                            num_tokens, static_cast<int>(row), slots,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int32_t partition_size) {
+  AttnShape s;
+  if (check_attention_shape(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq,
+                            partition_size, &s) != PKV_OK)
+    return 0;
+  return s.ws_bytes;
+}
+
+pkv_status pkv_paged_attention_partition(void* out, const void* query, const void* key_cache,
+                                         const void* value_cache, const int32_t* block_tables,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         float scale, int32_t partition_size,
+                                         pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::AttentionArgs a;
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      partition_size, kv_dtype, out_dtype, workspace,
+                                      workspace_bytes, true, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return hip_status(pkv::launch_attention_partition(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t partition_size,
+                                      pkv_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  pkv::AttentionArgs a;
+  pkv_status st = fill_attention_args(out, nullptr, nullptr, nullptr, nullptr, context_lens,
+                                      num_seqs, num_heads, 0, head_dim, block_size,
+                                      max_blocks_per_seq, 0, 1.0f, partition_size, PKV_F32,
+                                      out_dtype, workspace, workspace_bytes, false, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return hip_status(pkv::launch_attention_reduce(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, float scale, int32_t partition_size,
+                                      pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  pkv::AttentionArgs a;
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      partition_size, kv_dtype, out_dtype, workspace,
+                                      workspace_bytes, true, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_attention_partition(a, s));
+  if (st != PKV_OK) return st;
+  if (a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));
+  return st;
+}
+
+}  // extern "C"

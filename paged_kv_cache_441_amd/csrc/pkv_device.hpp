@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedkv: element types,
+// bfloat16 conversion, wave64 DPP reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Storage tags.  A 16-byte "chunk" is the unit every lane loads.
+struct F32 {
+  using storage = float;
+  static constexpr int kElemBytes = 4;
+  static constexpr int kPerChunk = 4;
+};
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int kElemBytes = 2;
+  static constexpr int kPerChunk = 8;
+};
+
+// bfloat16 -> fp32 is exact: the 16 bits are the top half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Unpack one 16-byte chunk into fp32 values.
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(const uint4& c, float* v);
+
+template <>
+__device__ __forceinline__ void unpack_chunk<F32>(const uint4& c, float* v) {
+  v[0] = __uint_as_float(c.x);
+  v[1] = __uint_as_float(c.y);
+  v[2] = __uint_as_float(c.z);
+  v[3] = __uint_as_float(c.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack_chunk<BF16>(const uint4& c, float* v) {
+  v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+  v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+  v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+  v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+}
+
+// ---- DPP within one 16-lane row of a wave64 -------------------------------------
+// Control codes of the gfx9 data-parallel-primitive lane selectors.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;   // lane r <- lane 15-r
+constexpr int kDppRowHalfMirror = 0x141;  // lane r <- lane 7-r within each half-row
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// After these four steps every lane of a 16-lane row holds the row's result.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppRowMirror>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+__device__ __forceinline__ float readlane(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

@@ -1,0 +1,200 @@
+"""Torch-facing wrappers over the libpagedkv C ABI.
+
+Argument marshalling only: each function checks dtype, device and contiguity,
+passes raw device pointers, sizes and the current HIP stream of the tensors'
+device, and raises ``PkvError`` on a non-OK status.  All computation happens in
+the library's kernels; tensors must already live on the GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_KV_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    _dev(t, name)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32 (got {t.dtype})")
+
+
+def _kv(t: torch.Tensor, name: str) -> int:
+    _dev(t, name)
+    if t.dtype not in _KV_DTYPES:
+        raise TypeError(f"{name} must be float32 or bfloat16 (got {t.dtype})")
+    return _KV_DTYPES[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {devs}")
+
+
+def slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                 num_blocks: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Slot of each sequence's new token (position context_len - 1); -1 if invalid."""
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    B = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=context_lens.device)
+    _i32(out, "out")
+    _same_device(block_tables, context_lens, out)
+    lib = _lib.load_library()
+    st = lib.pkv_slot_mapping(_ptr(block_tables), _ptr(context_lens), _ptr(out), B,
+                              block_tables.shape[1], int(block_size), int(num_blocks),
+                              _stream(out))
+    _lib.check(st, "pkv_slot_mapping")
+    return out
+
+
+def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """reshape_and_cache: copy each token's K/V row into its slot of the paged caches."""
+    dt = _kv(key, "key")
+    for t, n in ((value, "value"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        if _kv(t, n) != dt:
+            raise TypeError(f"{n} dtype differs from key")
+    _i32(slot_mapping, "slot_mapping")
+    _same_device(key, value, key_cache, value_cache, slot_mapping)
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("caches must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    NB, BS, Hkv, D = key_cache.shape
+    T = slot_mapping.shape[0]
+    if key.shape != (T, Hkv, D) or value.shape != (T, Hkv, D):
+        raise ValueError(f"key/value must be [{T}, {Hkv}, {D}]")
+    lib = _lib.load_library()
+    st = lib.pkv_kv_cache_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                _ptr(slot_mapping), T, Hkv, D, BS, NB, dt, _stream(key))
+    _lib.check(st, "pkv_kv_cache_write")
+
+
+def workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, block_size: int,
+                    max_blocks_per_seq: int, partition_size: int = 0) -> int:
+    return int(_lib.load_library().pkv_paged_attention_workspace_bytes(
+        num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, partition_size))
+
+
+def alloc_workspace(query: torch.Tensor, block_tables: torch.Tensor, block_size: int,
+                    partition_size: int = 0) -> torch.Tensor:
+    B, H, D = query.shape
+    n = workspace_bytes(B, H, D, block_size, block_tables.shape[1], partition_size)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=query.device)
+
+
+def _attention_args(query, key_cache, value_cache, block_tables, context_lens, out, out_dtype,
+                    workspace, partition_size):
+    dt = _kv(query, "query")
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        if _kv(t, n) != dt:
+            raise TypeError(f"{n} dtype differs from query")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if query.dim() != 3 or key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("query [B, H, D]; caches [NB, BS, Hkv, D]")
+    B, H, D = query.shape
+    NB, BS, Hkv, Dk = key_cache.shape
+    if Dk != D or context_lens.shape != (B,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype, device=query.device)
+    if out.dtype not in _KV_DTYPES or out.shape != (B, H, D):
+        raise ValueError("out must be float32/bfloat16 [B, H, D]")
+    _dev(out, "out")
+    if workspace is None:
+        workspace = alloc_workspace(query, block_tables, BS, partition_size)
+    _dev(workspace, "workspace")
+    _same_device(query, key_cache, value_cache, block_tables, context_lens, out, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return (dt, out, workspace, ws_bytes, B, H, Hkv, D, BS, NB)
+
+
+def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                           out_dtype: torch.dtype = torch.float32,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of one query per sequence over its paged context."""
+    dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
+        partition_size)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
+    _lib.check(st, "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_partition(query, key_cache, value_cache, block_tables, context_lens, scale,
+                              partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
+    """First half of paged_attention_decode (see the header); returns (out, workspace)."""
+    dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
+        partition_size)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_partition(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
+    _lib.check(st, "pkv_paged_attention_partition")
+    return out, ws
+
+
+def paged_attention_reduce(out: torch.Tensor, context_lens: torch.Tensor, workspace: torch.Tensor,
+                           block_size: int, max_blocks_per_seq: int,
+                           partition_size: int = 0) -> torch.Tensor:
+    """Second half of paged_attention_decode: merge the partition records into ``out``."""
+    _dev(out, "out")
+    _i32(context_lens, "context_lens")
+    _dev(workspace, "workspace")
+    if out.dtype not in _KV_DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    B, H, D = out.shape
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_reduce(
+        _ptr(out), _ptr(context_lens), B, H, D, int(block_size), int(max_blocks_per_seq),
+        int(partition_size), _KV_DTYPES[out.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(out))
+    _lib.check(st, "pkv_paged_attention_reduce")
+    return out
+
+
+def decode_step(query, key, value, key_cache, value_cache, block_tables, context_lens, scale,
+                partition_size=0, out=None, out_dtype=torch.float32, workspace=None,
+                slots=None):
+    """One decode step on the GPU: slot mapping, cache write, paged attention."""
+    NB, BS = key_cache.shape[0], key_cache.shape[1]
+    slots = slot_mapping(block_tables, context_lens, BS, NB, out=slots)
+    kv_cache_write(key, value, key_cache, value_cache, slots)
+    return paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
+                                  partition_size, out=out, out_dtype=out_dtype,
+                                  workspace=workspace)

@@ -1,0 +1,203 @@
+"""GPU parity of the HIP path against the CPU fp64 oracle (run on an MI355X).
+
+Cache write and slot mapping: bit-exact.  Attention: max |GPU - oracle| <= 2e-3
+with fp32 accumulation and fp32 output; bf16 output is the fp32 result rounded to
+nearest even.  Invariances (block relabelling, prefix sharing, repeated runs) are
+bitwise, since no reduction order depends on timing or on physical placement.
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_441_amd as pkv
+from gpu_helpers import (ATOL, bits, check_cache_write, device_meta, max_err, oracle_outputs,
+                         require_gpu, run_step)
+from workloads import (CONFIGS, build_batch, make_config, permute_physical_blocks,
+                       unshare_prefix_blocks)
+from workloads.decode_batches import ConfigSpec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+_cache = {}
+
+
+def config_batch(name):
+    if name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        _cache[name] = make_config(name, device="cuda")
+    return _cache[name]
+
+
+def spec_of(D=128, G=4, Hkv=2, BS=16, dtype="bf16", NB=4096, seed=5):
+    return ConfigSpec("custom", 1, G * Hkv, Hkv, D, BS, NB, dtype, 1, ("fixed", (1,)), seed)
+
+
+# ----------------------------------------------------------------------------
+# slot mapping and cache write: bit-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_slot_mapping_and_cache_write_exact(name):
+    b = config_batch(name)
+    slots, kc, vc, _ = run_step(b)
+    ref = oracle.slot_mapping(b.block_tables, b.context_lens, b.spec.block_size)
+    assert (slots.cpu().numpy().astype(np.int64) == ref).all()
+    check_cache_write(b, kc, vc, ref)
+
+
+def test_cache_write_skips_padding_and_out_of_pool_slots():
+    b = build_batch(spec_of(NB=64), [5, 20, 33], device="cuda")
+    kc, vc = b.key_cache.clone(), b.value_cache.clone()
+    NB, BS = kc.shape[:2]
+    slots = torch.tensor([-1, NB * BS, 7], dtype=torch.int32, device="cuda")
+    pkv.kv_cache_write(b.key, b.value, kc, vc, slots)
+    torch.cuda.synchronize()
+    # only slot 7 may change, and it must hold token 2's rows
+    for new, old, src in ((kc, b.key_cache, b.key), (vc, b.value_cache, b.value)):
+        nb, ob = bits(new).reshape(NB * BS, -1), bits(old).reshape(NB * BS, -1)
+        assert (nb != ob).any(dim=1).nonzero().flatten().tolist() == [7]
+        assert torch.equal(nb[7], bits(src[2]).reshape(-1))
+
+
+def test_slot_mapping_invalid_inputs_give_minus_one():
+    bt = torch.tensor([[3, 4], [5, -1], [7, 9], [1, 2]], dtype=torch.int32, device="cuda")
+    cl = torch.tensor([0, 17, 33, 20], dtype=torch.int32, device="cuda")
+    # ctx 0 (invalid), ctx 17 lands in block -1 (invalid), ctx 33 > 2*16 (invalid)
+    s = pkv.slot_mapping(bt, cl, 16, 8).cpu().tolist()
+    assert s[:3] == [-1, -1, -1]
+    assert s[3] == 2 * 16 + 3
+    s = pkv.slot_mapping(bt, torch.tensor([1, 1, 17, 20], dtype=torch.int32, device="cuda"), 16, 8)
+    assert s.cpu().tolist() == [3 * 16, 5 * 16, -1, 2 * 16 + 3]      # block 9 >= pool of 8
+
+
+# ----------------------------------------------------------------------------
+# attention vs the oracle on the named workloads
+# ----------------------------------------------------------------------------
+
+SAMPLES = {
+    "tiny": None,
+    "llama2_7b": None,
+    "llama3_8b": "sample",
+    "long_ctx": [0, 3, 7],
+    "prefix_shared": None,
+}
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_attention_matches_oracle(name):
+    b = config_batch(name)
+    seqs = SAMPLES[name]
+    if seqs == "sample":
+        order = np.argsort(b.context_lens)
+        seqs = sorted(set(order[:4].tolist() + order[-4:].tolist() + list(range(0, b.num_seqs, 37))))
+    _, _, _, out = run_step(b, partition_size=b.spec.partition_size)
+    ref = oracle_outputs(b, seqs)
+    err = max_err(out, ref, seqs)
+    print(f"{name}: max |gpu - oracle| = {err:.3e} over {len(ref)} sequences")
+    assert np.isfinite(out.cpu().numpy()).all()
+    assert err <= ATOL
+
+
+BOUNDARY = [1, 15, 16, 17, 511, 512, 513, 1024, 8192]
+
+
+@pytest.mark.parametrize("D,G,BS,dtype", [
+    (128, 4, 16, "bf16"), (128, 1, 16, "bf16"), (128, 2, 32, "bf16"), (128, 8, 16, "bf16"),
+    (64, 4, 32, "bf16"), (64, 1, 16, "f32"), (128, 4, 16, "f32"), (64, 8, 32, "f32"),
+])
+def test_boundary_contexts(D, G, BS, dtype):
+    b = build_batch(spec_of(D=D, G=G, BS=BS, dtype=dtype, NB=2048), BOUNDARY, device="cuda")
+    for P in (512, 64):
+        _, _, _, out = run_step(b, partition_size=P)
+        ref = oracle_outputs(b)
+        err = max_err(out, ref)
+        print(f"D={D} G={G} BS={BS} {dtype} P={P}: max err {err:.3e}")
+        assert err <= ATOL
+
+
+def test_partitioned_equals_single_partition():
+    b = build_batch(spec_of(NB=4096), [1, 100, 600, 1500, 5000, 9000], device="cuda")
+    MB = b.max_blocks_per_seq
+    _, _, _, single = run_step(b, partition_size=MB * 16)
+    _, _, _, split = run_step(b, partition_size=512)
+    _, _, _, fine = run_step(b, partition_size=16)
+    ref = oracle_outputs(b)
+    for o in (single, split, fine):
+        assert max_err(o, ref) <= ATOL
+    assert (single - split).abs().max().item() <= 2e-5
+    assert (single - fine).abs().max().item() <= 2e-5
+
+
+# ----------------------------------------------------------------------------
+# bitwise invariances
+# ----------------------------------------------------------------------------
+
+def test_block_permutation_invariance_bitwise():
+    b = build_batch(spec_of(NB=1024), [1, 33, 700, 1200, 3000], device="cuda")
+    perm = np.random.default_rng(0).permutation(1024)
+    pb = permute_physical_blocks(b, perm)
+    o1 = run_step(b)[3]
+    o2 = run_step(pb)[3]
+    assert torch.equal(bits(o1), bits(o2))
+
+
+def test_prefix_sharing_equals_private_copies_bitwise():
+    b = config_batch("prefix_shared")
+    u = unshare_prefix_blocks(b)
+    o1 = run_step(b)[3]
+    o2 = run_step(u)[3]
+    assert torch.equal(bits(o1), bits(o2))
+
+
+def test_run_to_run_determinism():
+    b = build_batch(spec_of(NB=4096), [17, 900, 4000, 8192, 2], device="cuda")
+    outs = [run_step(b)[3] for _ in range(3)]
+    assert torch.equal(bits(outs[0]), bits(outs[1])) and torch.equal(bits(outs[0]), bits(outs[2]))
+
+
+# ----------------------------------------------------------------------------
+# output dtype, split entry points, invalid device data
+# ----------------------------------------------------------------------------
+
+def test_bf16_output_is_rounded_fp32_result():
+    b = build_batch(spec_of(NB=1024), [1, 40, 700, 2000], device="cuda")
+    o32 = run_step(b)[3]
+    o16 = run_step(b, out_dtype=torch.bfloat16)[3]
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(bits(o16), bits(o32.to(torch.bfloat16)))
+
+
+def test_partition_then_reduce_equals_decode():
+    b = build_batch(spec_of(NB=2048), [3, 513, 2000, 5000], device="cuda")
+    slots, kc, vc, out = run_step(b)
+    bt, cl = device_meta(b)
+    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512)
+    pkv.paged_attention_reduce(out2, cl, ws, 16, bt.shape[1], 512)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(out2))
+
+
+def test_invalid_device_data_gives_nan_rows_only():
+    b = build_batch(spec_of(NB=1024), [20, 300, 40, 700], device="cuda")
+    slots, kc, vc, good = run_step(b, partition_size=128)
+    bt, cl = device_meta(b)
+    bt_bad = bt.clone()
+    bt_bad[1, 3] = 5000            # out of the pool, inside sequence 1's context
+    cl_bad = cl.clone()
+    cl_bad[2] = 0                  # empty context
+    out = pkv.paged_attention_decode(b.query, kc, vc, bt_bad, cl_bad, b.scale, 128)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
+    assert torch.equal(bits(o[[0, 3]]), bits(good.cpu()[[0, 3]]))

@@ -224,7 +224,8 @@ def build_batch(spec: ConfigSpec, context_lens: Sequence[int], device="cpu",
     seed = spec.seed if seed is None else seed
     ctx = np.asarray(context_lens, dtype=np.int32)
     assert ctx.ndim == 1 and (ctx >= 1).all()
-    spec = replace(spec, num_seqs=int(ctx.shape[0]))
+    spec = replace(spec, num_seqs=int(ctx.shape[0]),
+                   max_context=max(spec.max_context, int(ctx.max())))
     if block_tables is None:
         block_tables = deal_block_tables(spec, ctx, seed, max_blocks_per_seq)
     B, H, Hkv, D = spec.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim
