@@ -119,11 +119,13 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs (0 for invalid
- * arguments).  The workspace holds one (max, sum, partial output) record per
- * (sequence, query head, context partition):
- *     num_seqs * num_heads * ceil(max_blocks_per_seq*block_size / P) * (head_dim + 2) * 4
- * bytes, P being the effective partition size.  Its contents need no
- * initialisation and are scratch between calls.
+ * arguments).  With P the effective partition size and
+ * NP = ceil(max_blocks_per_seq*block_size / P), the workspace holds
+ *   - the work plan: 256 bytes, then one 16-byte item per (sequence, partition),
+ *     rounded up to 256 bytes:  256 + roundup256(num_seqs * NP * 16);
+ *   - one (max, sum, partial output) fp32 record per (sequence, query head,
+ *     partition):  num_seqs * num_heads * NP * (head_dim + 2) * 4.
+ * Its contents need no initialisation and are scratch between calls.
  */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                            int32_t head_dim, int32_t block_size,
@@ -181,13 +183,34 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
                                       size_t workspace_bytes, void* stream);
 
 /*
- * The two halves of pkv_paged_attention_decode, for callers that want to place
- * or time them separately.  Called back to back on one stream with the same
- * arguments and workspace they produce exactly what pkv_paged_attention_decode
- * produces.  The partition half writes single-partition sequences to `out` and
- * every multi-partition sequence's per-partition records to the workspace; the
- * reduce half merges those records into `out`.
+ * The three stages of pkv_paged_attention_decode, for callers that want to place,
+ * reuse or time them separately.  Called in this order on one stream with the
+ * same arguments and workspace they produce exactly what
+ * pkv_paged_attention_decode produces.
+ *
+ * pkv_paged_attention_plan writes the work list into the start of the workspace:
+ * one item per (sequence, partition) that holds tokens -- whole partitions
+ * first, then the partial last partitions from largest to smallest -- so that
+ * the partition stage hands the longest work out first.  It reads only
+ * context_lens; a plan stays valid for as long as context_lens, block_size,
+ * max_blocks_per_seq, partition_size and num_seqs are unchanged (for example for
+ * every layer of one decode step).  It needs workspace_bytes of at least the
+ * plan part described above.
+ *
+ * pkv_paged_attention_partition runs the planned work: it writes single-partition
+ * sequences straight to `out` and every multi-partition sequence's per-partition
+ * records to the workspace.  It checks the plan's items against num_seqs and the
+ * partition count, so a stale plan yields wrong numbers, never an access outside
+ * the buffers.
+ *
+ * pkv_paged_attention_reduce merges the partition records of multi-partition
+ * sequences into `out`, in partition order.
  */
+pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 pkv_status pkv_paged_attention_partition(void* out, const void* query, const void* key_cache,
                                          const void* value_cache, const int32_t* block_tables,
                                          const int32_t* context_lens, int32_t num_seqs,

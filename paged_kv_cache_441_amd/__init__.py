@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     kv_cache_write,
     paged_attention_decode,
     paged_attention_partition,
+    paged_attention_plan,
     paged_attention_reduce,
     slot_mapping,
     workspace_bytes,

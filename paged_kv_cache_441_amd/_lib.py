@@ -33,6 +33,7 @@ SIGNATURES = {
     "pkv_paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_plan": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_paged_attention_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz,
                                              _vp]),

@@ -99,9 +99,97 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool 
   else
     static_cast<float*>(out)[idx] = v;
 }
+// Build-time tuning knob (default: the measured best on MI355X).
+#ifndef PKV_WAVES_PER_EU
+#define PKV_WAVES_PER_EU 1         // occupancy floor handed to the register allocator
+#endif
 
-template <typename T, int D, int G, int TPG>
-__global__ __launch_bounds__(256) void paged_attention_partition_kernel(AttentionArgs a) {
+size_t plan_bytes(int64_t num_seqs, int64_t max_parts) {
+  return 256 + ((size_t)(num_seqs * max_parts) * sizeof(int4) + 255) / 256 * 256;
+}
+
+// ---- work plan -------------------------------------------------------------------
+// The partition kernel's grid is sized for the longest context the block tables
+// allow, so most of its workgroups may find nothing to do, and the hardware hands
+// out workgroups in index order.  The plan lists the real (sequence, partition)
+// work items so that workgroup k takes item k / num_kv_heads: every whole
+// partition first, then the partial last partitions, longest first (eight size
+// classes), then nothing.  Dispatching the longest items first keeps the end of
+// the kernel from waiting on a few long ones, and the idle workgroups all sit at
+// the end of the grid where they cost almost nothing.  A sequence with an invalid
+// context length gets one item, whose workgroups write its NaN output.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanClasses = 8;
+
+// Exclusive prefix sum over the workgroup; *total receives the sum.
+__device__ __forceinline__ int plan_scan(int x, int* lds, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int v = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == kWave - 1) lds[wave] = v;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / kWave; ++w) {
+    const int t = lds[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + v - x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void paged_attention_plan_kernel(AttentionArgs a) {
+  __shared__ int lds[kPlanThreads / kWave];
+  const int P = a.partition_size;
+  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+  int offset = 0;
+  // whole partitions (and the single item of an invalid sequence)
+  for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+    const int i = c0 + threadIdx.x;
+    const int ctx = i < a.num_seqs ? a.context_lens[i] : 0;
+    const bool valid = ctx >= 1 && ctx <= max_ctx;
+    const int n = i >= a.num_seqs ? 0 : (valid ? ctx / P : 1);
+    const int nparts = valid ? (ctx + P - 1) / P : 1;
+    int total;
+    const int pos = offset + plan_scan(n, lds, &total);
+    for (int p = 0; p < n; ++p) a.plan_items[pos + p] = make_int4(i, p, ctx, nparts);
+    offset += total;
+  }
+  // partial last partitions, by size class, largest first
+  for (int cls = 0; cls < kPlanClasses; ++cls) {
+    for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+      const int i = c0 + threadIdx.x;
+      const int ctx = i < a.num_seqs ? a.context_lens[i] : 0;
+      const bool valid = ctx >= 1 && ctx <= max_ctx;
+      const int rem = valid ? ctx % P : 0;
+      const int mine = rem > 0 && (int)(((int64_t)(P - rem) * kPlanClasses) / P) == cls;
+      int total;
+      const int pos = offset + plan_scan(mine, lds, &total);
+      if (mine) a.plan_items[pos] = make_int4(i, ctx / P, ctx, (ctx + P - 1) / P);
+      offset += total;
+    }
+  }
+  if (threadIdx.x == 0) *a.plan_count = offset;
+}
+
+// The loads of one 16-token tile, in flight while the previous tile is computed.
+template <int QKC, int STEPS>
+struct TileLoads {
+  uint4 k[QKC];     // key chunks in MFMA B-operand order
+  uint4 v[STEPS];   // value chunks, one per wave load of RPS rows
+  int ntok;         // live tokens of the tile; 0 = no tile (past the end, or a bad block)
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_attention_partition_kernel(AttentionArgs a) {
   using Geo = Geometry<T, D, G>;
   constexpr int EPL = Geo::kEPL;
   constexpr int NCH = Geo::kChunksPerRow;
@@ -110,22 +198,30 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
   constexpr int STEPS = Geo::kSteps;
   constexpr int EB = T::kElemBytes;
 
-  __shared__ float p_lds[4][TPG][16][G];
+  __shared__ float p_lds[4][16][G];     // per wave: probabilities of its current tile
   __shared__ float red_o[4][G][D];
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
   __shared__ int red_bad[4];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // The wave index is the same in every lane; saying so lets everything derived
+  // from it (tile numbers, block ids, block base addresses) live in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
   const int H = Hkv * G;
+  // Workgroup -> (plan item, kv head); heads vary fastest.  Items are checked so
+  // that a stale plan can give wrong numbers but never an out-of-range access.
   const int g = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int part = rest % a.max_parts;
-  const int seq = rest / a.max_parts;
+  const int idx = blockIdx.x / Hkv;
+  const int count = min(*a.plan_count, a.num_seqs * a.max_parts);
+  if (idx >= count) return;
+  const int4 item = a.plan_items[idx];
+  const int seq = item.x;
+  const int part = item.y;
+  const int ctx = item.z;
+  if (seq < 0 || seq >= a.num_seqs || part < 0 || part >= a.max_parts) return;
 
-  const int ctx = a.context_lens[seq];
   const int max_ctx = a.max_blocks_per_seq << a.block_shift;
   if (ctx < 1 || ctx > max_ctx) {
     // Invalid context length: the sequence's rows become NaN (written once).
@@ -156,9 +252,16 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
       qa[c] = col < G ? load16(qrow, (4 * c + quarter) * 16) : make_uint4(0, 0, 0, 0);
   }
 
-  const int64_t row_bytes = (int64_t)Hkv * D * EB;  // between consecutive tokens of a block
+  // Byte offsets: the block base is the same for the whole wave (a scalar), the
+  // per-lane part fits in 32 bits.
+  const uint32_t row_bytes = (uint32_t)Hkv * D * EB;   // between consecutive tokens of a block
+  const uint32_t k_lane = col * row_bytes + quarter * 16;
+  const uint32_t v_lane = rg * row_bytes + li * 16;
   const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.block_shift) - 1;
+  const int64_t head_bytes = (int64_t)g * D * EB;
+  const char* kcache = static_cast<const char*>(a.key_cache);
+  const char* vcache = static_cast<const char*>(a.value_cache);
   const float kNegInf = -__builtin_inff();
 
   float m_run[G];
@@ -174,63 +277,42 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
   for (int j = 0; j < 4; ++j) l_lane[j] = 0.f;
   int bad = 0;
 
-  for (int t0 = wave; t0 < ntiles; t0 += 4 * TPG) {
-    int64_t base[TPG];
-    int ntok[TPG];
-    bool tv[TPG];
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const int tile = t0 + 4 * i;
-      const int tok0 = p_start + 16 * tile;
-      tv[i] = tile < ntiles;
-      ntok[i] = tv[i] ? min(16, p_end - tok0) : 0;
-      int32_t blk = tv[i] ? bt_row[tok0 >> a.block_shift] : 0;
-      if (tv[i] && (blk < 0 || (int64_t)blk >= a.num_blocks)) {
-        bad = 1;
-        tv[i] = false;
-        ntok[i] = 0;
-      }
-      base[i] = (((int64_t)blk << a.block_shift) + (tok0 & bs_mask)) * row_bytes + (int64_t)g * D * EB;
-    }
+  using Loads = TileLoads<QKC, STEPS>;
 
-    uint4 kr[TPG][QKC];
-    uint4 vr[TPG][STEPS];
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      if (tv[i]) {
+  // Issue the key and value loads of tile ``tile`` (wave-uniform decisions only).
+  auto issue = [&](Loads& r, int tile) {
+    r.ntok = 0;
+    if (tile < ntiles) {
+      const int tok0 = p_start + 16 * tile;
+      const int32_t blk = bt_row[tok0 >> a.block_shift];
+      if (blk < 0 || (int64_t)blk >= a.num_blocks) {
+        bad = 1;
+      } else {
+        r.ntok = min(16, p_end - tok0);
+        const int64_t off = (((int64_t)blk << a.block_shift) + (tok0 & bs_mask)) * row_bytes +
+                            head_bytes;
+        const char* kb = kcache + off;
+        const char* vb = vcache + off;
 #pragma unroll
         for (int c = 0; c < QKC; ++c)
-          kr[i][c] = load16(a.key_cache, base[i] + col * row_bytes + (4 * c + quarter) * 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      if (tv[i]) {
+          r.k[c] = *reinterpret_cast<const uint4*>(kb + k_lane + c * 64);
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
-          vr[i][s] = load16(a.value_cache, base[i] + (s * RPS + rg) * row_bytes + li * 16);
+          r.v[s] = *reinterpret_cast<const uint4*>(vb + v_lane + s * RPS * row_bytes);
       }
     }
+  };
 
-    // ---- scores ---------------------------------------------------------------
-    float sc[TPG][4];
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      floatx4 r = {0.f, 0.f, 0.f, 0.f};
-      if (tv[i]) r = tile_scores<T, QKC>(qa, kr[i]);
-      const bool live = col < ntok[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[i][j] = live ? r[j] * a.scale_log2 : kNegInf;
-    }
-
-    // ---- running maximum, probabilities ---------------------------------------
-    float gmax[4];
+  // Scores, running maximum, probabilities and P.V for one loaded tile.
+  auto compute = [&](const Loads& r) {
+    if (r.ntok == 0) return;
+    const floatx4 s4 = tile_scores<T, QKC>(qa, r.k);
+    const bool live = col < r.ntok;
+    float sc[4], gmax[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float x = sc[0][j];
-#pragma unroll
-      for (int i = 1; i < TPG; ++i) x = fmaxf(x, sc[i][j]);
-      gmax[j] = row16_max(x);
+      sc[j] = live ? s4[j] * a.scale_log2 : kNegInf;
+      gmax[j] = row16_max(sc[j]);
     }
     float alpha[G];
     bool rescale = false;
@@ -242,26 +324,18 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
       rescale |= m_run[h] != mn;
       m_run[h] = mn;
     }
-    float mrow[4], arow[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      float mrow, arow;
       if constexpr (G <= 4) {
-        mrow[j] = j < G ? m_run[j < G ? j : 0] : 0.f;
-        arow[j] = j < G ? alpha[j < G ? j : 0] : 1.f;
+        mrow = j < G ? m_run[j < G ? j : 0] : 0.f;
+        arow = j < G ? alpha[j < G ? j : 0] : 1.f;
       } else {
-        mrow[j] = quarter == 0 ? m_run[j] : m_run[(4 + j) % G];
-        arow[j] = quarter == 0 ? alpha[j] : alpha[(4 + j) % G];
+        mrow = quarter == 0 ? m_run[j] : m_run[(4 + j) % G];
+        arow = quarter == 0 ? alpha[j] : alpha[(4 + j) % G];
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        sc[i][j] = fast_exp2(sc[i][j] - mrow[j]);
-        lsum += sc[i][j];
-      }
-      l_lane[j] = l_lane[j] * arow[j] + lsum;
+      sc[j] = fast_exp2(sc[j] - mrow);
+      l_lane[j] = l_lane[j] * arow + sc[j];
     }
     if (rescale) {
 #pragma unroll
@@ -271,37 +345,44 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
     }
     if (quarter < Geo::kQuarters) {
 #pragma unroll
-      for (int i = 0; i < TPG; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * quarter + j < G) p_lds[wave][i][col][(4 * quarter + j) % G] = sc[i][j];
+      for (int j = 0; j < 4; ++j)
+        if (4 * quarter + j < G) p_lds[wave][col][(4 * quarter + j) % G] = sc[j];
     }
     __builtin_amdgcn_wave_barrier();
-
-    // ---- P.V ----------------------------------------------------------------------
+    const bool full = r.ntok == 16;
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      if (!tv[i]) continue;
-      const bool full = ntok[i] == 16;
+    for (int s = 0; s < STEPS; ++s) {
+      const int n = s * RPS + rg;
+      float pv[G];
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        const int n = s * RPS + rg;
-        float pv[G];
+      for (int h = 0; h < G; ++h) pv[h] = p_lds[wave][n][h];
+      float v[EPL];
+      unpack_chunk<T>(r.v[s], v);
+      if (!full && n >= r.ntok) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) pv[h] = p_lds[wave][i][n][h];
-        float v[EPL];
-        unpack_chunk<T>(vr[i][s], v);
-        if (!full && n >= ntok[i]) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
+        for (int e = 0; e < EPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
       }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // Wave w takes tiles w, w+4, w+8, ...; the next tile's loads are issued before
+  // the current tile is computed (two register sets used in turn).
+  Loads A, B;
+  int t = wave;
+  issue(A, t);
+  while (t < ntiles) {
+    issue(B, t + 4);
+    compute(A);
+    t += 4;
+    if (t >= ntiles) break;
+    issue(A, t + 4);
+    compute(B);
+    t += 4;
   }
 
   // ---- merge the four waves ---------------------------------------------------
@@ -359,34 +440,170 @@ __global__ __launch_bounds__(256) void paged_attention_partition_kernel(Attentio
   }
 }
 
-// Merge the partition records of every multi-partition (sequence, head), in
-// partition order: M = max m_k, w_k = l_k * 2^(m_k - M), out = sum w_k o_k / sum w_k.
+// ---- partition merge --------------------------------------------------------------
+// For every multi-partition (sequence, head) row: M = max m_k, w_k = l_k 2^(m_k - M),
+// out = sum w_k o_k / sum w_k.  Lanes read 16-byte pieces of the partial outputs.
+// Each lane group keeps its own running (max, sum, weighted output) over a fixed
+// subset of the partitions; the groups are then merged in a fixed order, so the
+// result does not depend on timing.
+
+struct Running {
+  float m;     // running maximum (base-2 exponent domain); -inf when empty
+  float l;     // sum of weights relative to m
+  float4 o;    // weighted partial outputs relative to m
+};
+
+__device__ __forceinline__ float rel_scale(float m_old, float m_new) {
+  return m_old == -__builtin_inff() ? 0.f : fast_exp2(m_old - m_new);
+}
+
+__device__ __forceinline__ void merge_into(Running& r, const Running& s) {
+  const float mn = fmaxf(r.m, s.m);
+  const float fr = rel_scale(r.m, mn), fs = rel_scale(s.m, mn);
+  r.l = r.l * fr + s.l * fs;
+  r.o.x = r.o.x * fr + s.o.x * fs;
+  r.o.y = r.o.y * fr + s.o.y * fs;
+  r.o.z = r.o.z * fr + s.o.z * fs;
+  r.o.w = r.o.w * fr + s.o.w * fs;
+  r.m = mn;
+}
+
+template <int N>
+__device__ __forceinline__ void accumulate(Running& r, const float (&m)[N], const float (&l)[N],
+                                           const float4 (&o)[N], const bool (&live)[N]) {
+  float mb = r.m;
+#pragma unroll
+  for (int u = 0; u < N; ++u) mb = live[u] ? fmaxf(mb, m[u]) : mb;
+  const float f = rel_scale(r.m, mb);
+  r.l *= f;
+  r.o.x *= f; r.o.y *= f; r.o.z *= f; r.o.w *= f;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const float w = live[u] ? l[u] * fast_exp2(m[u] - mb) : 0.f;
+    r.l += w;
+    r.o.x = fmaf(w, o[u].x, r.o.x);
+    r.o.y = fmaf(w, o[u].y, r.o.y);
+    r.o.z = fmaf(w, o[u].z, r.o.z);
+    r.o.w = fmaf(w, o[u].w, r.o.w);
+  }
+  r.m = mb;
+}
+
+__device__ __forceinline__ void store_row4(const AttentionArgs& a, int64_t idx, const Running& r) {
+  store_out(a.out, idx + 0, r.o.x / r.l, a.out_bf16);
+  store_out(a.out, idx + 1, r.o.y / r.l, a.out_bf16);
+  store_out(a.out, idx + 2, r.o.z / r.l, a.out_bf16);
+  store_out(a.out, idx + 3, r.o.w / r.l, a.out_bf16);
+}
+
+// Few partitions per row: one wave per row, four rows per workgroup, one round of
+// loads, no barriers.
+constexpr int kNarrowMaxParts = 16;
+
 template <int D>
-__global__ __launch_bounds__(D) void paged_attention_reduce_kernel(AttentionArgs a) {
-  const int h = blockIdx.x % a.num_heads;
-  const int seq = blockIdx.x / a.num_heads;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void paged_attention_reduce_narrow_kernel(AttentionArgs a) {
+  constexpr int LPR = D / 4;             // lanes per record (float4 each)
+  constexpr int KGW = kWave / LPR;       // records per wave load
+  constexpr int NK = kNarrowMaxParts / KGW;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= (int64_t)a.num_seqs * a.num_heads) return;
+  const int seq = (int)(row / a.num_heads);
   const int ctx = a.context_lens[seq];
   const int max_ctx = a.max_blocks_per_seq << a.block_shift;
   if (ctx < 1 || ctx > max_ctx) return;
   const int nparts = (ctx + a.partition_size - 1) / a.partition_size;
   if (nparts <= 1) return;
-  const int64_t row = (int64_t)seq * a.num_heads + h;
+  const int kg = lane / LPR;
+  const int lr = lane % LPR;
   const int64_t rec0 = row * a.max_parts;
-  float M = -__builtin_inff();
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_m[rec0 + k]);
-  float num = 0.f, den = 0.f;
-  for (int k = 0; k < nparts; ++k) {
-    const float w = a.ws_l[rec0 + k] * fast_exp2(a.ws_m[rec0 + k] - M);
-    num = fmaf(w, a.ws_o[(rec0 + k) * D + d], num);
-    den += w;
+  float m[NK], l[NK];
+  float4 o[NK];
+  bool live[NK];
+#pragma unroll
+  for (int u = 0; u < NK; ++u) {
+    const int k = kg + u * KGW;
+    live[u] = k < nparts;
+    m[u] = live[u] ? a.ws_m[rec0 + k] : 0.f;
+    l[u] = live[u] ? a.ws_l[rec0 + k] : 0.f;
+    o[u] = live[u] ? reinterpret_cast<const float4*>(a.ws_o + (rec0 + k) * D)[lr]
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  store_out(a.out, row * D + d, num / den, a.out_bf16);
+  Running r{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  accumulate(r, m, l, o, live);
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    Running s;
+    s.m = __shfl_xor(r.m, off);
+    s.l = __shfl_xor(r.l, off);
+    s.o.x = __shfl_xor(r.o.x, off);
+    s.o.y = __shfl_xor(r.o.y, off);
+    s.o.z = __shfl_xor(r.o.z, off);
+    s.o.w = __shfl_xor(r.o.w, off);
+    // both lanes of a pair merge the same two values in the same order
+    if (lane & off) { const Running t = r; r = s; s = t; }
+    merge_into(r, s);
+  }
+  if (kg == 0) store_row4(a, row * D + lr * 4, r);
+}
+
+// Many partitions per row (long contexts): one workgroup per row, KG lane groups
+// each streaming every KG-th partition four at a time, merged through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void paged_attention_reduce_wide_kernel(AttentionArgs a) {
+  constexpr int kThreads = 256;
+  constexpr int LPR = D / 4;
+  constexpr int KG = kThreads / LPR;
+  constexpr int kUnroll = 4;
+  __shared__ float4 red_o[KG][LPR];
+  __shared__ float red_m[KG];
+  __shared__ float red_l[KG];
+  const int64_t row = blockIdx.x;
+  const int seq = (int)(row / a.num_heads);
+  const int ctx = a.context_lens[seq];
+  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+  if (ctx < 1 || ctx > max_ctx) return;
+  const int nparts = (ctx + a.partition_size - 1) / a.partition_size;
+  if (nparts <= 1) return;
+  const int kg = threadIdx.x / LPR;
+  const int lr = threadIdx.x % LPR;
+  const int64_t rec0 = row * a.max_parts;
+  Running r{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int k0 = kg; k0 < nparts; k0 += KG * kUnroll) {
+    float m[kUnroll], l[kUnroll];
+    float4 o[kUnroll];
+    bool live[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = k0 + u * KG;
+      live[u] = k < nparts;
+      m[u] = live[u] ? a.ws_m[rec0 + k] : 0.f;
+      l[u] = live[u] ? a.ws_l[rec0 + k] : 0.f;
+      o[u] = live[u] ? reinterpret_cast<const float4*>(a.ws_o + (rec0 + k) * D)[lr]
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    accumulate(r, m, l, o, live);
+  }
+  red_o[kg][lr] = r.o;
+  if (lr == 0) {
+    red_m[kg] = r.m;
+    red_l[kg] = r.l;
+  }
+  __syncthreads();
+  if (threadIdx.x < LPR) {
+    Running t{red_m[0], red_l[0], red_o[0][threadIdx.x]};
+#pragma unroll
+    for (int q = 1; q < KG; ++q) merge_into(t, Running{red_m[q], red_l[q], red_o[q][threadIdx.x]});
+    store_row4(a, row * D + threadIdx.x * 4, t);
+  }
 }
 
 // ---- dispatch ------------------------------------------------------------------
 
-constexpr int kTilesPerGroup = 2;
+hipError_t launch_attention_plan(const AttentionArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(paged_attention_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 template <typename T, int D>
 static hipError_t launch_partition_g(const AttentionArgs& a, hipStream_t stream) {
@@ -394,10 +611,10 @@ static hipError_t launch_partition_g(const AttentionArgs& a, hipStream_t stream)
   const dim3 grid((unsigned)((int64_t)a.num_kv_heads * a.max_parts * a.num_seqs));
   const dim3 block(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 1, kTilesPerGroup>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 2, kTilesPerGroup>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 4, kTilesPerGroup>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 8, kTilesPerGroup>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((paged_attention_partition_kernel<T, D, 8>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -415,13 +632,21 @@ hipError_t launch_attention_partition(const AttentionArgs& a, hipStream_t stream
 }
 
 hipError_t launch_attention_reduce(const AttentionArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.num_heads * a.num_seqs));
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL(paged_attention_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL(paged_attention_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
-  else
+  const int64_t rows = (int64_t)a.num_heads * a.num_seqs;
+  const bool narrow = a.max_parts <= kNarrowMaxParts;
+  if (a.head_dim == 64) {
+    if (narrow)
+      hipLaunchKernelGGL(paged_attention_reduce_narrow_kernel<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(paged_attention_reduce_wide_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, a);
+  } else if (a.head_dim == 128) {
+    if (narrow)
+      hipLaunchKernelGGL(paged_attention_reduce_narrow_kernel<128>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(paged_attention_reduce_wide_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

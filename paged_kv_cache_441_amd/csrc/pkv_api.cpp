@@ -34,7 +34,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
 struct AttnShape {
   int64_t max_parts = 0;
   int partition = 0;
-  size_t ws_bytes = 0;
+  size_t plan_bytes = 0;    // the work plan at the start of the workspace
+  size_t ws_bytes = 0;      // plan + partition records
 };
 
 // Shape checks common to every attention entry point; fills the derived sizes.
@@ -56,8 +57,21 @@ pkv_status check_attention_shape(int32_t num_seqs, int32_t num_heads, int32_t he
     return PKV_ERR_INVALID_ARG;
   int64_t bytes = 0;
   if (!mul_ok(recs, int64_t{head_dim} + 2, INT64_MAX / 8, &bytes)) return PKV_ERR_INVALID_ARG;
-  s->ws_bytes = static_cast<size_t>(bytes) * 4;
+  int64_t items = 0;
+  if (!mul_ok(num_seqs, s->max_parts, INT32_MAX, &items)) return PKV_ERR_UNSUPPORTED;
+  s->plan_bytes = pkv::plan_bytes(num_seqs, s->max_parts);
+  s->ws_bytes = s->plan_bytes + static_cast<size_t>(bytes) * 4;
   return PKV_OK;
+}
+
+void set_workspace(pkv::AttentionArgs* a, void* workspace, size_t plan_bytes, int64_t recs) {
+  char* ws = static_cast<char*>(workspace);
+  a->plan_count = ws ? reinterpret_cast<int*>(ws) : nullptr;
+  a->plan_items = ws ? reinterpret_cast<int4*>(ws + 256) : nullptr;
+  float* f = ws ? reinterpret_cast<float*>(ws + plan_bytes) : nullptr;
+  a->ws_m = f;
+  a->ws_l = f ? f + recs : nullptr;
+  a->ws_o = f ? f + 2 * recs : nullptr;
 }
 
 pkv_status fill_attention_args(void* out, const void* query, const void* key_cache,
@@ -114,11 +128,7 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   a->max_parts = static_cast<int>(s.max_parts);
   a->kv_bf16 = kv_dtype == PKV_BF16;
   a->out_bf16 = out_dtype == PKV_BF16;
-  const int64_t recs = int64_t{num_seqs} * num_heads * s.max_parts;
-  float* ws = static_cast<float*>(workspace);
-  a->ws_m = ws;
-  a->ws_l = ws ? ws + recs : nullptr;
-  a->ws_o = ws ? ws + 2 * recs : nullptr;
+  set_workspace(a, workspace, s.plan_bytes, int64_t{num_seqs} * num_heads * s.max_parts);
   return PKV_OK;
 }
 
@@ -188,6 +198,28 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, 
   return s.ws_bytes;
 }
 
+pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  AttnShape s;
+  pkv_status st = check_attention_shape(num_seqs, 1, 64, block_size, max_blocks_per_seq,
+                                        partition_size, &s);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens) return PKV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < s.plan_bytes) return PKV_ERR_WORKSPACE;
+  pkv::AttentionArgs a{};
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.block_shift = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_size = s.partition;
+  a.max_parts = static_cast<int>(s.max_parts);
+  set_workspace(&a, workspace, s.plan_bytes, 0);
+  return hip_status(pkv::launch_attention_plan(a, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status pkv_paged_attention_partition(void* out, const void* query, const void* key_cache,
                                          const void* value_cache, const int32_t* block_tables,
                                          const int32_t* context_lens, int32_t num_seqs,
@@ -237,6 +269,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
                                       workspace_bytes, true, &a);
   if (st != PKV_OK || num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_attention_plan(a, s));
+  if (st != PKV_OK) return st;
   st = hip_status(pkv::launch_attention_partition(a, s));
   if (st != PKV_OK) return st;
   if (a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));

@@ -34,11 +34,19 @@ struct AttentionArgs {
   int max_parts;            // ceil(max_blocks_per_seq * block_size / partition_size)
   bool kv_bf16;
   bool out_bf16;
+  int* plan_count;          // number of work items in the plan
+  int4* plan_items;         // [num_seqs * max_parts] (seq, partition, context length, partitions)
   float* ws_m;              // [num_seqs][num_heads][max_parts]
   float* ws_l;              // [num_seqs][num_heads][max_parts]
   float* ws_o;              // [num_seqs][num_heads][max_parts][head_dim]
 };
 
+// Workspace layout, in bytes from its start (all offsets 256-byte aligned):
+//   plan: count (int32) at 0, items (int4) at 256;
+//   then m, l and o records of the partitions (fp32).
+size_t plan_bytes(int64_t num_seqs, int64_t max_parts);
+
+hipError_t launch_attention_plan(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_partition(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_reduce(const AttentionArgs& a, hipStream_t stream);
 

@@ -154,9 +154,24 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
     return out
 
 
+def paged_attention_plan(context_lens: torch.Tensor, workspace: torch.Tensor, block_size: int,
+                         max_blocks_per_seq: int, partition_size: int = 0) -> torch.Tensor:
+    """Stage 1 of paged_attention_decode: the work list, written into ``workspace``."""
+    _i32(context_lens, "context_lens")
+    _dev(workspace, "workspace")
+    _same_device(context_lens, workspace)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_plan(_ptr(context_lens), context_lens.shape[0], int(block_size),
+                                      int(max_blocks_per_seq), int(partition_size),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(workspace))
+    _lib.check(st, "pkv_paged_attention_plan")
+    return workspace
+
+
 def paged_attention_partition(query, key_cache, value_cache, block_tables, context_lens, scale,
                               partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
-    """First half of paged_attention_decode (see the header); returns (out, workspace)."""
+    """Stage 2 of paged_attention_decode (needs a plan in ``workspace``); returns (out, workspace)."""
     dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
         query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
         partition_size)
@@ -172,7 +187,7 @@ def paged_attention_partition(query, key_cache, value_cache, block_tables, conte
 def paged_attention_reduce(out: torch.Tensor, context_lens: torch.Tensor, workspace: torch.Tensor,
                            block_size: int, max_blocks_per_seq: int,
                            partition_size: int = 0) -> torch.Tensor:
-    """Second half of paged_attention_decode: merge the partition records into ``out``."""
+    """Stage 3 of paged_attention_decode: merge the partition records into ``out``."""
     _dev(out, "out")
     _i32(context_lens, "context_lens")
     _dev(workspace, "workspace")

@@ -46,13 +46,17 @@ def test_status_strings(lib):
     assert lib.pkv_status_string(OK) == b"ok"
 
 
+def _ws(B, H, D, NP):
+    plan = 256 + (B * NP * 16 + 255) // 256 * 256
+    return plan + B * H * NP * (D + 2) * 4
+
+
 def test_workspace_bytes_formula(lib):
-    # B * H * ceil(MB*BS/P) * (D + 2) * 4
-    assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 512) == \
-        256 * 32 * 16 * 130 * 4
-    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == \
-        8 * 32 * 256 * 130 * 4
-    assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 512) == 4 * 4 * 1 * 66 * 4
+    # plan (256 + roundup256(B*NP*16)) + B * H * NP * (D + 2) * 4, NP = ceil(MB*BS/P)
+    assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 512) == _ws(256, 32, 128, 16)
+    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == _ws(8, 32, 128, 256)
+    assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 512) == _ws(4, 4, 64, 1)
+    assert _ws(4, 4, 64, 1) == 512 + 4 * 4 * 66 * 4
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 24) == 0     # P % 16
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 32, 7, 16) == 0     # P % BS
     assert lib.pkv_paged_attention_workspace_bytes(-1, 4, 64, 16, 7, 0) == 0
@@ -98,6 +102,15 @@ def test_decode_rejects(lib, kw, status):
 def test_decode_empty_batch_is_noop(lib):
     assert _decode(lib, B=0, out=NULL, query=NULL, kc=NULL, vc=NULL, bt=NULL, cl=NULL,
                    ws=NULL, wsb=0) == OK
+
+
+def test_plan_rejects(lib):
+    p = lib.pkv_paged_attention_plan
+    assert p(NULL, 4, 16, 64, 0, FAKE, 1 << 20, NULL) == INV
+    assert p(FAKE, 4, 16, 64, 24, FAKE, 1 << 20, NULL) == INV          # P % 16
+    assert p(FAKE, 4, 16, 64, 0, FAKE, 300, NULL) == WS                # needs 256 + 256
+    assert p(FAKE, 4, 16, 64, 0, NULL, 1 << 20, NULL) == WS
+    assert p(NULL, 0, 16, 64, 0, NULL, 0, NULL) == OK
 
 
 def test_partition_and_reduce_reject(lib):

@@ -182,7 +182,9 @@ def test_partition_then_reduce_equals_decode():
     b = build_batch(spec_of(NB=2048), [3, 513, 2000, 5000], device="cuda")
     slots, kc, vc, out = run_step(b)
     bt, cl = device_meta(b)
-    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512)
+    ws = pkv.alloc_workspace(b.query, bt, 16, 512)
+    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], 512)
+    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512, workspace=ws)
     pkv.paged_attention_reduce(out2, cl, ws, 16, bt.shape[1], 512)
     torch.cuda.synchronize()
     assert torch.equal(bits(out), bits(out2))
@@ -201,3 +203,57 @@ def test_invalid_device_data_gives_nan_rows_only():
     o = out.cpu()
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
     assert torch.equal(bits(o[[0, 3]]), bits(good.cpu()[[0, 3]]))
+
+
+# ----------------------------------------------------------------------------
+# the work plan
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [16, 512, 1024])
+def test_plan_lists_every_partition_longest_first(P):
+    ctx = np.array([1, 15, 16, 17, 511, 512, 513, 1024, 3000, 8192, 0, 9000], np.int32)
+    MB = 8192 // 16
+    cl = torch.as_tensor(ctx, device="cuda")
+    ws = torch.zeros(pkv.workspace_bytes(len(ctx), 4, 64, 16, MB, P), dtype=torch.uint8,
+                     device="cuda")
+    pkv.paged_attention_plan(cl, ws, 16, MB, P)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    count = int(raw[:4].view(np.int32)[0])
+    items = raw[256:256 + 16 * count].view(np.int32).reshape(count, 4)
+    expect = set()
+    for i, c in enumerate(ctx):
+        if 1 <= c <= MB * 16:
+            expect |= {(i, p) for p in range(-(-c // P))}
+        else:
+            expect.add((i, 0))                     # invalid length: one item for its NaN rows
+    got = [(int(s), int(p)) for s, p in items[:, :2]]
+    assert len(got) == len(set(got)) and set(got) == expect
+    for s, p, c, n in items:
+        if 1 <= ctx[s] <= MB * 16:
+            assert c == ctx[s] and n == -(-ctx[s] // P)
+    # whole partitions first, then partial ones by non-increasing size class
+    sizes = [min(P, int(c) - int(p) * P) if 1 <= c <= MB * 16 else P for _, p, c, _ in items]
+    partial = [k for k, z in enumerate(sizes) if z < P]
+    assert all(sizes[k] == P for k in range(partial[0] if partial else len(sizes)))
+    cls = [((P - sizes[k]) * 8) // P for k in partial]
+    assert cls == sorted(cls)
+
+
+def test_one_plan_serves_every_layer():
+    b = build_batch(spec_of(NB=2048), [5, 700, 1600, 4000], device="cuda")
+    bt, cl = device_meta(b)
+    ws = pkv.alloc_workspace(b.query, bt, 16, 512)
+    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], 512)
+    for layer in range(2):
+        kc = b.key_cache.clone()
+        vc = b.value_cache.clone()
+        if layer:
+            kc.copy_(kc.flip(0))
+            vc.copy_(vc.flip(-1))
+        ref = pkv.paged_attention_decode(b.query, kc, vc, bt, cl, b.scale, 512)
+        out, _ = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512,
+                                               workspace=ws)
+        pkv.paged_attention_reduce(out, cl, ws, 16, bt.shape[1], 512)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(ref))
