@@ -99,9 +99,16 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool 
   else
     static_cast<float*>(out)[idx] = v;
 }
-// Build-time tuning knob (default: the measured best on MI355X).
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferFlags = 0x00020000;
+
+// Build-time tuning knobs (defaults: the measured best on MI355X).
 #ifndef PKV_WAVES_PER_EU
 #define PKV_WAVES_PER_EU 1         // occupancy floor handed to the register allocator
+#endif
+#ifndef PKV_Q_IN_LDS
+#define PKV_Q_IN_LDS 0             // 1: the query operand lives in LDS, not registers
 #endif
 
 size_t plan_bytes(int64_t num_seqs, int64_t max_parts) {
@@ -243,6 +250,18 @@ void paged_attention_partition_kernel(AttentionArgs a) {
   const int li = lane % NCH;       // 16-byte chunk within a value row
 
   // Query rows of this kv head's group, as the MFMA A operand (rows >= G are zero).
+#if PKV_Q_IN_LDS
+  // Kept in LDS and re-read for every tile, which frees the registers it would pin.
+  __shared__ uint4 q_lds[QKC][kWave];
+  if (wave == 0) {
+    const char* qrow = static_cast<const char*>(a.query) +
+                       ((int64_t)seq * H + g * G + (col < G ? col : 0)) * D * EB;
+#pragma unroll
+    for (int c = 0; c < QKC; ++c)
+      q_lds[c][lane] = col < G ? load16(qrow, (4 * c + quarter) * 16) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+#else
   uint4 qa[QKC];
   {
     const char* qrow = static_cast<const char*>(a.query) +
@@ -251,6 +270,7 @@ void paged_attention_partition_kernel(AttentionArgs a) {
     for (int c = 0; c < QKC; ++c)
       qa[c] = col < G ? load16(qrow, (4 * c + quarter) * 16) : make_uint4(0, 0, 0, 0);
   }
+#endif
 
   // Byte offsets: the block base is the same for the whole wave (a scalar), the
   // per-lane part fits in 32 bits.
@@ -260,6 +280,8 @@ void paged_attention_partition_kernel(AttentionArgs a) {
   const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.block_shift) - 1;
   const int64_t head_bytes = (int64_t)g * D * EB;
+  const int num_blocks = (int)a.num_blocks;               // the ABI keeps it below 2^31
+  const int tile_span = (int)(15 * row_bytes + D * EB);   // bytes of one head's 16 rows
   const char* kcache = static_cast<const char*>(a.key_cache);
   const char* vcache = static_cast<const char*>(a.value_cache);
   const float kNegInf = -__builtin_inff();
@@ -280,32 +302,56 @@ void paged_attention_partition_kernel(AttentionArgs a) {
   using Loads = TileLoads<QKC, STEPS>;
 
   // Issue the key and value loads of tile ``tile`` (wave-uniform decisions only).
+  // The loads themselves are unconditional, so the compiler can count them and
+  // wait for exactly the tile being computed while the next one is in flight: a
+  // tile that does not exist (past the partition's end, or a bad block id) reads
+  // pool block 0 instead, which is always in bounds and, shared by every
+  // workgroup, stays in cache.
+  //
+  // Loads go through raw buffer descriptors built per tile in scalar registers:
+  // base = the tile's first row of this head, range = the 16 rows of the head.
+  // Lane offsets stay 32-bit, no 64-bit address arithmetic lands in vector
+  // registers, and the hardware returns zeros for anything past the range.
   auto issue = [&](Loads& r, int tile) {
-    r.ntok = 0;
+    int ntok = 0;
+    int64_t off = 0;
     if (tile < ntiles) {
       const int tok0 = p_start + 16 * tile;
       const int32_t blk = bt_row[tok0 >> a.block_shift];
-      if (blk < 0 || (int64_t)blk >= a.num_blocks) {
+      if (blk < 0 || blk >= num_blocks) {
         bad = 1;
       } else {
-        r.ntok = min(16, p_end - tok0);
-        const int64_t off = (((int64_t)blk << a.block_shift) + (tok0 & bs_mask)) * row_bytes +
-                            head_bytes;
-        const char* kb = kcache + off;
-        const char* vb = vcache + off;
-#pragma unroll
-        for (int c = 0; c < QKC; ++c)
-          r.k[c] = *reinterpret_cast<const uint4*>(kb + k_lane + c * 64);
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s)
-          r.v[s] = *reinterpret_cast<const uint4*>(vb + v_lane + s * RPS * row_bytes);
+        ntok = min(16, p_end - tok0);
+        off = (((int64_t)blk << a.block_shift) + (tok0 & bs_mask)) * row_bytes + head_bytes;
       }
     }
+    r.ntok = ntok;
+    const auto kd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kcache + off), 0,
+                                                      tile_span, kBufferFlags);
+    const auto vd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vcache + off), 0,
+                                                      tile_span, kBufferFlags);
+#pragma unroll
+    for (int c = 0; c < QKC; ++c)
+      r.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             kd, k_lane + c * 64, 0, 0));
+    // keys before values in every copy of this code, so the wait counts agree
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+      r.v[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             vd, v_lane, s * RPS * row_bytes, 0));
   };
 
   // Scores, running maximum, probabilities and P.V for one loaded tile.
   auto compute = [&](const Loads& r) {
     if (r.ntok == 0) return;
+#if PKV_Q_IN_LDS
+    uint4 qa[QKC];
+    int ql = lane;
+    asm volatile("" : "+v"(ql));   // keep the reads in the loop
+#pragma unroll
+    for (int c = 0; c < QKC; ++c) qa[c] = q_lds[c][ql];
+#endif
     const floatx4 s4 = tile_scores<T, QKC>(qa, r.k);
     const bool live = col < r.ntok;
     float sc[4], gmax[4];

@@ -89,7 +89,8 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_INVALID_ARG;
   if (need_inputs) {
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
-    if (num_blocks <= 0 || !std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+    if (num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale))
+      return PKV_ERR_INVALID_ARG;   // block ids are int32
     int64_t pool = 0;
     if (!mul_ok(num_blocks, block_size, INT64_MAX / 4096, &pool) ||
         !mul_ok(pool, int64_t{num_kv_heads} * head_dim, INT64_MAX / 8, &pool))
