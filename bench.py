@@ -1,7 +1,8 @@
 """Benchmark of one PagedAttention decode step on one MI355X.
 
 A step is the whole hot path over one batch: slot mapping, cache write of every
-sequence's new token, the attention partition kernel, the log-sum-exp reduce.
+sequence's new token and the attention work plan (one fused launch), the attention
+partition kernel, the log-sum-exp reduce.
 Inputs are seeded synthetic batches already resident in HBM.  The headline is the
 KV bytes the step must read (sum of context lengths x kv heads x head_dim x 2 x
 element size) per second, the same figure as a fraction of the 8 TB/s HBM peak, and
@@ -45,7 +46,25 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle runs on (0: chosen for ~10-30 s)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "known-size reference for HBM traffic counters)")
     return ap.parse_args(argv)
+
+
+def copy_calibration() -> int:
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": 3}), flush=True)
+    return 0
 
 
 def cpu_model() -> str:
@@ -60,6 +79,8 @@ def cpu_model() -> str:
 
 def main(argv=None) -> int:
     args = parse(argv)
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
                                    "has no multi-GPU mode (use --gpus 1)"}))
@@ -95,9 +116,7 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pkv.slot_mapping(bt, cl, BS, NB, out=slots)
-        pkv.kv_cache_write(b.key, b.value, kc, vc, slots)
-        pkv.paged_attention_plan(cl, ws, BS, MB, P)
+        pkv.decode_prologue(bt, cl, b.key, b.value, kc, vc, ws, P, slot_mapping=slots)
         if ev is not None:
             ev[1].record()
         pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, out=out, workspace=ws)
@@ -162,7 +181,7 @@ def main(argv=None) -> int:
         "kv_bytes_per_step": kv_bytes,
         "attention_kv_gbs": round(kv_bytes / (attn_ms / 1e3) / 1e9, 1),
         "kernel_ms": {
-            "slot_mapping+kv_cache_write+plan": round(float(t_write.mean()), 5),
+            "decode_prologue (slot mapping, cache write, plan)": round(float(t_write.mean()), 5),
             "attention_partition": round(part_ms, 5),
             "attention_reduce": round(float(t_red.mean()), 5),
             "step_events": round(float(t_gpu.mean()), 5),

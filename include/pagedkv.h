@@ -118,6 +118,29 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
                               void* stream);
 
 /*
+ * pkv_decode_prologue -- the steps of a decode step that come before attention,
+ * in one launch: pkv_slot_mapping for every sequence (written to slot_mapping),
+ * pkv_kv_cache_write of every sequence's new token (key/value row t belongs to
+ * sequence t) at that slot, and pkv_paged_attention_plan into the workspace.
+ * The results are bit-identical to the three separate calls.  A model with
+ * several layers calls it for its first layer and reuses slot_mapping and the
+ * plan for the others (pkv_kv_cache_write + the partition and reduce stages).
+ *
+ *   key, value    device [num_seqs][num_kv_heads][head_dim], kv_dtype
+ *   slot_mapping  device int32 [num_seqs], written
+ *   workspace     at least the plan part of pkv_paged_attention_workspace_bytes()
+ *
+ * Arguments are checked as for the three separate calls.
+ */
+pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
+                               const void* key, const void* value, void* key_cache,
+                               void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_decode needs (0 for invalid
  * arguments).  With P the effective partition size and
  * NP = ceil(max_blocks_per_seq*block_size / P), the workspace holds

@@ -30,6 +30,8 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_slot_mapping": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp]),
     "pkv_kv_cache_write": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_decode_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   _i64, _i32, _i32, _vp, _sz, _vp]),
     "pkv_paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),

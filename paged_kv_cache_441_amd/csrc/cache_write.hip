@@ -9,8 +9,25 @@
 // slot * num_kv_heads * head_dim, so the write is a row copy per token.
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
+#include "pkv_plan.hpp"
 
 namespace pkv {
+
+// Slot of sequence i's new token, or -1 for an invalid length or block id.
+__device__ __forceinline__ int32_t slot_of(const int32_t* __restrict__ block_tables,
+                                           const int32_t* __restrict__ context_lens, int i,
+                                           int max_blocks_per_seq, int block_shift,
+                                           int64_t num_blocks) {
+  const int ctx = context_lens[i];
+  const int block_size = 1 << block_shift;
+  if (ctx < 1 || ctx > max_blocks_per_seq * block_size) return -1;
+  const int pos = ctx - 1;
+  const int logical = pos >> block_shift;
+  const int offset = pos & (block_size - 1);
+  const int32_t physical = block_tables[(int64_t)i * max_blocks_per_seq + logical];
+  if (physical < 0 || (int64_t)physical >= num_blocks) return -1;
+  return physical * block_size + offset;
+}
 
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -18,17 +35,8 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
     int block_shift, int64_t num_blocks) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= num_seqs) return;
-  const int ctx = context_lens[i];
-  const int block_size = 1 << block_shift;
-  int32_t slot = -1;
-  if (ctx >= 1 && ctx <= max_blocks_per_seq * block_size) {
-    const int pos = ctx - 1;
-    const int logical = pos >> block_shift;
-    const int offset = pos & (block_size - 1);
-    const int32_t physical = block_tables[(int64_t)i * max_blocks_per_seq + logical];
-    if (physical >= 0 && (int64_t)physical < num_blocks) slot = physical * block_size + offset;
-  }
-  slot_mapping[i] = slot;
+  slot_mapping[i] = slot_of(block_tables, context_lens, i, max_blocks_per_seq, block_shift,
+                            num_blocks);
 }
 
 // One workgroup per token: copy the token's K row and V row (num_kv_heads*head_dim
@@ -49,6 +57,51 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
       value_cache[dst + c - chunks_per_row] = value[src + c - chunks_per_row];
     }
   }
+}
+
+// The decode step's prologue in one launch: workgroup 0 builds the attention plan
+// while workgroup 1 + i computes sequence i's slot and stores its new K/V rows.
+constexpr int kPrologueThreads = 256;
+
+__global__ __launch_bounds__(kPrologueThreads) void decode_prologue_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ key_cache,
+    uint4* __restrict__ value_cache, int32_t* __restrict__ slot_mapping, int num_seqs,
+    int max_blocks_per_seq, int block_shift, int64_t num_blocks, int chunks_per_row,
+    int partition_size, int4* __restrict__ plan_items, int* __restrict__ plan_count) {
+  if (blockIdx.x == 0) {
+    build_plan<kPrologueThreads>(context_lens, num_seqs, partition_size,
+                                 max_blocks_per_seq << block_shift, plan_items, plan_count);
+    return;
+  }
+  const int t = blockIdx.x - 1;
+  const int32_t slot = slot_of(block_tables, context_lens, t, max_blocks_per_seq, block_shift,
+                               num_blocks);
+  if (threadIdx.x == 0) slot_mapping[t] = slot;
+  if (slot < 0) return;
+  const int64_t src = (int64_t)t * chunks_per_row;
+  const int64_t dst = (int64_t)slot * chunks_per_row;
+  for (int c = threadIdx.x; c < 2 * chunks_per_row; c += blockDim.x) {
+    if (c < chunks_per_row)
+      key_cache[dst + c] = key[src + c];
+    else
+      value_cache[dst + c - chunks_per_row] = value[src + c - chunks_per_row];
+  }
+}
+
+hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
+                                  const void* key, const void* value, void* key_cache,
+                                  void* value_cache, int32_t* slot_mapping, int num_seqs,
+                                  int max_blocks_per_seq, int block_shift, int64_t num_blocks,
+                                  int row_bytes, int partition_size, int4* plan_items,
+                                  int* plan_count, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_prologue_kernel, dim3(num_seqs + 1), dim3(kPrologueThreads), 0, stream,
+                     block_tables, context_lens, static_cast<const uint4*>(key),
+                     static_cast<const uint4*>(value), static_cast<uint4*>(key_cache),
+                     static_cast<uint4*>(value_cache), slot_mapping, num_seqs, max_blocks_per_seq,
+                     block_shift, num_blocks, row_bytes / 16, partition_size, plan_items,
+                     plan_count);
+  return hipGetLastError();
 }
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* context_lens,

@@ -28,6 +28,7 @@
 
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
+#include "pkv_plan.hpp"
 
 namespace pkv {
 
@@ -115,75 +116,10 @@ size_t plan_bytes(int64_t num_seqs, int64_t max_parts) {
   return 256 + ((size_t)(num_seqs * max_parts) * sizeof(int4) + 255) / 256 * 256;
 }
 
-// ---- work plan -------------------------------------------------------------------
-// The partition kernel's grid is sized for the longest context the block tables
-// allow, so most of its workgroups may find nothing to do, and the hardware hands
-// out workgroups in index order.  The plan lists the real (sequence, partition)
-// work items so that workgroup k takes item k / num_kv_heads: every whole
-// partition first, then the partial last partitions, longest first (eight size
-// classes), then nothing.  Dispatching the longest items first keeps the end of
-// the kernel from waiting on a few long ones, and the idle workgroups all sit at
-// the end of the grid where they cost almost nothing.  A sequence with an invalid
-// context length gets one item, whose workgroups write its NaN output.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanClasses = 8;
-
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-__device__ __forceinline__ int plan_scan(int x, int* lds, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  int v = x;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  if (lane == kWave - 1) lds[wave] = v;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kPlanThreads / kWave; ++w) {
-    const int t = lds[w];
-    base += w < wave ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + v - x;
-}
-
+// The standalone plan stage: one workgroup.
 __global__ __launch_bounds__(kPlanThreads) void paged_attention_plan_kernel(AttentionArgs a) {
-  __shared__ int lds[kPlanThreads / kWave];
-  const int P = a.partition_size;
-  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
-  int offset = 0;
-  // whole partitions (and the single item of an invalid sequence)
-  for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
-    const int i = c0 + threadIdx.x;
-    const int ctx = i < a.num_seqs ? a.context_lens[i] : 0;
-    const bool valid = ctx >= 1 && ctx <= max_ctx;
-    const int n = i >= a.num_seqs ? 0 : (valid ? ctx / P : 1);
-    const int nparts = valid ? (ctx + P - 1) / P : 1;
-    int total;
-    const int pos = offset + plan_scan(n, lds, &total);
-    for (int p = 0; p < n; ++p) a.plan_items[pos + p] = make_int4(i, p, ctx, nparts);
-    offset += total;
-  }
-  // partial last partitions, by size class, largest first
-  for (int cls = 0; cls < kPlanClasses; ++cls) {
-    for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
-      const int i = c0 + threadIdx.x;
-      const int ctx = i < a.num_seqs ? a.context_lens[i] : 0;
-      const bool valid = ctx >= 1 && ctx <= max_ctx;
-      const int rem = valid ? ctx % P : 0;
-      const int mine = rem > 0 && (int)(((int64_t)(P - rem) * kPlanClasses) / P) == cls;
-      int total;
-      const int pos = offset + plan_scan(mine, lds, &total);
-      if (mine) a.plan_items[pos] = make_int4(i, ctx / P, ctx, (ctx + P - 1) / P);
-      offset += total;
-    }
-  }
-  if (threadIdx.x == 0) *a.plan_count = offset;
+  build_plan<kPlanThreads>(a.context_lens, a.num_seqs, a.partition_size,
+                           a.max_blocks_per_seq << a.block_shift, a.plan_items, a.plan_count);
 }
 
 // The loads of one 16-token tile, in flight while the previous tile is computed.

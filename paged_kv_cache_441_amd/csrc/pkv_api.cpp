@@ -199,6 +199,40 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, 
   return s.ws_bytes;
 }
 
+pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
+                               const void* key, const void* value, void* key_cache,
+                               void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  AttnShape s;
+  pkv_status st = check_attention_shape(num_seqs, 1, 64, block_size, max_blocks_per_seq,
+                                        partition_size, &s);
+  if (st != PKV_OK) return st;
+  int64_t t = 0, row = 0, cache_bytes = 0;
+  if (!mul_ok(num_blocks, block_size, INT32_MAX, &t)) return PKV_ERR_INVALID_ARG;  // int32 slots
+  if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row) ||
+      !mul_ok(t, row, INT64_MAX / 2, &cache_bytes))
+    return PKV_ERR_INVALID_ARG;
+  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !key || !value || !key_cache || !value_cache ||
+      !slot_mapping)
+    return PKV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < s.plan_bytes) return PKV_ERR_WORKSPACE;
+  pkv::AttentionArgs a{};
+  set_workspace(&a, workspace, s.plan_bytes, 0);
+  return hip_status(pkv::launch_decode_prologue(
+      block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping, num_seqs,
+      max_blocks_per_seq, log2_exact(block_size), num_blocks, static_cast<int>(row), s.partition,
+      a.plan_items, a.plan_count, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
                                     int32_t block_size, int32_t max_blocks_per_seq,
                                     int32_t partition_size, void* workspace,

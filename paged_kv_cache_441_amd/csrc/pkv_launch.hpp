@@ -15,6 +15,13 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
                               void* value_cache, const int32_t* slot_mapping, int num_tokens,
                               int row_bytes, int64_t num_slots, hipStream_t stream);
 
+hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
+                                  const void* key, const void* value, void* key_cache,
+                                  void* value_cache, int32_t* slot_mapping, int num_seqs,
+                                  int max_blocks_per_seq, int block_shift, int64_t num_blocks,
+                                  int row_bytes, int partition_size, int4* plan_items,
+                                  int* plan_count, hipStream_t stream);
+
 struct AttentionArgs {
   void* out;
   const void* query;

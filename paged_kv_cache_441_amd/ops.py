@@ -95,6 +95,41 @@ def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _lib.check(st, "pkv_kv_cache_write")
 
 
+def decode_prologue(block_tables: torch.Tensor, context_lens: torch.Tensor, key: torch.Tensor,
+                    value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    workspace: torch.Tensor, partition_size: int = 0,
+                    slot_mapping: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Slot mapping + cache write + attention plan in one launch; returns the slots."""
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    dt = _kv(key, "key")
+    for t, n in ((value, "value"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        if _kv(t, n) != dt:
+            raise TypeError(f"{n} dtype differs from key")
+    _dev(workspace, "workspace")
+    B = context_lens.shape[0]
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("caches must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    NB, BS, Hkv, D = key_cache.shape
+    if key.shape != (B, Hkv, D) or value.shape != (B, Hkv, D):
+        raise ValueError(f"key/value must be [{B}, {Hkv}, {D}]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(B, dtype=torch.int32, device=key.device)
+    _i32(slot_mapping, "slot_mapping")
+    _same_device(block_tables, context_lens, key, value, key_cache, value_cache, workspace,
+                 slot_mapping)
+    lib = _lib.load_library()
+    st = lib.pkv_decode_prologue(_ptr(block_tables), _ptr(context_lens), _ptr(key), _ptr(value),
+                                 _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), B,
+                                 block_tables.shape[1], Hkv, D, BS, NB, dt, int(partition_size),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(key))
+    _lib.check(st, "pkv_decode_prologue")
+    return slot_mapping
+
+
 def workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, block_size: int,
                     max_blocks_per_seq: int, partition_size: int = 0) -> int:
     return int(_lib.load_library().pkv_paged_attention_workspace_bytes(

@@ -32,6 +32,16 @@ def lib():
     return _lib.load_library()
 
 
+@pytest.fixture(scope="module")
+def cpu_only():
+    # The calls below pass fake device pointers and rely on argument checks failing
+    # first; on a machine with a GPU a wrong expectation could launch a kernel on
+    # them, so there they are left to the GPU suite, which uses real buffers.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer ABI checks run only where no GPU is visible")
+
+
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
     assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -95,16 +105,16 @@ def _decode(lib, **kw):
     (dict(ws=NULL), WS),
     (dict(wsb=16), WS),
 ])
-def test_decode_rejects(lib, kw, status):
+def test_decode_rejects(lib, cpu_only, kw, status):
     assert _decode(lib, **kw) == status
 
 
-def test_decode_empty_batch_is_noop(lib):
+def test_decode_empty_batch_is_noop(lib, cpu_only):
     assert _decode(lib, B=0, out=NULL, query=NULL, kc=NULL, vc=NULL, bt=NULL, cl=NULL,
                    ws=NULL, wsb=0) == OK
 
 
-def test_plan_rejects(lib):
+def test_plan_rejects(lib, cpu_only):
     p = lib.pkv_paged_attention_plan
     assert p(NULL, 4, 16, 64, 0, FAKE, 1 << 20, NULL) == INV
     assert p(FAKE, 4, 16, 64, 24, FAKE, 1 << 20, NULL) == INV          # P % 16
@@ -113,7 +123,25 @@ def test_plan_rejects(lib):
     assert p(NULL, 0, 16, 64, 0, NULL, 0, NULL) == OK
 
 
-def test_partition_and_reduce_reject(lib):
+def test_prologue_rejects(lib, cpu_only):
+    p = lib.pkv_decode_prologue
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 8, 128, 16, 1024, BF16, 0, FAKE,
+            1 << 20, NULL]
+    assert p(*args[:0], NULL, *args[1:]) == INV                        # block_tables
+    assert p(*args[:6], NULL, *args[7:]) == INV                        # slot_mapping
+    bad = list(args); bad[11] = 12                                     # block size not 2^k
+    assert p(*bad) == INV
+    bad = list(args); bad[13] = 9                                      # dtype
+    assert p(*bad) == INV
+    bad = list(args); bad[16] = 100                                    # workspace too small
+    assert p(*bad) == WS
+    bad = list(args); bad[9], bad[10] = 1, 3                           # 6-byte rows
+    assert p(*bad) == UNS
+    empty = list(args); empty[7] = 0
+    assert p(*[NULL if i < 7 or i == 15 else x for i, x in enumerate(empty)]) == OK
+
+
+def test_partition_and_reduce_reject(lib, cpu_only):
     assert lib.pkv_paged_attention_partition(FAKE, NULL, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 128,
                                              16, 64, 1024, 0.1, 0, BF16, F32, FAKE, 1 << 30,
                                              NULL) == INV
@@ -125,7 +153,7 @@ def test_partition_and_reduce_reject(lib):
                                           NULL) == OK
 
 
-def test_cache_write_rejects(lib):
+def test_cache_write_rejects(lib, cpu_only):
     w = lib.pkv_kv_cache_write
     assert w(NULL, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 1024, BF16, NULL) == INV
     assert w(FAKE, FAKE, FAKE, FAKE, NULL, 4, 8, 128, 16, 1024, BF16, NULL) == INV
@@ -136,7 +164,7 @@ def test_cache_write_rejects(lib):
     assert w(NULL, NULL, NULL, NULL, NULL, 0, 8, 128, 16, 1024, BF16, NULL) == OK
 
 
-def test_slot_mapping_rejects(lib):
+def test_slot_mapping_rejects(lib, cpu_only):
     s = lib.pkv_slot_mapping
     assert s(NULL, FAKE, FAKE, 4, 64, 16, 1024, NULL) == INV
     assert s(FAKE, FAKE, FAKE, 4, 64, 12, 1024, NULL) == INV           # block size not 2^k

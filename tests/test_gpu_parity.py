@@ -257,3 +257,63 @@ def test_one_plan_serves_every_layer():
         pkv.paged_attention_reduce(out, cl, ws, 16, bt.shape[1], 512)
         torch.cuda.synchronize()
         assert torch.equal(bits(out), bits(ref))
+
+
+def _plan_bytes(ws):
+    raw = ws.cpu().numpy()
+    count = int(raw[:4].view(np.int32)[0])
+    return count, raw[256:256 + 16 * count].tobytes()
+
+
+def test_plan_with_many_sequences():
+    # more sequences than one workgroup's threads: the two-pass path of the plan
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(1, 3000, size=2500).astype(np.int32)
+    ctx[::97] = 0                                           # a few invalid lengths
+    MB = 3000 // 16 + 1
+    cl = torch.as_tensor(ctx, device="cuda")
+    P = 512
+    ws = torch.zeros(pkv.workspace_bytes(len(ctx), 1, 64, 16, MB, P), dtype=torch.uint8,
+                     device="cuda")
+    pkv.paged_attention_plan(cl, ws, 16, MB, P)
+    torch.cuda.synchronize()
+    count, raw = _plan_bytes(ws)
+    items = np.frombuffer(raw, dtype=np.int32).reshape(count, 4)
+    expect = sum(-(-int(c) // P) if c >= 1 else 1 for c in ctx)
+    assert count == expect
+    assert len({(int(a), int(b)) for a, b in items[:, :2]}) == count
+    sizes = [min(P, int(c) - int(p) * P) if c >= 1 else P for _, p, c, _ in items]
+    partial = [k for k, z in enumerate(sizes) if z < P]
+    assert all(z == P for z in sizes[:partial[0]])
+    cls = [((P - sizes[k]) * 8) // P for k in partial]
+    assert cls == sorted(cls)
+
+
+@pytest.mark.parametrize("nseq", [5, 600])
+def test_prologue_equals_separate_calls(nseq):
+    rng = np.random.default_rng(nseq)
+    ctx = rng.integers(1, 4000, size=nseq)
+    b = build_batch(spec_of(NB=nseq * 260 + 64), ctx, device="cuda")
+    bt, cl = device_meta(b)
+    NB, BS = b.key_cache.shape[:2]
+    P = 512
+    # separate calls
+    kc1, vc1 = b.key_cache.clone(), b.value_cache.clone()
+    ws1 = pkv.alloc_workspace(b.query, bt, BS, P)
+    s1 = pkv.slot_mapping(bt, cl, BS, NB)
+    pkv.kv_cache_write(b.key, b.value, kc1, vc1, s1)
+    pkv.paged_attention_plan(cl, ws1, BS, bt.shape[1], P)
+    # one launch
+    kc2, vc2 = b.key_cache.clone(), b.value_cache.clone()
+    ws2 = pkv.alloc_workspace(b.query, bt, BS, P)
+    s2 = pkv.decode_prologue(bt, cl, b.key, b.value, kc2, vc2, ws2, P)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+    assert _plan_bytes(ws1) == _plan_bytes(ws2)
+    # and attention run on either plan gives the same bits
+    o1, _ = pkv.paged_attention_partition(b.query, kc1, vc1, bt, cl, b.scale, P, workspace=ws1)
+    pkv.paged_attention_reduce(o1, cl, ws1, BS, bt.shape[1], P)
+    o2 = pkv.paged_attention_decode(b.query, kc2, vc2, bt, cl, b.scale, P)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o1), bits(o2))
