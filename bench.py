@@ -32,6 +32,33 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+# Sources the partition kernel is built from: stored traffic counters are used only
+# while these are unchanged.
+KERNEL_SOURCES = ("paged_attention.hip", "pkv_device.hpp", "pkv_launch.hpp", "pkv_plan.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_attention_partition_llama3_8b.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_441_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, partition_size: int):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter runs,
+    or None when they were taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload
+            or t.get("partition_size") != partition_size):
+        return None
+    return t.get("traffic_bytes_per_launch")
 METRIC = "paged-attn decode KV HBM GB/s (% of peak) and tokens/s at batch×ctx, 1 GPU"
 
 
@@ -195,7 +222,9 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(spec.name, P),
+            "traffic_unit": "bytes per launch (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, "
+                            "factors from a plain 1 GiB copy)",
         },
         "device": torch.cuda.get_device_name(dev),
         "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
