@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 # Sources the partition kernel is built from: stored traffic counters are used only
 # while these are unchanged.
-KERNEL_SOURCES = ("paged_attention.hip", "pkv_device.hpp", "pkv_launch.hpp", "pkv_plan.hpp")
+KERNEL_SOURCES = ("paged_attention.hip", "paged_attention_stream.hip", "pkv_device.hpp",
+                  "pkv_launch.hpp", "pkv_plan.hpp", "pkv_tile.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_attention_partition_llama3_8b.json")
 
 
@@ -70,8 +71,10 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama3_8b")
-    ap.add_argument("--partition-size", type=int, default=0,
-                    help="tokens per context partition (0: the workload's own, 512)")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per context partition; 0 selects the balanced split "
+                         "(equal shares of the tile list per workgroup); default: the "
+                         "workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle runs on (0: the whole batch)")
@@ -129,7 +132,7 @@ def main(argv=None) -> int:
     t_gen = time.perf_counter()
     b = make_config(args.config, device=dev)
     spec = b.spec
-    P = args.partition_size or spec.partition_size
+    P = spec.partition_size if args.partition_size is None else args.partition_size
     B, H, Hkv, D, BS, NB = (b.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim,
                             spec.block_size, spec.num_blocks)
     MB = b.max_blocks_per_seq
@@ -219,7 +222,8 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_partition_kernel",
+            "kernel": "paged_attention_stream_kernel" if P == 0 else
+                      "paged_attention_partition_kernel",
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

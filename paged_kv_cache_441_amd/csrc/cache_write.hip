@@ -68,10 +68,15 @@ __global__ __launch_bounds__(kPrologueThreads) void decode_prologue_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ key_cache,
     uint4* __restrict__ value_cache, int32_t* __restrict__ slot_mapping, int num_seqs,
     int max_blocks_per_seq, int block_shift, int64_t num_blocks, int chunks_per_row,
-    int partition_size, int4* __restrict__ plan_items, int* __restrict__ plan_count) {
+    int partition_size, int4* __restrict__ plan_items, int* __restrict__ plan_count,
+    bool balanced, int* __restrict__ tile_cum, int* __restrict__ tile_hdr) {
   if (blockIdx.x == 0) {
-    build_plan<kPrologueThreads>(context_lens, num_seqs, partition_size,
-                                 max_blocks_per_seq << block_shift, plan_items, plan_count);
+    if (balanced)
+      build_tile_plan<kPrologueThreads>(context_lens, num_seqs, max_blocks_per_seq << block_shift,
+                                        tile_cum, tile_hdr);
+    else
+      build_plan<kPrologueThreads>(context_lens, num_seqs, partition_size,
+                                   max_blocks_per_seq << block_shift, plan_items, plan_count);
     return;
   }
   const int t = blockIdx.x - 1;
@@ -94,13 +99,14 @@ hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* co
                                   void* value_cache, int32_t* slot_mapping, int num_seqs,
                                   int max_blocks_per_seq, int block_shift, int64_t num_blocks,
                                   int row_bytes, int partition_size, int4* plan_items,
-                                  int* plan_count, hipStream_t stream) {
+                                  int* plan_count, bool balanced, int* tile_cum, int* tile_hdr,
+                                  hipStream_t stream) {
   hipLaunchKernelGGL(decode_prologue_kernel, dim3(num_seqs + 1), dim3(kPrologueThreads), 0, stream,
                      block_tables, context_lens, static_cast<const uint4*>(key),
                      static_cast<const uint4*>(value), static_cast<uint4*>(key_cache),
                      static_cast<uint4*>(value_cache), slot_mapping, num_seqs, max_blocks_per_seq,
                      block_shift, num_blocks, row_bytes / 16, partition_size, plan_items,
-                     plan_count);
+                     plan_count, balanced, tile_cum, tile_hdr);
   return hipGetLastError();
 }
 

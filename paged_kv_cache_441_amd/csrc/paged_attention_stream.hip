@@ -1,0 +1,672 @@
+// PagedAttention decode, balanced mode: a streaming partition stage and its merge.
+//
+// What is computed is the same as in paged_attention.hip (page "vllm源码分析：我是
+// 如何一步步读懂PagedAttention核心实现的？", 第三讲, and page "vLLM PagedAttention 原理与
+// 源码深度解析", section 5.3): per sequence and query head, scaled dot products with
+// the context's keys found through the block table, a softmax, the weighted sum of
+// the values.  Splitting a context into pieces merged by log-sum-exp leaves the
+// result unchanged; where the pieces fall is this design's choice.
+//
+// Work split.  All (sequence, tile) pairs, a tile being 16 consecutive tokens of one
+// sequence, form one ordered list; each sequence's tiles are preceded by kSeqCost
+// positions that stand for the fixed cost of starting and closing a sequence, so
+// that shares crossing many short sequences get fewer tiles (the tile plan holds
+// the prefix sums).  The grid has as many workgroups per kv-head group as the GPU
+// holds at once, and workgroup w takes the w-th of that many equal contiguous
+// shares of the list.  It streams
+// through its share without a break: the copies of the next tile are in flight
+// while a tile is computed, also across sequence boundaries, and every workgroup
+// ends at about the same time.  The run of one sequence inside one share is a
+// segment.  A segment that is a whole sequence writes its output directly; the
+// others write their (m, l, o) record under the label w + sequence (labels grow
+// along the list, so they are unique), and the merge kernel combines a sequence's
+// records in share order.
+//
+// How the bytes move.  One wave per kv head of the workgroup's group of HW heads.
+// A tile is the 16 token rows of the HW heads' keys and values, HW*D*elem bytes per
+// row, which the heads of one block row hold contiguously (the whole 2 KiB row of
+// a Llama-3-8B-shaped cache).  The workgroup copies it from HBM straight into LDS
+// with 16-byte direct-to-LDS loads, each wave instruction covering 1 KiB of
+// consecutive bytes, so every token row is fetched whole and at once.  On MI355X
+// this reads the batch's blocks at up to 6.2 TB/s, against 5.5-5.9 TB/s when each
+// head's 256-byte pieces are read by a workgroup of their own.
+//
+// LDS image of a tile: row r at r*ROW bytes; its 16-byte slots are XOR-swizzled
+// (slot j of the row is stored at j ^ (r & 15)), so that sixteen lanes reading the
+// same slot of sixteen rows (the MFMA key operand) or sixteen slots of one row (the
+// value reads) hit sixteen different bank groups.  The swizzle is done on the
+// global side: each lane fetches the global slot that belongs in its LDS slot.
+//
+// NBUF tiles rotate through distinct LDS buffers.  Per tile: issue the copies of
+// the tile NBUF - 1 ahead, wait for this wave's copies of the tile, barrier, compute
+// the tile from LDS: Q.K^T on the matrix cores (the GQA group of the wave's head as
+// the A operand), online softmax in the base-2 exponent domain, P.V on the VALU in
+// fp32; barrier.  While a wave waits for a tile, the tiles after it are already in
+// flight.  No atomics: results do not depend on timing.
+#include "pkv_device.hpp"
+#include "pkv_launch.hpp"
+#include "pkv_plan.hpp"
+#include "pkv_tile.hpp"
+
+#include <atomic>
+
+namespace pkv {
+
+#define PKV_AS_GLOBAL(p) ((const void __attribute__((address_space(1)))*)(p))
+#define PKV_AS_LOCAL(p) ((void __attribute__((address_space(3)))*)(p))
+
+// Reads through the constant address space become scalar loads when the address is
+// wave-uniform; used for data no kernel of this launch writes (tables, lengths, the
+// tile plan), so their waits do not hold up the tile copies in flight.
+typedef const int32_t __attribute__((address_space(4))) cint32;
+
+// s_waitcnt immediate with only the vector-memory count constrained (gfx9 layout:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// A workgroup barrier with no memory fence: the fence of __syncthreads would wait
+// for every outstanding copy, including the ones meant to stay in flight.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <typename T, int D, int HW, int TOK>
+struct Stage {
+  static constexpr int kRowBytes = HW * D * T::kElemBytes;   // one token row of the HW heads
+  static constexpr int kSlots = kRowBytes / 16;               // 16-byte slots per row
+  static constexpr int kSwz = kSlots >= 16 ? 15 : kSlots - 1;
+  static constexpr int kTileBytes = TOK * kRowBytes;          // per cache
+  static constexpr int kTileSlots = kTileBytes / 16;
+  static constexpr int kCopies = kTileBytes / (HW * 1024);    // 1 KiB wave copies per cache
+  static_assert(kTileBytes % (HW * 1024) == 0, "a tile splits into 1 KiB wave copies");
+  static_assert(kSlots >= 8, "rows of at least 128 bytes");
+};
+
+// Share w of the tile list is [floor(w * total / nwg), floor((w + 1) * total / nwg)).
+// The share holding tile j:
+__device__ __forceinline__ int share_of(int64_t j, int nwg, int total) {
+  return (int)(((j + 1) * nwg - 1) / total);
+}
+
+// Shares are empty when there are more workgroups than tiles.
+__device__ __forceinline__ bool share_nonempty(int w, int nwg, int total) {
+  return (int64_t)w * total / nwg < (int64_t)(w + 1) * total / nwg;
+}
+
+#ifndef PKV_STREAM_NBUF
+#define PKV_STREAM_NBUF 2
+#endif
+
+template <typename T, int D, int G, int HW, int NBUF>
+__global__ __launch_bounds__(HW * kWave)
+void paged_attention_stream_kernel(AttentionArgs a) {
+  constexpr int TOK = kTileTokens;
+  using Geo = Geometry<T, D, G>;
+  using St = Stage<T, D, HW, TOK>;
+  constexpr int EPL = Geo::kEPL;
+  constexpr int NCH = Geo::kChunksPerRow;   // 16-byte chunks of one head's row
+  constexpr int QKC = Geo::kQkChunks;
+  constexpr int RPS = Geo::kRowsPerStep;
+  constexpr int STEPS = TOK / RPS;
+  constexpr int EB = T::kElemBytes;
+  constexpr int L = 2 * St::kCopies;        // copy instructions per wave per tile
+  constexpr int NS = St::kTileSlots;
+  static_assert(TOK % RPS == 0 && TOK <= 16, "tile rows");
+  static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
+
+  // Distinct objects per buffer, so that reads of one buffer are never made to wait
+  // for copies into another.
+  __shared__ uint4 kb0[NS], vb0[NS], kb1[NS], vb1[NS];
+  __shared__ uint4 kb2[NBUF > 2 ? NS : 1], vb2[NBUF > 2 ? NS : 1];
+  __shared__ uint4 kb3[NBUF > 3 ? NS : 1], vb3[NBUF > 3 ? NS : 1];
+  __shared__ float p_lds[HW][16][G];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwg = gridDim.x;                // workgroups per kv-head group
+  const int w = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int B = a.num_seqs;
+  const int H = a.num_kv_heads * G;
+  const int g = hg * HW + wave;             // this wave's kv head
+
+  cint32* cum = (cint32*)a.tile_cum;
+  cint32* ctx_of = (cint32*)a.context_lens;
+  cint32* tables = (cint32*)a.block_tables;
+  const int total = ((cint32*)a.tile_hdr)[0];
+  if (w == 0 && hg == 0 && threadIdx.x == 0) a.tile_hdr[1] = nwg;   // for the merge
+  const int64_t start = (int64_t)w * total / nwg;
+  const int64_t end = (int64_t)(w + 1) * total / nwg;
+  if (start >= end) return;
+
+  // The sequence holding position `start`: the last i in [0, B] with cum[i] <=
+  // start (sequences without tiles share their cum value with the next one).  A
+  // 64-way search, one vector load per round.
+  int lo = 0, len = B + 1;
+  while (len > 1) {
+    const int step = (len + kWave - 1) / kWave;
+    const int i = lo + lane * step;
+    const bool ok = i < lo + len && a.tile_cum[i] <= start;
+    const int k = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
+    const int nlo = lo + (k - 1) * step;
+    len = min(step, lo + len - nlo);
+    lo = nlo;
+  }
+  const int seq0 = lo;
+
+  const int quarter = lane >> 4;   // MFMA operand k-group / output row group
+  const int col = lane & 15;       // MFMA A row (head) and B column (token)
+  const int rg = lane / NCH;       // value row within a step
+  const int li = lane % NCH;       // 16-byte chunk within a head's value row
+
+  // Copy geometry.  Copy instruction i of this wave fills LDS slots
+  // [(i*HW + wave)*64, +64) of the tile image; this lane's slot is row r, slot p,
+  // and it fetches the global slot p ^ (r & swz) of that row.
+  const int64_t row_stride = (int64_t)a.num_kv_heads * D * EB;   // between tokens of a block
+  uint32_t copy_off[St::kCopies];
+#pragma unroll
+  for (int i = 0; i < St::kCopies; ++i) {
+    const int s = (i * HW + wave) * kWave + lane;
+    const int r = s / St::kSlots;
+    const int p = s % St::kSlots;
+    copy_off[i] = (uint32_t)(r * row_stride) + (uint32_t)((p ^ (r & St::kSwz)) * 16);
+  }
+  const char* kcache = static_cast<const char*>(a.key_cache) + (int64_t)hg * St::kRowBytes;
+  const char* vcache = static_cast<const char*>(a.value_cache) + (int64_t)hg * St::kRowBytes;
+  const int shift = a.block_shift;
+  const int bs_mask = (1 << shift) - 1;
+  const int MB = a.max_blocks_per_seq;
+  const int num_blocks = (int)a.num_blocks;               // the ABI keeps it below 2^31
+  const float kNegInf = -__builtin_inff();
+
+  // A cursor over the real tiles of this share: sequence s, tile t, tiles of the
+  // sequence nt, and stop, the end of the share's part of the sequence (t < stop
+  // while the cursor is valid).  Sequence i's real tile t sits at position
+  // cum[i] + kSeqCost + t of the list.
+  struct Cursor {
+    int s, t, nt, stop;
+  };
+  // Moves c to the next sequence with real tiles in this share, or invalidates it.
+  auto next_seq = [&](Cursor& c) {
+    int cs = cum[c.s + 1];
+    for (;;) {
+      ++c.s;
+      if (c.s >= B || cs + kSeqCost >= end) {
+        c.t = c.stop = 0;
+        return;
+      }
+      const int cn = cum[c.s + 1];
+      if (cn > cs) {
+        c.t = 0;
+        c.nt = cn - cs - kSeqCost;
+        c.stop = min(c.nt, (int)(end - cs - kSeqCost));
+        return;
+      }
+      cs = cn;
+    }
+  };
+  auto first_cursor = [&](Cursor& c) {
+    const int cs = cum[seq0];
+    c.s = seq0;
+    c.nt = cum[seq0 + 1] - cs - kSeqCost;
+    c.t = max(0, (int)(start - cs - kSeqCost));
+    c.stop = min(c.nt, (int)(end - cs - kSeqCost));
+    if (c.t >= c.stop) next_seq(c);
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.t == c.stop) next_seq(c);
+  };
+
+  // ---- issue side: the copies of the next tile of the share ----------------------
+  Cursor ic;
+  first_cursor(ic);
+  // Copies of the tile under the issue cursor into (kb, vb), then advance.  Past the
+  // share's end, or behind an invalid block id, pool block 0 is copied instead:
+  // always in bounds, and the copy count per tile stays fixed, which the wait counts
+  // rely on.  bad_pipe bit k: the tile issued k issues ago sat behind an invalid
+  // block id.
+  unsigned bad_pipe = 0;
+  auto issue = [&](uint4* kb, uint4* vb) {
+    int64_t base = 0;
+    bad_pipe <<= 1;
+    if (ic.t < ic.stop) {
+      const int tok0 = ic.t * TOK;
+      const int32_t blk = tables[(int64_t)ic.s * MB + (tok0 >> shift)];
+      if (blk >= 0 && blk < num_blocks)
+        base = (((int64_t)blk << shift) + (tok0 & bs_mask)) * row_stride;
+      else
+        bad_pipe |= 1u;
+      advance(ic);
+    }
+    char* kd = reinterpret_cast<char*>(kb) + wave * 1024;
+    char* vd = reinterpret_cast<char*>(vb) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < St::kCopies; ++i)
+      __builtin_amdgcn_global_load_lds(PKV_AS_GLOBAL(kcache + base + copy_off[i]),
+                                       PKV_AS_LOCAL(kd + i * HW * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < St::kCopies; ++i)
+      __builtin_amdgcn_global_load_lds(PKV_AS_GLOBAL(vcache + base + copy_off[i]),
+                                       PKV_AS_LOCAL(vd + i * HW * 1024), 16, 0, 0);
+  };
+
+  // ---- compute side ------------------------------------------------------------------
+  Cursor cc;
+  first_cursor(cc);
+  if (cc.t >= cc.stop) return;           // only sequence overheads in this share
+  int cctx = ctx_of[cc.s];
+  bool seg_from_zero = cc.t == 0;        // the segment began at the sequence's first tile
+  int seg_bad = 0;
+
+  // Query rows of this kv head's group as the MFMA A operand.  Row m holds query
+  // head m % G: the rows past G repeat real ones and their scores are never used,
+  // so every lane loads unconditionally and the load's wait can stay where the
+  // first MFMA needs it (a masked load would be waited for at once, draining the
+  // copies in flight).
+  uint4 qa[QKC];
+  auto load_query = [&](int s) {
+    const char* qrow = static_cast<const char*>(a.query) +
+                       ((int64_t)s * H + g * G + col % G) * D * EB;
+#pragma unroll
+    for (int c = 0; c < QKC; ++c)
+      qa[c] = *reinterpret_cast<const uint4*>(qrow + (4 * c + quarter) * 16);
+  };
+
+  float m_run[G];
+  float acc[G][EPL];
+  float l_lane[4];
+  auto reset = [&]() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_run[h] = kNegInf;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_lane[j] = 0.f;
+    seg_bad = 0;
+  };
+
+  // Scores, probabilities and P.V for the current tile.  The probabilities are
+  // taken relative to a reference m_run per head that is raised only when a
+  // tile's maximum exceeds it by more than 2^kRebase (then the accumulators are
+  // rescaled); in between they stay below 2^kRebase.  Any reference gives the same
+  // normalised result; this one keeps the rescaling off almost every tile.
+  auto compute = [&](const uint4* kb, const uint4* vb, bool bad) {
+    constexpr float kRebase = 8.f;
+    const int tok0 = cc.t * TOK;
+    const int ntok = min(TOK, cctx - tok0);
+    seg_bad |= bad;
+    // key operand: this lane's column is token kr of the tile (columns past TOK
+    // repeat rows; they are masked out below)
+    const int kr = col & (TOK - 1);
+    uint4 kk[QKC];
+#pragma unroll
+    for (int c = 0; c < QKC; ++c)
+      kk[c] = kb[kr * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ (kr & St::kSwz))];
+    const floatx4 s4 = tile_scores<T, QKC>(qa, kk);
+    const bool live = col < ntok;
+    float sc[4];
+    int gkey[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = live ? s4[j] * a.scale_log2 : kNegInf;
+      gkey[j] = row_max_key<TOK>(float_key(sc[j]));
+    }
+    float alpha[G];
+    bool rebase = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float gm = key_float(__builtin_amdgcn_readlane(gkey[h & 3], 16 * (h >> 2)));
+      const bool up = gm > m_run[h] + kRebase;   // uniform across the wave
+      const float mn = up ? gm : m_run[h];
+      alpha[h] = up ? fast_exp2(m_run[h] - mn) : 1.f;
+      rebase |= up;
+      m_run[h] = mn;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mrow, arow;
+      if constexpr (G <= 4) {
+        mrow = j < G ? m_run[j < G ? j : 0] : 0.f;
+        arow = j < G ? alpha[j < G ? j : 0] : 1.f;
+      } else {
+        mrow = quarter == 0 ? m_run[j] : m_run[(4 + j) % G];
+        arow = quarter == 0 ? alpha[j] : alpha[(4 + j) % G];
+      }
+      sc[j] = fast_exp2(sc[j] - mrow);
+      l_lane[j] = rebase ? l_lane[j] * arow + sc[j] : l_lane[j] + sc[j];
+    }
+    if (rebase) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+    }
+    if (quarter < Geo::kQuarters) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * quarter + j < G) p_lds[wave][col][(4 * quarter + j) % G] = sc[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool full = ntok == TOK;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int n = s * RPS + rg;
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = p_lds[wave][n][h];
+      float v[EPL];
+      unpack_chunk<T>(vb[n * St::kSlots + ((wave * NCH + li) ^ (n & St::kSwz))], v);
+      if (!full && n >= ntok) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // End of a segment: fold the row groups, normalise, store (the output itself for
+  // a whole sequence, else the record under label w + sequence), 16 bytes at a time.
+  auto finish = [&](bool whole) {
+#pragma unroll
+    for (int off = NCH; off < kWave; off <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_lane[j] = row16_sum(l_lane[j]);
+    float l_head[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_head[h] = readlane(l_lane[h & 3], 16 * (h >> 2));
+    if (lane >= NCH) return;
+    float res[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / l_head[h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) res[h][e] = seg_bad ? __builtin_nanf("") : acc[h][e] * inv;
+    }
+    if (whole) {
+      const int64_t row0 = (int64_t)cc.s * H + g * G;
+      if (a.out_bf16) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + row0 * D + li * EPL;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4) {
+            uint2 v;
+            v.x = f32_to_bf16_rne(res[h][e]) | (uint32_t)f32_to_bf16_rne(res[h][e + 1]) << 16;
+            v.y = f32_to_bf16_rne(res[h][e + 2]) | (uint32_t)f32_to_bf16_rne(res[h][e + 3]) << 16;
+            *reinterpret_cast<uint2*>(o + h * D + e) = v;
+          }
+      } else {
+        float* o = static_cast<float*>(a.out) + row0 * D + li * EPL;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(o + h * D + e) =
+                make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
+      }
+    } else {
+      const int64_t rec0 = ((int64_t)w + cc.s) * H + g * G;
+      float* o = a.ws_o + rec0 * D + li * EPL;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+          *reinterpret_cast<float4*>(o + h * D + e) =
+              make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
+      if (lane < G) {
+        // lane h < G writes head h's (m, l); m_run and l_head are uniform
+        float mh = m_run[0], lh = l_head[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) {
+          mh = lane == h ? m_run[h] : mh;
+          lh = lane == h ? l_head[h] : lh;
+        }
+        a.ws_m[rec0 + lane] = mh;
+        a.ws_l[rec0 + lane] = lh;
+      }
+    }
+  };
+
+  reset();
+  load_query(cc.s);
+
+  // One step of the ring: issue the copies of the tile NBUF - 1 ahead into the
+  // buffer freed at the end of the previous step, wait for this wave's copies of
+  // tile j (the later tiles stay in flight), barrier (every wave's copies of tile j
+  // have landed), compute tile j, barrier (every wave is done reading its buffer),
+  // close the segment where it ends.
+#define PKV_STREAM_STEP(KB, VB, KF, VF)                                   \
+  if (cc.t >= cc.stop) break;                                             \
+  issue(KF, VF);                                                          \
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NBUF - 1) * L));                 \
+  bare_barrier();                                                         \
+  compute(KB, VB, (bad_pipe >> (NBUF - 1)) & 1u);                         \
+  bare_barrier();                                                         \
+  if (cc.t == cc.stop - 1) {                                              \
+    /* the share's part of this sequence ends with this tile */           \
+    finish(seg_from_zero && cc.stop == cc.nt);                            \
+    reset();                                                              \
+    next_seq(cc);                                                         \
+    seg_from_zero = true;                                                 \
+    if (cc.t < cc.stop) {                                                 \
+      cctx = ctx_of[cc.s];                                                \
+      load_query(cc.s);                                                   \
+    }                                                                     \
+  } else {                                                                \
+    ++cc.t;                                                               \
+  }
+
+  if constexpr (NBUF == 2) {
+    issue(kb0, vb0);
+    for (;;) {
+      PKV_STREAM_STEP(kb0, vb0, kb1, vb1)
+      PKV_STREAM_STEP(kb1, vb1, kb0, vb0)
+    }
+  } else if constexpr (NBUF == 3) {
+    issue(kb0, vb0);
+    issue(kb1, vb1);
+    for (;;) {
+      PKV_STREAM_STEP(kb0, vb0, kb2, vb2)
+      PKV_STREAM_STEP(kb1, vb1, kb0, vb0)
+      PKV_STREAM_STEP(kb2, vb2, kb1, vb1)
+    }
+  } else {
+    issue(kb0, vb0);
+    issue(kb1, vb1);
+    issue(kb2, vb2);
+    for (;;) {
+      PKV_STREAM_STEP(kb0, vb0, kb3, vb3)
+      PKV_STREAM_STEP(kb1, vb1, kb0, vb0)
+      PKV_STREAM_STEP(kb2, vb2, kb1, vb1)
+      PKV_STREAM_STEP(kb3, vb3, kb2, vb2)
+    }
+  }
+#undef PKV_STREAM_STEP
+  // the ring's last copies (of block 0) land before the wave ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+#undef PKV_AS_GLOBAL
+#undef PKV_AS_LOCAL
+
+// ---- tile plan ---------------------------------------------------------------------
+
+__global__ __launch_bounds__(kPlanThreads) void tile_plan_kernel(AttentionArgs a) {
+  build_tile_plan<kPlanThreads>(a.context_lens, a.num_seqs, a.max_blocks_per_seq << a.block_shift,
+                                a.tile_cum, a.tile_hdr);
+}
+
+size_t tile_plan_bytes(int64_t num_seqs) {
+  return 256 + ((size_t)(num_seqs + 1) * sizeof(int) + 255) / 256 * 256;
+}
+
+hipError_t launch_tile_plan(const AttentionArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---- merge of the segments ------------------------------------------------------------
+// One wave per (sequence, query head) row.  Sequences without tiles (invalid
+// context length) get NaN rows; a sequence inside one share was written by the
+// partition stage; otherwise its records, labels w + sequence for the non-empty
+// shares w it spans, are merged in share order.  Lane groups take every KGW-th record, U at a
+// time; the groups are combined in a fixed order, so the result does not depend on
+// timing.
+template <int D>
+__global__ __launch_bounds__(256) void paged_attention_stream_reduce_kernel(AttentionArgs a) {
+  constexpr int LPR = D / 4;             // lanes per record (float4 each)
+  constexpr int KGW = kWave / LPR;       // records per wave round
+  constexpr int U = 4;                   // rounds in flight
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= (int64_t)a.num_seqs * a.num_heads) return;
+  const int H = a.num_heads;
+  const int seq = (int)(row / H);
+  const int qh = (int)(row % H);
+  const int kg = lane / LPR;
+  const int lr = lane % LPR;
+  const int ctx = a.context_lens[seq];
+  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+  if (ctx < 1 || ctx > max_ctx) {
+    if (kg == 0) {
+      const float nan = __builtin_nanf("");
+      store_row4(a, row * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
+    }
+    return;
+  }
+  const int total = a.tile_hdr[0];
+  const int nwg = a.tile_hdr[1];
+  // shares holding the sequence's first and last real tiles
+  const int w0 = share_of((int64_t)a.tile_cum[seq] + kSeqCost, nwg, total);
+  const int w1 = share_of((int64_t)a.tile_cum[seq + 1] - 1, nwg, total);
+  if (w0 == w1) return;
+  Running r{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int w = w0 + kg; w <= w1; w += KGW * U) {
+    float m[U], l[U];
+    float4 o[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ww = w + u * KGW;
+      live[u] = ww <= w1 && share_nonempty(ww, nwg, total);   // empty shares wrote nothing
+      const int64_t rec = ((int64_t)ww + seq) * H + qh;
+      m[u] = live[u] ? a.ws_m[rec] : 0.f;
+      l[u] = live[u] ? a.ws_l[rec] : 0.f;
+      o[u] = live[u] ? reinterpret_cast<const float4*>(a.ws_o + rec * D)[lr]
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    accumulate(r, m, l, o, live);
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    Running s;
+    s.m = __shfl_xor(r.m, off);
+    s.l = __shfl_xor(r.l, off);
+    s.o.x = __shfl_xor(r.o.x, off);
+    s.o.y = __shfl_xor(r.o.y, off);
+    s.o.z = __shfl_xor(r.o.z, off);
+    s.o.w = __shfl_xor(r.o.w, off);
+    // both lanes of a pair merge the same two values in the same order
+    if (lane & off) { const Running t = r; r = s; s = t; }
+    merge_into(r, s);
+  }
+  if (kg == 0) store_row4(a, row * D + lr * 4, r);
+}
+
+hipError_t launch_attention_stream_reduce(const AttentionArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_heads * a.num_seqs;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(paged_attention_stream_reduce_kernel<64>, grid, dim3(256), 0, stream, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL(paged_attention_stream_reduce_kernel<128>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---- dispatch ------------------------------------------------------------------
+
+// Compute units of the current device, looked up once per device.
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <typename T, int D, int G, int HW>
+static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream) {
+  auto kernel = paged_attention_stream_kernel<T, D, G, HW, PKV_STREAM_NBUF>;
+  // Workgroups one compute unit holds at once, from the kernel's own resource use.
+  static const int per_cu = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, HW * kWave, 0) != hipSuccess)
+      n = 1;
+    return n > 0 ? n : 1;
+  }();
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int hgroups = a.num_kv_heads / HW;
+  const int nwg = max(1, min(kMaxStreamWgs, per_cu * cus / hgroups));
+  hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(HW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+#ifndef PKV_STREAM_MAX_ROW
+#define PKV_STREAM_MAX_ROW 2048
+#endif
+
+// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the kv heads and keeps
+// a token row of the group within PKV_STREAM_MAX_ROW bytes.
+template <typename T, int D, int G>
+static hipError_t launch_stream_hw(const AttentionArgs& a, hipStream_t stream) {
+  constexpr int kRow = D * T::kElemBytes;
+  if constexpr (8 * kRow <= PKV_STREAM_MAX_ROW)
+    if (a.num_kv_heads % 8 == 0) return launch_stream_shape<T, D, G, 8>(a, stream);
+  if constexpr (4 * kRow <= PKV_STREAM_MAX_ROW)
+    if (a.num_kv_heads % 4 == 0) return launch_stream_shape<T, D, G, 4>(a, stream);
+  if (a.num_kv_heads % 2 == 0) return launch_stream_shape<T, D, G, 2>(a, stream);
+  return launch_stream_shape<T, D, G, 1>(a, stream);
+}
+
+template <typename T, int D>
+static hipError_t launch_stream_g(const AttentionArgs& a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_stream_hw<T, D, 1>(a, stream);
+    case 2: return launch_stream_hw<T, D, 2>(a, stream);
+    case 4: return launch_stream_hw<T, D, 4>(a, stream);
+    case 8: return launch_stream_hw<T, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream) {
+  if (a.kv_bf16) {
+    if (a.head_dim == 64) return launch_stream_g<BF16, 64>(a, stream);
+    if (a.head_dim == 128) return launch_stream_g<BF16, 128>(a, stream);
+  } else {
+    if (a.head_dim == 64) return launch_stream_g<F32, 64>(a, stream);
+    if (a.head_dim == 128) return launch_stream_g<F32, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

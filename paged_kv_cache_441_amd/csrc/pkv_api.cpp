@@ -32,8 +32,10 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
 }
 
 struct AttnShape {
+  bool balanced = false;    // partition_size 0: equal shares of the tile list per workgroup
   int64_t max_parts = 0;
   int partition = 0;
+  int64_t recs = 0;         // partial-result records (one per row of head_dim + 2 floats)
   size_t plan_bytes = 0;    // the work plan at the start of the workspace
   size_t ws_bytes = 0;      // plan + partition records
 };
@@ -46,20 +48,36 @@ pkv_status check_attention_shape(int32_t num_seqs, int32_t num_heads, int32_t he
       max_blocks_per_seq <= 0 || partition_size < 0)
     return PKV_ERR_INVALID_ARG;
   if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
-  const int P = partition_size == 0 ? 512 : partition_size;
-  if (P % block_size != 0 || P % 16 != 0) return PKV_ERR_INVALID_ARG;
   int64_t max_ctx = 0;
   if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX, &max_ctx)) return PKV_ERR_INVALID_ARG;
-  s->partition = P;
-  s->max_parts = (max_ctx + P - 1) / P;
   int64_t recs = 0, t = 0;
-  if (!mul_ok(num_seqs, num_heads, INT64_MAX / 8, &t) || !mul_ok(t, s->max_parts, INT64_MAX / 8, &recs))
-    return PKV_ERR_INVALID_ARG;
+  if (partition_size == 0) {
+    // Balanced: one record row per (segment label, head); labels < max workgroups + seqs.
+    s->balanced = true;
+    s->partition = 0;
+    s->max_parts = 1;
+    int64_t tiles = 0;
+    if (!mul_ok(num_seqs, (max_ctx + pkv::kTileTokens - 1) / pkv::kTileTokens + pkv::kSeqCost,
+                INT32_MAX / 2, &tiles))
+      return PKV_ERR_UNSUPPORTED;   // the tile list is indexed with int32
+    if (!mul_ok(int64_t{num_seqs} + pkv::kMaxStreamWgs, num_heads, INT64_MAX / 8, &recs))
+      return PKV_ERR_INVALID_ARG;
+    s->plan_bytes = pkv::tile_plan_bytes(num_seqs);
+  } else {
+    const int P = partition_size;
+    if (P % block_size != 0 || P % 16 != 0) return PKV_ERR_INVALID_ARG;
+    s->partition = P;
+    s->max_parts = (max_ctx + P - 1) / P;
+    if (!mul_ok(num_seqs, num_heads, INT64_MAX / 8, &t) ||
+        !mul_ok(t, s->max_parts, INT64_MAX / 8, &recs))
+      return PKV_ERR_INVALID_ARG;
+    int64_t items = 0;
+    if (!mul_ok(num_seqs, s->max_parts, INT32_MAX, &items)) return PKV_ERR_UNSUPPORTED;
+    s->plan_bytes = pkv::plan_bytes(num_seqs, s->max_parts);
+  }
   int64_t bytes = 0;
   if (!mul_ok(recs, int64_t{head_dim} + 2, INT64_MAX / 8, &bytes)) return PKV_ERR_INVALID_ARG;
-  int64_t items = 0;
-  if (!mul_ok(num_seqs, s->max_parts, INT32_MAX, &items)) return PKV_ERR_UNSUPPORTED;
-  s->plan_bytes = pkv::plan_bytes(num_seqs, s->max_parts);
+  s->recs = recs;
   s->ws_bytes = s->plan_bytes + static_cast<size_t>(bytes) * 4;
   return PKV_OK;
 }
@@ -68,6 +86,8 @@ void set_workspace(pkv::AttentionArgs* a, void* workspace, size_t plan_bytes, in
   char* ws = static_cast<char*>(workspace);
   a->plan_count = ws ? reinterpret_cast<int*>(ws) : nullptr;
   a->plan_items = ws ? reinterpret_cast<int4*>(ws + 256) : nullptr;
+  a->tile_hdr = ws ? reinterpret_cast<int*>(ws) : nullptr;
+  a->tile_cum = ws ? reinterpret_cast<int*>(ws + 256) : nullptr;
   float* f = ws ? reinterpret_cast<float*>(ws + plan_bytes) : nullptr;
   a->ws_m = f;
   a->ws_l = f ? f + recs : nullptr;
@@ -129,7 +149,8 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   a->max_parts = static_cast<int>(s.max_parts);
   a->kv_bf16 = kv_dtype == PKV_BF16;
   a->out_bf16 = out_dtype == PKV_BF16;
-  set_workspace(a, workspace, s.plan_bytes, int64_t{num_seqs} * num_heads * s.max_parts);
+  a->balanced = s.balanced;
+  set_workspace(a, workspace, s.plan_bytes, s.recs);
   return PKV_OK;
 }
 
@@ -230,7 +251,8 @@ pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* conte
   return hip_status(pkv::launch_decode_prologue(
       block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping, num_seqs,
       max_blocks_per_seq, log2_exact(block_size), num_blocks, static_cast<int>(row), s.partition,
-      a.plan_items, a.plan_count, static_cast<hipStream_t>(stream)));
+      a.plan_items, a.plan_count, s.balanced, a.tile_cum, a.tile_hdr,
+      static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
@@ -251,6 +273,7 @@ pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seq
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.partition_size = s.partition;
   a.max_parts = static_cast<int>(s.max_parts);
+  a.balanced = s.balanced;
   set_workspace(&a, workspace, s.plan_bytes, 0);
   return hip_status(pkv::launch_attention_plan(a, static_cast<hipStream_t>(stream)));
 }
@@ -308,7 +331,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
   if (st != PKV_OK) return st;
   st = hip_status(pkv::launch_attention_partition(a, s));
   if (st != PKV_OK) return st;
-  if (a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));
+  if (a.balanced || a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));
   return st;
 }
 

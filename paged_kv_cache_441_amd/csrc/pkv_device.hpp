@@ -78,6 +78,36 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Order-preserving integer keys of floats (any value but NaN): a signed integer
+// compare of the keys orders the floats, so maxima can use the integer max, which
+// needs no NaN canonicalisation and fuses with DPP lane moves.
+__device__ __forceinline__ int float_key(float x) {
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key_float(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int x) {
+  // all rows and banks enabled, so bound_ctrl never applies; it lets the move fuse
+  // into the instruction that consumes it
+  return __builtin_amdgcn_mov_dpp(x, kCtrl, 0xF, 0xF, true);
+}
+
+// Maximum of the keys over the first N lanes (N = 8 or 16) of every 16-lane row;
+// lanes 0..N-1 of each row receive it.
+template <int N>
+__device__ __forceinline__ int row_max_key(int k) {
+  static_assert(N == 8 || N == 16, "row span");
+  if constexpr (N == 16) k = max(k, dpp_i<kDppRowMirror>(k));
+  k = max(k, dpp_i<kDppRowHalfMirror>(k));
+  k = max(k, dpp_i<kDppQuadXor2>(k));
+  k = max(k, dpp_i<kDppQuadXor1>(k));
+  return k;
+}
+
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<kDppRowMirror>(x);
   x += dpp<kDppRowHalfMirror>(x);

@@ -15,12 +15,15 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
                               void* value_cache, const int32_t* slot_mapping, int num_tokens,
                               int row_bytes, int64_t num_slots, hipStream_t stream);
 
+// Builds the fixed-partition plan (plan_items, plan_count) or, when balanced, the
+// tile plan (tile_cum, tile_hdr).
 hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
                                   const void* key, const void* value, void* key_cache,
                                   void* value_cache, int32_t* slot_mapping, int num_seqs,
                                   int max_blocks_per_seq, int block_shift, int64_t num_blocks,
                                   int row_bytes, int partition_size, int4* plan_items,
-                                  int* plan_count, hipStream_t stream);
+                                  int* plan_count, bool balanced, int* tile_cum, int* tile_hdr,
+                                  hipStream_t stream);
 
 struct AttentionArgs {
   void* out;
@@ -46,15 +49,42 @@ struct AttentionArgs {
   float* ws_m;              // [num_seqs][num_heads][max_parts]
   float* ws_l;              // [num_seqs][num_heads][max_parts]
   float* ws_o;              // [num_seqs][num_heads][max_parts][head_dim]
+  // Balanced mode (partition_size 0): the tile plan, and the partial results of the
+  // segments, one record row per (segment label, query head).
+  bool balanced;
+  int* tile_hdr;            // [0] total tiles, [1] workgroups per kv-head group
+  int* tile_cum;            // [num_seqs + 1] tiles before each sequence
 };
+
+// Balanced mode: at most this many workgroups per kv-head group, so segment labels
+// (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.
+constexpr int kMaxStreamWgs = 1024;
+// Balanced mode: tokens per tile of the tile list.
+#ifndef PKV_TILE_TOKENS
+#define PKV_TILE_TOKENS 16
+#endif
+constexpr int kTileTokens = PKV_TILE_TOKENS;
+// Balanced mode: list positions charged per sequence on top of its tiles (the cost
+// of starting and closing a sequence, in tiles).
+#ifndef PKV_SEQ_COST
+#define PKV_SEQ_COST 1
+#endif
+constexpr int kSeqCost = PKV_SEQ_COST;
 
 // Workspace layout, in bytes from its start (all offsets 256-byte aligned):
 //   plan: count (int32) at 0, items (int4) at 256;
 //   then m, l and o records of the partitions (fp32).
 size_t plan_bytes(int64_t num_seqs, int64_t max_parts);
+// Balanced mode: header (256 bytes) and the tile prefix sums.
+size_t tile_plan_bytes(int64_t num_seqs);
 
 hipError_t launch_attention_plan(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_partition(const AttentionArgs& a, hipStream_t stream);
+// Balanced mode: the tile plan, the streaming partition stage (whole token rows
+// staged through LDS, equal shares of the tile list per workgroup) and its merge.
+hipError_t launch_tile_plan(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_attention_stream_reduce(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_reduce(const AttentionArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "pkv_device.hpp"
+#include "pkv_launch.hpp"
 
 namespace pkv {
 
@@ -137,6 +138,52 @@ __device__ void build_plan(const int32_t* __restrict__ context_lens, int num_seq
     }
   }
   if (threadIdx.x == 0) *count = total;
+}
+
+// ---- tile plan (balanced split) -------------------------------------------------------
+// In the balanced mode the attention work is the ordered list of all (sequence,
+// tile) pairs, a tile being kTileTokens consecutive tokens of one sequence, each
+// sequence's tiles preceded by kSeqCost positions that stand for its fixed cost;
+// the partition stage cuts the list into equal contiguous shares, one per
+// workgroup.  The plan is the exclusive prefix sum of the positions: cum[i]
+// positions precede sequence i (i = 0..num_seqs), and hdr[0] = cum[num_seqs] is
+// the total.  A sequence with an invalid context length has no positions.
+// (kTileTokens, kSeqCost: pkv_launch.hpp.)
+
+template <int NT>
+__device__ void build_tile_plan(const int32_t* __restrict__ context_lens, int num_seqs,
+                                int max_ctx, int* __restrict__ cum, int* __restrict__ hdr) {
+  __shared__ int lds[NT / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int carry = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += NT) {
+    const int i = c0 + threadIdx.x;
+    const int ctx = i < num_seqs ? context_lens[i] : 0;
+    const int x =
+        (ctx >= 1 && ctx <= max_ctx) ? (ctx + kTileTokens - 1) / kTileTokens + kSeqCost : 0;
+    int inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) lds[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int t = lds[w];
+      before += w < wave ? t : 0;
+      total += t;
+    }
+    if (i < num_seqs) cum[i] = carry + before + inc - x;
+    carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    cum[num_seqs] = carry;
+    hdr[0] = carry;
+  }
 }
 
 }  // namespace pkv

@@ -61,10 +61,20 @@ def _ws(B, H, D, NP):
     return plan + B * H * NP * (D + 2) * 4
 
 
+def _ws_balanced(B, H, D, max_wgs=1024):
+    plan = 256 + ((B + 1) * 4 + 255) // 256 * 256
+    return plan + (max_wgs + B) * H * (D + 2) * 4
+
+
 def test_workspace_bytes_formula(lib):
     # plan (256 + roundup256(B*NP*16)) + B * H * NP * (D + 2) * 4, NP = ceil(MB*BS/P)
     assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 512) == _ws(256, 32, 128, 16)
-    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == _ws(8, 32, 128, 256)
+    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 512) == _ws(8, 32, 128, 256)
+    # partition_size 0 (balanced split): tile plan 256 + roundup256((B + 1) * 4), then one
+    # record row per (segment label < 1024 + B, head)
+    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == _ws_balanced(8, 32, 128)
+    assert _ws_balanced(8, 32, 128) == 512 + 1032 * 32 * 130 * 4
+    assert lib.pkv_paged_attention_workspace_bytes(300, 4, 64, 16, 7, 0) == _ws_balanced(300, 4, 64)
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 512) == _ws(4, 4, 64, 1)
     assert _ws(4, 4, 64, 1) == 512 + 4 * 4 * 66 * 4
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 24) == 0     # P % 16

@@ -178,14 +178,15 @@ def test_bf16_output_is_rounded_fp32_result():
     assert torch.equal(bits(o16), bits(o32.to(torch.bfloat16)))
 
 
-def test_partition_then_reduce_equals_decode():
+@pytest.mark.parametrize("P", [512, 0])
+def test_partition_then_reduce_equals_decode(P):
     b = build_batch(spec_of(NB=2048), [3, 513, 2000, 5000], device="cuda")
-    slots, kc, vc, out = run_step(b)
+    slots, kc, vc, out = run_step(b, partition_size=P)
     bt, cl = device_meta(b)
-    ws = pkv.alloc_workspace(b.query, bt, 16, 512)
-    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], 512)
-    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512, workspace=ws)
-    pkv.paged_attention_reduce(out2, cl, ws, 16, bt.shape[1], 512)
+    ws = pkv.alloc_workspace(b.query, bt, 16, P)
+    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], P)
+    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, workspace=ws)
+    pkv.paged_attention_reduce(out2, cl, ws, 16, bt.shape[1], P)
     torch.cuda.synchronize()
     assert torch.equal(bits(out), bits(out2))
 
