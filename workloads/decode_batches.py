@@ -77,10 +77,11 @@ CONFIGS = {
     "llama2_7b": ConfigSpec("llama2_7b", 64, 32, 32, 128, 16, 16384, "bf16", 2048,
                             ("uniform", 128, 2048), 1),
     # One Llama-3-8B layer: GQA 32/8, D=128, bf16, lognormal contexts (median 1024,
-    # sigma 1.0 in log space), clipped to [16, 8192], 200k-block pool.  Partitions
-    # of 2048 tokens (the workload fixes none; 2048 measured fastest on MI355X).
+    # sigma 1.0 in log space), clipped to [16, 8192], 200k-block pool.  The workload
+    # fixes no partition size; it runs in the balanced split (partition_size 0),
+    # which measured fastest on MI355X.
     "llama3_8b": ConfigSpec("llama3_8b", 256, 32, 8, 128, 16, 200_000, "bf16", 8192,
-                            ("lognormal", 1024, 1.0, 16, 8192), 2, partition_size=2048),
+                            ("lognormal", 1024, 1.0, 16, 8192), 2, partition_size=0),
     # Long-context split decode: 8 sequences of 32k..128k tokens, partition 512.
     "long_ctx": ConfigSpec("long_ctx", 8, 32, 8, 128, 16, 65536, "bf16", 131072,
                            ("uniform", 32768, 131072), 3),
