@@ -7,10 +7,21 @@
  *   2. pkv_kv_cache_write          -- scatter the new tokens' K/V rows there
  *                                     (reshape_and_cache);
  *   3. pkv_paged_attention_decode  -- attention of each sequence's query over its
- *                                     whole paged context, split into context
- *                                     partitions that are merged by log-sum-exp
- *                                     (= pkv_paged_attention_partition followed by
- *                                     pkv_paged_attention_reduce).
+ *                                     whole paged context, split into pieces that
+ *                                     are merged by log-sum-exp (= the plan, the
+ *                                     partition and the reduce stages below).
+ *
+ * Two ways to split the contexts, chosen by partition_size:
+ *  - partition_size P > 0 (fixed partitions): sequence i is cut into partitions of
+ *    P tokens; one workgroup per (partition, kv head); longest partitions first.
+ *  - partition_size 0 (balanced split): the (sequence, 16-token tile) pairs of the
+ *    whole batch, plus one position per sequence for its fixed cost, form one list
+ *    that is cut into equal contiguous shares, one per workgroup of a grid the GPU
+ *    holds at once; each workgroup streams whole token rows of its kv-head group
+ *    through LDS.  Where the pieces of a sequence end therefore depends on the
+ *    whole batch (and on the GPU's compute-unit count), so a sequence's result
+ *    may differ between batches in the last bits of fp32; for one batch on one
+ *    GPU it is deterministic.
  *
  * Cache layout (both key_cache and value_cache), row-major, no padding:
  *     [num_blocks][block_size][num_kv_heads][head_dim]
@@ -142,12 +153,17 @@ pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* conte
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs (0 for invalid
- * arguments).  With P the effective partition size and
+ * arguments).  With fixed partitions of P tokens and
  * NP = ceil(max_blocks_per_seq*block_size / P), the workspace holds
  *   - the work plan: 256 bytes, then one 16-byte item per (sequence, partition),
  *     rounded up to 256 bytes:  256 + roundup256(num_seqs * NP * 16);
  *   - one (max, sum, partial output) fp32 record per (sequence, query head,
  *     partition):  num_seqs * num_heads * NP * (head_dim + 2) * 4.
+ * With the balanced split (partition_size 0) it holds
+ *   - the tile plan: 256 bytes of header, then num_seqs + 1 int32 prefix sums,
+ *     rounded up to 256 bytes:  256 + roundup256((num_seqs + 1) * 4);
+ *   - one record per (segment label, query head), labels below 1024 + num_seqs:
+ *     (1024 + num_seqs) * num_heads * (head_dim + 2) * 4.
  * Its contents need no initialisation and are scratch between calls.
  */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
@@ -170,10 +186,11 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  * softmax, weighted sum of V.  The max subtraction and the partition merge below
  * are not printed on the pages; they leave the result unchanged.)
  *
- * Long contexts are split into partitions of P = partition_size tokens, each
- * giving (m_k, l_k, o_k); the partitions are merged as
+ * Contexts are split into pieces (fixed partitions of P = partition_size tokens,
+ * or the segments of the balanced split when partition_size is 0), each giving
+ * (m_k, l_k, o_k); the pieces are merged in order as
  *     M = max m_k,  w_k = l_k exp(m_k - M),  out = sum w_k o_k / sum w_k.
- * A sequence with a single partition is written directly.
+ * A sequence in a single piece is written directly.
  *
  *   out           device [num_seqs][num_heads][head_dim], out_dtype (written)
  *   query         device [num_seqs][num_heads][head_dim], kv_dtype
@@ -182,8 +199,8 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *                 ceil(ctx/block_size) are never read
  *   context_lens  device int32 [num_seqs], 1 <= ctx <= max_blocks_per_seq*block_size
  *   scale         multiplies q.k (1/sqrt(head_dim) for standard attention)
- *   partition_size  P in tokens; 0 selects 512; must be a multiple of block_size
- *                 and of 16
+ *   partition_size  P in tokens, a multiple of block_size and of 16; or 0 for the
+ *                 balanced split
  *   workspace     device buffer of at least pkv_paged_attention_workspace_bytes()
  *
  * Supported: kv_dtype in {PKV_F32, PKV_BF16}; out_dtype in {PKV_F32, PKV_BF16}
@@ -211,23 +228,29 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
  * same arguments and workspace they produce exactly what
  * pkv_paged_attention_decode produces.
  *
- * pkv_paged_attention_plan writes the work list into the start of the workspace:
- * one item per (sequence, partition) that holds tokens -- whole partitions
- * first, then the partial last partitions from largest to smallest -- so that
- * the partition stage hands the longest work out first.  It reads only
- * context_lens; a plan stays valid for as long as context_lens, block_size,
- * max_blocks_per_seq, partition_size and num_seqs are unchanged (for example for
- * every layer of one decode step).  It needs workspace_bytes of at least the
- * plan part described above.
+ * pkv_paged_attention_plan writes the work plan into the start of the workspace.
+ * Fixed partitions: one item per (sequence, partition) that holds tokens -- whole
+ * partitions first, then the partial last partitions from largest to smallest --
+ * so that the partition stage hands the longest work out first.  Balanced split:
+ * the prefix sums of the sequences' list positions (ceil(ctx / 16) + 1 for a valid
+ * context, 0 otherwise) and their total.  It reads only context_lens; a plan stays
+ * valid for as long as context_lens, block_size, max_blocks_per_seq,
+ * partition_size and num_seqs are unchanged (for example for every layer of one
+ * decode step).  It needs workspace_bytes of at least the plan part described
+ * above.
  *
- * pkv_paged_attention_partition runs the planned work: it writes single-partition
- * sequences straight to `out` and every multi-partition sequence's per-partition
- * records to the workspace.  It checks the plan's items against num_seqs and the
- * partition count, so a stale plan yields wrong numbers, never an access outside
- * the buffers.
+ * pkv_paged_attention_partition runs the planned work: it writes sequences that
+ * fit in one piece straight to `out` and the records of the others to the
+ * workspace.  Fixed partitions: it checks the plan's items against num_seqs and
+ * the partition count, so a stale plan yields wrong numbers, never an access
+ * outside the buffers.  Balanced split: a stale plan likewise yields wrong numbers
+ * (tiles past a table row count as invalid blocks), never an access outside the
+ * buffers.
  *
- * pkv_paged_attention_reduce merges the partition records of multi-partition
- * sequences into `out`, in partition order.
+ * pkv_paged_attention_reduce merges the records of the sequences split into
+ * several pieces into `out`, in piece order.  With the balanced split it also
+ * writes the NaN rows of sequences with an invalid context length, so it must
+ * follow every partition stage there.
  */
 pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
                                     int32_t block_size, int32_t max_blocks_per_seq,

@@ -175,6 +175,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
   const int MB = a.max_blocks_per_seq;
+  const int max_ctx = MB << shift;
   const int num_blocks = (int)a.num_blocks;               // the ABI keeps it below 2^31
   const float kNegInf = -__builtin_inff();
 
@@ -230,7 +231,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     bad_pipe <<= 1;
     if (ic.t < ic.stop) {
       const int tok0 = ic.t * TOK;
-      const int32_t blk = tables[(int64_t)ic.s * MB + (tok0 >> shift)];
+      // a tile past the table (possible only with a stale plan) counts as invalid
+      const int32_t blk = tok0 < max_ctx ? tables[(int64_t)ic.s * MB + (tok0 >> shift)] : -1;
       if (blk >= 0 && blk < num_blocks)
         base = (((int64_t)blk << shift) + (tok0 & bs_mask)) * row_stride;
       else
