@@ -78,6 +78,11 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle runs on (0: the whole batch)")
+    ap.add_argument("--component", default="decode", choices=["decode", "copy_blocks"],
+                    help="decode: the decode step (default); copy_blocks: the copy-on-write "
+                         "block copy kernel alone")
+    ap.add_argument("--copy-pairs", type=int, default=4096,
+                    help="block pairs per copy_blocks launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for HBM traffic counters)")
@@ -117,6 +122,8 @@ def main(argv=None) -> int:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
                                    "has no multi-GPU mode (use --gpus 1)"}))
         return 2
+    if args.component == "copy_blocks":
+        return bench_copy_blocks(args)
 
     import torch
     import paged_kv_cache_441_amd as pkv
@@ -242,6 +249,55 @@ def main(argv=None) -> int:
         result["cpu_baseline"], result["parity"] = cpu_baseline(b, out, args.cpu_sample_seqs)
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_copy_blocks(args) -> int:
+    """The copy-on-write block copy on the workload's pool: --copy-pairs disjoint
+    (src, dst) pairs of random blocks per launch; bytes = pairs x block bytes x 2
+    caches, read and written."""
+    import torch
+    import paged_kv_cache_441_amd as pkv
+    from workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    pkv.load_library()
+    spec = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if spec.kv_dtype == "bf16" else torch.float32
+    shape = (spec.num_blocks, spec.block_size, spec.num_kv_heads, spec.head_dim)
+    kc = torch.zeros(shape, dtype=dt, device=dev)
+    vc = torch.zeros(shape, dtype=dt, device=dev)
+    n = min(args.copy_pairs, spec.num_blocks // 2)
+    perm = np.random.default_rng(spec.seed).permutation(spec.num_blocks)
+    pairs = torch.as_tensor(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int32), device=dev)
+    for _ in range(args.warmup):
+        pkv.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k].record()
+        pkv.copy_blocks(kc, vc, pairs)
+    ev[-1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
+    block_bytes = kc[0].numel() * kc.element_size()
+    moved = n * block_bytes * 2 * 2
+    gbs = moved / (float(t.mean()) / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "copy_blocks HBM GB/s (bytes read + written)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "dtype": spec.kv_dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "pairs": n, "block_bytes": block_bytes},
+        "kernel_ms": round(float(t.mean()), 5),
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+    }), flush=True)
     return 0
 
 

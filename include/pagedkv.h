@@ -56,14 +56,15 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, inconsistent shapes */
   PKV_ERR_UNSUPPORTED = 2,  /* a valid combination this build has no kernel for */
   PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
-  PKV_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+  PKV_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
+  PKV_ERR_NO_BLOCKS = 5     /* the block pool has no free block left */
 } pkv_status;
 
 typedef enum {
@@ -127,6 +128,76 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
                               void* stream);
+
+/*
+ * ---- The block pool (host) and block copies (device) -----------------------------
+ *
+ * The pool owns the ids 0 .. num_blocks-1 of the physical KV blocks: a first-in
+ * first-out list of free ids and a reference count per block.  (Page
+ * "vllm源码分析：我是如何一步步读懂PagedAttention核心实现的？", 第一讲, the
+ * BlockAllocator: allocation takes the first free id and sets its count to 1, an
+ * empty list is an error, a block goes back to the end of the list when its count
+ * drops to 0; page "读一个真实 serving 系统 · vLLM 架构巡礼": sequences that share a
+ * prefix point at the same blocks, the shared count is above one, and a shared block
+ * is copied before it is changed.)  The pool lives in host memory, owned by the
+ * library between create and destroy; it is not thread-safe (callers serialise the
+ * calls on one pool).  Block tables passed to it are host int32 arrays owned by the
+ * caller.
+ *
+ * pkv_block_pool_allocate   takes one free block (count 1); PKV_ERR_NO_BLOCKS if none.
+ * pkv_block_pool_release    drops one reference to each listed block (a block may be
+ *                           listed several times); blocks reaching 0 go back to the
+ *                           free list in list order.  INVALID_ARG, with nothing
+ *                           changed, if an id is out of range or would drop below 0.
+ * pkv_block_pool_fork       adds one reference to each listed block: a forked
+ *                           sequence's table is a copy of its parent's (the caller
+ *                           copies it).  INVALID_ARG, nothing changed, for an id out
+ *                           of range or not in use.
+ * pkv_block_pool_num_free   free blocks (-1 for a null pool).
+ * pkv_block_pool_ref_count  a block's count (-1 for a bad id or a null pool).
+ *
+ * pkv_block_pool_append_slots -- the slot of each sequence's next token, in sequence
+ * order.  Sequence i has num_tokens[i] tokens and the table
+ * tables[i*table_capacity .. +table_lens[i]) (ceil(num_tokens[i] / block_size) ids).
+ * Its next token, at position n = num_tokens[i]:
+ *   - n % block_size == 0: a new block is allocated and appended to the table;
+ *   - otherwise it goes into the last block; if that block is shared (count > 1) a
+ *     fresh block is allocated, the pair (old, fresh) is appended to `copies`
+ *     (int32 [num_seqs][2], host), one reference to the old block is dropped and the
+ *     fresh block replaces it in the table.
+ * slots[i] = table[n / block_size] * block_size + n % block_size.  (Page "vLLM
+ * PagedAttention 原理与源码深度解析", sections 3.3 and 5.2: a full last block means a new
+ * block; the page's sketch writes into the old block after allocating a new one,
+ * while here the token goes to the block that holds its position.)  The copies must
+ * be done (pkv_copy_blocks) before the new tokens are written.  *done receives the
+ * number of sequences handled; on PKV_ERR_NO_BLOCKS or INVALID_ARG the sequences
+ * before *done have been updated and the rest have not.
+ *
+ * pkv_copy_blocks -- for each (src, dst) in pairs (device int32 [num_pairs][2]), block
+ * dst of key_cache and value_cache becomes a bitwise copy of block src.  Pairs run
+ * in parallel: no dst may repeat or also be a src (copy-on-write pairs from one
+ * pkv_block_pool_append_slots call satisfy this).  Pairs with an id outside
+ * [0, num_blocks) are skipped.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+pkv_status pkv_block_pool_create(int32_t num_blocks, pkv_block_pool** pool);
+void pkv_block_pool_destroy(pkv_block_pool* pool);
+int32_t pkv_block_pool_num_free(const pkv_block_pool* pool);
+int32_t pkv_block_pool_ref_count(const pkv_block_pool* pool, int32_t block);
+pkv_status pkv_block_pool_allocate(pkv_block_pool* pool, int32_t* block);
+pkv_status pkv_block_pool_release(pkv_block_pool* pool, const int32_t* blocks, int32_t n);
+pkv_status pkv_block_pool_fork(pkv_block_pool* pool, const int32_t* blocks, int32_t n);
+pkv_status pkv_block_pool_append_slots(pkv_block_pool* pool, int32_t* tables,
+                                       int32_t* table_lens, int32_t table_capacity,
+                                       const int32_t* num_tokens, int32_t num_seqs,
+                                       int32_t block_size, int32_t* slots, int32_t* copies,
+                                       int32_t* num_copies, int32_t* done);
+
+pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                           void* stream);
 
 /*
  * pkv_decode_prologue -- the steps of a decode step that come before attention,

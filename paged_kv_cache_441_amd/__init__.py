@@ -7,7 +7,9 @@ include/pagedkv.h; this package only marshals torch tensors into that ABI.
 
 from ._lib import LIB_PATH, PkvError, load_library, status_string  # noqa: F401
 from .ops import (  # noqa: F401
+    BlockPool,
     alloc_workspace,
+    copy_blocks,
     decode_prologue,
     decode_step,
     kv_cache_write,

@@ -18,6 +18,7 @@ PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE = 3
 PKV_ERR_HIP = 4
+PKV_ERR_NO_BLOCKS = 5
 
 PKV_F32 = 0
 PKV_BF16 = 1
@@ -32,6 +33,16 @@ SIGNATURES = {
     "pkv_kv_cache_write": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_decode_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i64, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_block_pool_create": (_i32, [_i32, _vp]),
+    "pkv_block_pool_destroy": (None, [_vp]),
+    "pkv_block_pool_num_free": (_i32, [_vp]),
+    "pkv_block_pool_ref_count": (_i32, [_vp, _i32]),
+    "pkv_block_pool_allocate": (_i32, [_vp, _vp]),
+    "pkv_block_pool_release": (_i32, [_vp, _vp, _i32]),
+    "pkv_block_pool_fork": (_i32, [_vp, _vp, _i32]),
+    "pkv_block_pool_append_slots": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
+                                           _vp]),
+    "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -43,7 +54,7 @@ SIGNATURES = {
                                           _sz, _vp]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lock = threading.Lock()
 _lib = None

@@ -133,4 +133,52 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
   return hipGetLastError();
 }
 
+// ---- block copies (copy-on-write) -------------------------------------------------
+// For every (src, dst) pair, block dst of both caches becomes a copy of block src.
+// Workgroup (p, c) copies chunk c (kCopyChunk bytes) of pair p's blocks: every lane
+// loads all of its 16-byte pieces of both caches before it stores any.  Pairs with
+// an id outside the pool are skipped.  Pairs run in parallel: the caller's contract
+// is that no dst repeats and no dst is also a src.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyPer = 4;                            // pieces per lane per cache
+constexpr int kCopyChunk = kCopyThreads * kCopyPer * 16;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ pairs, int64_t block_chunks, int64_t num_blocks) {
+  const int p = blockIdx.x;
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t c0 = (int64_t)blockIdx.y * (kCopyChunk / 16) + threadIdx.x;
+  const int64_t s = (int64_t)src * block_chunks, d = (int64_t)dst * block_chunks;
+  uint4 k[kCopyPer], v[kCopyPer];
+#pragma unroll
+  for (int i = 0; i < kCopyPer; ++i) {
+    const int64_t c = c0 + i * kCopyThreads;
+    if (c < block_chunks) {
+      k[i] = key_cache[s + c];
+      v[i] = value_cache[s + c];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyPer; ++i) {
+    const int64_t c = c0 + i * kCopyThreads;
+    if (c < block_chunks) {
+      key_cache[d + c] = k[i];
+      value_cache[d + c] = v[i];
+    }
+  }
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t stream) {
+  const dim3 grid((unsigned)num_pairs, (unsigned)((block_bytes + kCopyChunk - 1) / kCopyChunk));
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream,
+                     static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), pairs,
+                     block_bytes / 16, num_blocks);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

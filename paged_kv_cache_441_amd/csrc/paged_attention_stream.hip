@@ -517,8 +517,8 @@ hipError_t launch_tile_plan(const AttentionArgs& a, hipStream_t stream) {
 }
 
 // ---- merge of the segments ------------------------------------------------------------
-// One wave per (sequence, query head) row.  Sequences without tiles (invalid
-// context length) get NaN rows; a sequence inside one share was written by the
+// One wave per (sequence, query head) row.  Sequences without tiles (an invalid
+// context length: the plan gives them no positions) get NaN rows; a sequence inside one share was written by the
 // partition stage; otherwise its records, labels w + sequence for the non-empty
 // shares w it spans, are merged in share order.  Lane groups take every KGW-th record, U at a
 // time; the groups are combined in a fixed order, so the result does not depend on
@@ -536,20 +536,22 @@ __global__ __launch_bounds__(256) void paged_attention_stream_reduce_kernel(Atte
   const int qh = (int)(row % H);
   const int kg = lane / LPR;
   const int lr = lane % LPR;
-  const int ctx = a.context_lens[seq];
-  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
-  if (ctx < 1 || ctx > max_ctx) {
+  // One round of independent loads: the plan says which sequences have tiles (a
+  // valid context length) and where they sit.
+  const int c0 = a.tile_cum[seq];
+  const int c1 = a.tile_cum[seq + 1];
+  const int total = a.tile_hdr[0];
+  const int nwg = a.tile_hdr[1];
+  if (c1 == c0) {
     if (kg == 0) {
       const float nan = __builtin_nanf("");
       store_row4(a, row * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
     }
     return;
   }
-  const int total = a.tile_hdr[0];
-  const int nwg = a.tile_hdr[1];
   // shares holding the sequence's first and last real tiles
-  const int w0 = share_of((int64_t)a.tile_cum[seq] + kSeqCost, nwg, total);
-  const int w1 = share_of((int64_t)a.tile_cum[seq + 1] - 1, nwg, total);
+  const int w0 = share_of((int64_t)c0 + kSeqCost, nwg, total);
+  const int w1 = share_of((int64_t)c1 - 1, nwg, total);
   if (w0 == w1) return;
   Running r{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   for (int w = w0 + kg; w <= w1; w += KGW * U) {

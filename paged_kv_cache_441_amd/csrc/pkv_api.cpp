@@ -169,6 +169,7 @@ const char* pkv_status_string(int32_t status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported combination (head_dim, block_size, GQA group or dtype)";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error at launch";
+    case PKV_ERR_NO_BLOCKS: return "no free block left in the pool";
     default: return "unknown status";
   }
 }
@@ -208,6 +209,25 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
   return hip_status(pkv::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
                                             num_tokens, static_cast<int>(row), slots,
                                             static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                           void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  int64_t row = 0, block = 0, cache_bytes = 0;
+  if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row) ||
+      !mul_ok(row, block_size, INT32_MAX / 2, &block) ||
+      !mul_ok(block, num_blocks, INT64_MAX / 2, &cache_bytes))
+    return PKV_ERR_INVALID_ARG;
+  if (block % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !pairs) return PKV_ERR_INVALID_ARG;
+  return hip_status(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block,
+                                            num_blocks, static_cast<hipStream_t>(stream)));
 }
 
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -25,6 +25,10 @@ hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* co
                                   int* plan_count, bool balanced, int* tile_cum, int* tile_hdr,
                                   hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t stream);
+
 struct AttentionArgs {
   void* out;
   const void* query;

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -248,3 +249,100 @@ def decode_step(query, key, value, key_cache, value_cache, block_tables, context
     return paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
                                   partition_size, out=out, out_dtype=out_dtype,
                                   workspace=workspace)
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                pairs: torch.Tensor) -> None:
+    """Copy-on-write copies: block dst of both caches becomes block src, for every
+    (src, dst) row of ``pairs`` (int32 [n, 2] on the caches' device)."""
+    dt = _kv(key_cache, "key_cache")
+    if _kv(value_cache, "value_cache") != dt:
+        raise TypeError("value_cache dtype differs from key_cache")
+    _i32(pairs, "pairs")
+    _same_device(key_cache, value_cache, pairs)
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("caches must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    NB, BS, Hkv, D = key_cache.shape
+    lib = _lib.load_library()
+    st = lib.pkv_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), pairs.shape[0], Hkv,
+                             D, BS, NB, dt, _stream(key_cache))
+    _lib.check(st, "pkv_copy_blocks")
+
+
+class BlockPool:
+    """The library's host block pool (free list and reference counts of the physical
+    blocks).  Block tables are numpy int32 arrays [num_seqs, capacity] with their
+    lengths in a separate int32 array; both are updated in place."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = _lib.load_library()
+        h = ctypes.c_void_p()
+        _lib.check(self._lib.pkv_block_pool_create(int(num_blocks), ctypes.byref(h)),
+                   "pkv_block_pool_create")
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pkv_block_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return self._lib.pkv_block_pool_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._lib.pkv_block_pool_ref_count(self._h, int(block))
+
+    def allocate(self) -> int:
+        b = ctypes.c_int32()
+        _lib.check(self._lib.pkv_block_pool_allocate(self._h, ctypes.byref(b)),
+                   "pkv_block_pool_allocate")
+        return b.value
+
+    @staticmethod
+    def _ids(blocks):
+        a = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32).reshape(-1))
+        return a, a.ctypes.data_as(ctypes.c_void_p)
+
+    def release(self, blocks) -> None:
+        a, p = self._ids(blocks)
+        _lib.check(self._lib.pkv_block_pool_release(self._h, p, a.shape[0]),
+                   "pkv_block_pool_release")
+
+    def fork(self, blocks) -> None:
+        a, p = self._ids(blocks)
+        _lib.check(self._lib.pkv_block_pool_fork(self._h, p, a.shape[0]), "pkv_block_pool_fork")
+
+    def append_slots(self, tables: np.ndarray, table_lens: np.ndarray, num_tokens,
+                     block_size: int):
+        """Slots of every sequence's next token; returns (slots int32 [B], copies
+        int32 [n, 2]).  Raises PkvError (status PKV_ERR_NO_BLOCKS when the pool runs
+        dry); the sequences handled before the failure stay updated."""
+        for a, n in ((tables, "tables"), (table_lens, "table_lens")):
+            if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+                raise TypeError(f"{n} must be a C-contiguous numpy int32 array")
+        B = table_lens.shape[0]
+        if tables.ndim != 2 or tables.shape[0] != B:
+            raise ValueError("tables must be [num_seqs, capacity]")
+        ntok = np.ascontiguousarray(np.asarray(num_tokens, dtype=np.int32))
+        if ntok.shape != (B,):
+            raise ValueError("num_tokens must have one entry per sequence")
+        slots = np.empty(B, np.int32)
+        copies = np.empty((max(B, 1), 2), np.int32)
+        ncp, done = ctypes.c_int32(), ctypes.c_int32()
+        vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        st = self._lib.pkv_block_pool_append_slots(self._h, vp(tables), vp(table_lens),
+                                                   tables.shape[1], vp(ntok), B, int(block_size),
+                                                   vp(slots), vp(copies), ctypes.byref(ncp),
+                                                   ctypes.byref(done))
+        _lib.check(st, f"pkv_block_pool_append_slots (done {done.value} of {B})")
+        return slots, copies[:ncp.value].copy()
