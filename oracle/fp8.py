@@ -12,7 +12,8 @@ nor the scaling.  Readings adopted:
       mantissa bits; no infinities; S.1111.111 is NaN; the largest finite magnitude is
       1.75 * 2^8 = 448; exponent field 0 holds the subnormals m * 2^-9).
   F2  Scaling: one fp32 scale per cache (k_scale, v_scale).  A value x is stored as
-      E4M3(x / scale); the cache's real value is decode(code) * scale.
+      E4M3(x / scale), the quotient taken in fp32 (correctly rounded), the precision
+      the kernel divides in; the cache's real value is decode(code) * scale.
   F3  Encoding: round to nearest, ties to the even code; magnitudes past 448 saturate
       to +-448; NaN stays NaN (code 0x7F); the sign of zero is kept.
   F4  Attention reads decode(code) * scale exactly (in fp64 here) and is otherwise the
@@ -97,15 +98,18 @@ def e4m3_encode_array(x: np.ndarray) -> np.ndarray:
 
 
 def quantize(values: np.ndarray, scale: float) -> np.ndarray:
-    """F2/F3: codes of values / scale (values in fp64 or wider-than-fp8 floats)."""
-    return e4m3_encode_array(np.asarray(values, dtype=np.float64) / float(scale))
+    """F2/F3: codes of values / scale; values and scale are fp32-representable (the
+    cache write's inputs are bf16 or fp32), the quotient is rounded to fp32."""
+    q = np.asarray(values, dtype=np.float32) / np.float32(scale)
+    return e4m3_encode_array(q.astype(np.float64))
 
 
 def cache_write_fp8(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
                     value: np.ndarray, slots: np.ndarray, block_size: int,
                     k_scale: float, v_scale: float):
     """O2 with F2/F3: copies of the uint8 caches with each token's quantised K/V rows at
-    its slot (negative slots skipped).  ``key``/``value`` are real values (fp64)."""
+    its slot (negative slots skipped).  ``key``/``value`` hold fp32-representable
+    values (the widened bf16 or fp32 inputs)."""
     kc = key_cache.copy()
     vc = value_cache.copy()
     kq = quantize(key, k_scale)

@@ -65,12 +65,13 @@ def test_quantised_write_is_bitwise():
     rng = np.random.default_rng(1)
     kc = rng.integers(0, 256, (6, 4, 2, 8), dtype=np.uint8)
     vc = rng.integers(0, 256, (6, 4, 2, 8), dtype=np.uint8)
-    k = rng.normal(0, 3, (3, 2, 8))
-    v = rng.normal(0, 3, (3, 2, 8))
+    k = rng.normal(0, 3, (3, 2, 8)).astype(np.float32)
+    v = rng.normal(0, 3, (3, 2, 8)).astype(np.float32)
     slots = np.array([5, -1, 22])
     k2, v2 = of8.cache_write_fp8(kc, vc, k, v, slots, 4, 0.5, 2.0)
-    assert (k2[1, 1] == of8.e4m3_encode_array(k[0] / 0.5)).all()
-    assert (v2[5, 2] == of8.e4m3_encode_array(v[2] / 2.0)).all()
+    # the quotient is taken in fp32; scales 0.5 and 2 make it exact here
+    assert (k2[1, 1] == of8.e4m3_encode_array(k[0].astype(np.float32) / 0.5)).all()
+    assert (v2[5, 2] == of8.e4m3_encode_array(v[2].astype(np.float32) / 2.0)).all()
     changed = (k2 != kc).any(axis=(2, 3))
     assert set(zip(*np.nonzero(changed))) <= {(1, 1), (5, 2)}
 
@@ -113,3 +114,15 @@ def test_planted_rounding_mistake_fails_the_pins(monkeypatch):
     monkeypatch.setattr(of8, "e4m3_encode", half_up)
     with pytest.raises(AssertionError):
         test_midpoints_go_to_the_even_code()
+
+
+def test_quotient_is_rounded_to_fp32_before_encoding():
+    # x / s rounds (in fp32) onto the midpoint 1.0625 of codes 0x38 and 0x39, which then
+    # goes to the even code; the exact quotient lies above the midpoint (-> 0x39 in fp64)
+    from fractions import Fraction
+    s = np.float32(0.3)
+    x = np.float32(0.31875002)
+    assert Fraction(float(x)) / Fraction(float(s)) > Fraction(1.0625)
+    assert x / s == np.float32(1.0625)
+    assert of8.e4m3_encode(float(x) / float(s)) == 0x39
+    assert of8.quantize(np.array([x]), s)[0] == 0x38
