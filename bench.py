@@ -11,6 +11,9 @@ sequences (tokens) per second.
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config llama3_8b]
                     [--partition-size 512] [--no-cpu-baseline]
 
+A config named *_fp8 runs the same workload over E4M3 (8-bit float) caches: the
+prologue quantises the new rows, attention decodes the codes (balanced split only).
+
 Prints one JSON line.  The fp64 CPU oracle is timed on the same batch (all of it
 unless --cpu-sample-seqs says otherwise), on one host thread, repeated for about
 10 s of CPU work, and its outputs are compared with the GPU's.
@@ -36,7 +39,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 # while these are unchanged.
 KERNEL_SOURCES = ("paged_attention.hip", "paged_attention_stream.hip", "pkv_device.hpp",
                   "pkv_launch.hpp", "pkv_plan.hpp", "pkv_tile.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_attention_partition_llama3_8b.json")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
 
 
 def kernel_source_hash() -> str:
@@ -48,11 +55,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str, partition_size: int):
+def stored_traffic(kernel: str, workload: str, partition_size: int):
     """HBM bytes per partition-kernel launch from the committed rocprofv3 counter runs,
     or None when they were taken on other kernel sources or another workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -127,8 +134,12 @@ def main(argv=None) -> int:
 
     import torch
     import paged_kv_cache_441_amd as pkv
-    from workloads import make_config
+    from workloads import FP8_CONFIGS, make_config, make_fp8_config
 
+    fp8 = args.config in FP8_CONFIGS
+    if fp8 and args.partition_size not in (None, 0):
+        print(json.dumps({"error": "E4M3 caches run the balanced split only (partition size 0)"}))
+        return 2
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 2
@@ -137,9 +148,10 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
 
     t_gen = time.perf_counter()
-    b = make_config(args.config, device=dev)
+    b = make_fp8_config(args.config, device=dev) if fp8 else make_config(args.config, device=dev)
     spec = b.spec
     P = spec.partition_size if args.partition_size is None else args.partition_size
+    ks, vs = b.extra.get("k_scale"), b.extra.get("v_scale")
     B, H, Hkv, D, BS, NB = (b.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim,
                             spec.block_size, spec.num_blocks)
     MB = b.max_blocks_per_seq
@@ -155,10 +167,18 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pkv.decode_prologue(bt, cl, b.key, b.value, kc, vc, ws, P, slot_mapping=slots)
+        if fp8:
+            pkv.decode_prologue_fp8(bt, cl, b.key, b.value, kc, vc, ws, ks, vs, slot_mapping=slots)
+        else:
+            pkv.decode_prologue(bt, cl, b.key, b.value, kc, vc, ws, P, slot_mapping=slots)
         if ev is not None:
             ev[1].record()
-        pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, out=out, workspace=ws)
+        if fp8:
+            pkv.paged_attention_partition_fp8(b.query, kc, vc, bt, cl, b.scale, ks, vs, out=out,
+                                              workspace=ws)
+        else:
+            pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, out=out,
+                                          workspace=ws)
         if ev is not None:
             ev[2].record()
         pkv.paged_attention_reduce(out, cl, ws, BS, MB, P)
@@ -185,6 +205,7 @@ def main(argv=None) -> int:
     t_gpu = np.array([e[0].elapsed_time(e[3]) for e in events])
 
     kv_bytes = b.kv_bytes()
+    kernel = "paged_attention_stream" if P == 0 else "paged_attention_partition"
     tokens = int(b.context_lens.astype(np.int64).sum())
     step_s = ms_step / 1e3
     kv_gbs_step = kv_bytes / step_s / 1e9
@@ -203,7 +224,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if spec.kv_dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8_e4m3"}[spec.kv_dtype],
         "data": "synthetic",
         "config": {
             "workload": spec.name,
@@ -211,6 +232,7 @@ def main(argv=None) -> int:
             "block_size": BS, "num_blocks": NB, "max_blocks_per_seq": MB,
             "partition_size": P, "kv_dtype": spec.kv_dtype, "accumulate": "f32",
             "out_dtype": "f32", "context": str(spec.ctx),
+            **({"query_dtype": "bf16", "k_scale": ks, "v_scale": vs} if fp8 else {}),
             "context_sum": tokens, "context_mean": round(tokens / B, 1),
             "context_max": int(b.context_lens.max()), "seed": spec.seed,
         },
@@ -229,13 +251,12 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_stream_kernel" if P == 0 else
-                      "paged_attention_partition_kernel",
+            "kernel": f"{kernel}_kernel",
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(spec.name, P),
+            "traffic": stored_traffic(kernel, spec.name, P),
             "traffic_unit": "bytes per launch (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, "
                             "factors from a plain 1 GiB copy)",
         },
@@ -323,15 +344,29 @@ def cpu_baseline(b, gpu_out, n_sample, min_seconds=10.0, max_reps=20):
     k = b.numpy_storage(b.key)[:n]
     v = b.numpy_storage(b.value)[:n]
     ctx = b.context_lens[:n]
+    fp8 = b.kv_dtype == "fp8"
+
+    def run():
+        if not fp8:
+            return oracle.decode_step(q, k, v, kc, vc, tables, ctx, b.scale, b.kv_dtype)[3]
+        from oracle import fp8 as of8
+        ks, vs = b.extra["k_scale"], b.extra["v_scale"]
+        slots = oracle.slot_mapping(tables, ctx, b.spec.block_size)
+        kc2, vc2 = of8.cache_write_fp8(kc, vc, oracle.bf16_bits_to_f64(k),
+                                       oracle.bf16_bits_to_f64(v), slots, b.spec.block_size,
+                                       ks, vs)
+        return of8.paged_attention_decode_fp8(oracle.bf16_bits_to_f64(q), kc2, vc2, tables, ctx,
+                                              b.scale, ks, vs)
+
     times = []
     with threadpool_limits(limits=1):
         while len(times) < max_reps and sum(times) < min_seconds:
             t0 = time.perf_counter()
-            _, _, _, ref = oracle.decode_step(q, k, v, kc, vc, tables, ctx, b.scale, b.kv_dtype)
+            ref = run()
             times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     sample_kv = int(ctx.astype(np.int64).sum()) * b.spec.num_kv_heads * b.spec.head_dim * 2 * \
-        (2 if b.kv_dtype == "bf16" else 4)
+        {"bf16": 2, "f32": 4, "fp8": 1}[b.kv_dtype]
     g = gpu_out[:n].float().cpu().numpy().astype(np.float64)
     err = float(np.abs(g - ref).max())
     what = "the whole batch" if n == B else f"the first {n} of {B} sequences"

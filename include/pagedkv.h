@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_OK = 0,
@@ -68,8 +68,9 @@ typedef enum {
 } pkv_status;
 
 typedef enum {
-  PKV_F32 = 0,   /* IEEE binary32 */
-  PKV_BF16 = 1   /* bfloat16 (top 16 bits of a binary32) */
+  PKV_F32 = 0,      /* IEEE binary32 */
+  PKV_BF16 = 1,     /* bfloat16 (top 16 bits of a binary32) */
+  PKV_FP8_E4M3 = 2  /* OCP 8-bit float E4M3 (cache storage only; see the FP8 section) */
 } pkv_dtype;
 
 /* PKV_ABI_VERSION of the loaded library. */
@@ -121,7 +122,8 @@ pkv_status pkv_slot_mapping(const int32_t* block_tables, const int32_t* context_
  *   slot_mapping            device int32 [num_tokens]
  *
  * Any head_dim with num_kv_heads*head_dim*sizeof(kv_dtype) a multiple of 16 bytes
- * is accepted.  num_tokens == 0 is a no-op.
+ * is accepted; kv_dtype may be PKV_FP8_E4M3 (codes copied as they are).
+ * num_tokens == 0 is a no-op.
  */
 pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cache,
                               void* value_cache, const int32_t* slot_mapping,
@@ -198,6 +200,75 @@ pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pa
                            int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
                            void* stream);
+
+/*
+ * ---- FP8 (E4M3) caches -------------------------------------------------------------
+ *
+ * A KV cache of 8-bit floats (page "vLLM PagedAttention 原理与源码深度解析", section
+ * 8.4, names an fp8 KV cache as a serving option; the pages fix neither the format
+ * nor the scaling, so these are this library's choices):
+ *  - format: OCP E4M3 -- sign, 4 exponent bits biased by 7, 3 mantissa bits; no
+ *    infinities; S.1111.111 is NaN; the largest finite magnitude is 448; exponent
+ *    field 0 holds the subnormals m * 2^-9;
+ *  - one fp32 scale per cache (k_scale, v_scale, positive and finite): the cache
+ *    element e stands for decode(e) * scale;
+ *  - writing x stores E4M3(x / scale): the quotient rounded to fp32, then to the
+ *    nearest E4M3 value with ties to the even code; magnitudes of 448 and beyond
+ *    saturate to +-448 and NaN is stored as 0x7F.
+ * The cache layout is the one above with one byte per element.
+ *
+ * pkv_kv_cache_write_fp8 -- pkv_kv_cache_write storing the codes of fp32 or bf16
+ * (in_dtype) rows; num_kv_heads*head_dim must be a multiple of 16.
+ *
+ * pkv_decode_prologue_fp8 -- pkv_decode_prologue storing codes as above; it builds
+ * the balanced-split plan (partition_size 0).
+ *
+ * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 caches:
+ * scores scale * k_scale * <q, decode(k_t)>, output sum_t p_t v_scale decode(v_t) /
+ * sum_t p_t.  Decoding is exact (every E4M3 value is a bfloat16); queries are bf16;
+ * accumulation is fp32.  Always the balanced split: the workspace is
+ * pkv_paged_attention_workspace_bytes(..., partition_size = 0), and the staged form
+ * is pkv_paged_attention_plan and pkv_paged_attention_reduce with partition_size 0
+ * around pkv_paged_attention_partition_fp8.  Supported: head_dim 64 (with an even
+ * num_kv_heads) or 128, block_size 16 or 32, num_heads / num_kv_heads in {1, 2, 4,
+ * 8}, out_dtype PKV_F32 or PKV_BF16.  The device-side contract (NaN rows for a bad
+ * context length or block id) is that of pkv_paged_attention_decode.  The unscaled
+ * attention entry points reject PKV_FP8_E4M3 with PKV_ERR_INVALID_ARG.
+ */
+pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, void* key_cache,
+                                  void* value_cache, const int32_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, pkv_dtype in_dtype,
+                                  float k_scale, float v_scale, void* stream);
+
+pkv_status pkv_decode_prologue_fp8(const int32_t* block_tables, const int32_t* context_lens,
+                                   const void* key, const void* value, void* key_cache,
+                                   void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   pkv_dtype in_dtype, float k_scale, float v_scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                                          float scale, float k_scale, float v_scale,
+                                          pkv_dtype out_dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
+                                             const void* key_cache, const void* value_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size,
+                                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                                             float scale, float k_scale, float v_scale,
+                                             pkv_dtype out_dtype, void* workspace,
+                                             size_t workspace_bytes, void* stream);
 
 /*
  * pkv_decode_prologue -- the steps of a decode step that come before attention,

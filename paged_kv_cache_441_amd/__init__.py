@@ -11,10 +11,14 @@ from .ops import (  # noqa: F401
     alloc_workspace,
     copy_blocks,
     decode_prologue,
+    decode_prologue_fp8,
     decode_step,
     kv_cache_write,
+    kv_cache_write_fp8,
     paged_attention_decode,
+    paged_attention_decode_fp8,
     paged_attention_partition,
+    paged_attention_partition_fp8,
     paged_attention_plan,
     paged_attention_reduce,
     slot_mapping,

@@ -22,6 +22,7 @@ PKV_ERR_NO_BLOCKS = 5
 
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 
 _i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -31,6 +32,16 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_slot_mapping": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp]),
     "pkv_kv_cache_write": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_kv_cache_write_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32,
+                                      _f32, _f32, _vp]),
+    "pkv_decode_prologue_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _i64, _i32, _f32, _f32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _i64, _f32, _f32, _f32, _i32, _vp, _sz,
+                                              _vp]),
+    "pkv_paged_attention_partition_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                 _i32, _i32, _i32, _i64, _f32, _f32, _f32, _i32,
+                                                 _vp, _sz, _vp]),
     "pkv_decode_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i64, _i32, _i32, _vp, _sz, _vp]),
     "pkv_block_pool_create": (_i32, [_i32, _vp]),
@@ -54,7 +65,7 @@ SIGNATURES = {
                                           _sz, _vp]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lock = threading.Lock()
 _lib = None

@@ -59,17 +59,75 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
 }
 
+// The E4M3 cache write: the codes of x / scale (the quotient rounded to fp32, then to
+// E4M3) for 16 consecutive elements of a row, read as fp32 or bfloat16; 16 bytes out.
+template <bool kBf16In>
+__device__ __forceinline__ uint4 quantize16(const void* src, int64_t group, float scale) {
+  float x[16];
+  if constexpr (kBf16In) {
+    const uint4* p = static_cast<const uint4*>(src) + 2 * group;
+    unpack_chunk<BF16>(p[0], x);
+    unpack_chunk<BF16>(p[1], x + 8);
+  } else {
+    const uint4* p = static_cast<const uint4*>(src) + 4 * group;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_chunk<F32>(p[i], x + 4 * i);
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(__fdiv_rn(x[4 * i + j], scale)) << (8 * j);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Token t's K and V rows into cache slot `slot`, each cache row `chunks` 16-byte
+// chunks: a bit copy (quant 0) or the E4M3 codes of fp32 (quant 1) or bfloat16
+// (quant 2) inputs.  The workgroup's threads share the 2 * chunks pieces.
+__device__ __forceinline__ void store_token(const void* key, const void* value, void* key_cache,
+                                            void* value_cache, int64_t t, int64_t slot,
+                                            int chunks, int quant, float k_scale, float v_scale) {
+  const int64_t src = t * chunks, dst = slot * chunks;
+  for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
+    const bool is_k = c < chunks;
+    const int64_t cc = is_k ? c : c - chunks;
+    const void* in = is_k ? key : value;
+    uint4* out = static_cast<uint4*>(is_k ? key_cache : value_cache) + dst + cc;
+    if (quant == 0)
+      *out = static_cast<const uint4*>(in)[src + cc];
+    else if (quant == 1)
+      *out = quantize16<false>(in, src + cc, is_k ? k_scale : v_scale);
+    else
+      *out = quantize16<true>(in, src + cc, is_k ? k_scale : v_scale);
+  }
+}
+
+// One workgroup per token: the E4M3 codes of the token's K and V rows.
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const void* __restrict__ key, const void* __restrict__ value, void* __restrict__ key_cache,
+    void* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int chunks_per_row,
+    int64_t num_slots, int quant, float k_scale, float v_scale) {
+  const int t = blockIdx.x;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  store_token(key, value, key_cache, value_cache, t, slot, chunks_per_row, quant, k_scale,
+              v_scale);
+}
+
 // The decode step's prologue in one launch: workgroup 0 builds the attention plan
 // while workgroup 1 + i computes sequence i's slot and stores its new K/V rows.
 constexpr int kPrologueThreads = 256;
 
 __global__ __launch_bounds__(kPrologueThreads) void decode_prologue_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ key_cache,
-    uint4* __restrict__ value_cache, int32_t* __restrict__ slot_mapping, int num_seqs,
+    const void* __restrict__ key, const void* __restrict__ value, void* __restrict__ key_cache,
+    void* __restrict__ value_cache, int32_t* __restrict__ slot_mapping, int num_seqs,
     int max_blocks_per_seq, int block_shift, int64_t num_blocks, int chunks_per_row,
     int partition_size, int4* __restrict__ plan_items, int* __restrict__ plan_count,
-    bool balanced, int* __restrict__ tile_cum, int* __restrict__ tile_hdr) {
+    bool balanced, int* __restrict__ tile_cum, int* __restrict__ tile_hdr, int quant,
+    float k_scale, float v_scale) {
   if (blockIdx.x == 0) {
     if (balanced)
       build_tile_plan<kPrologueThreads>(context_lens, num_seqs, max_blocks_per_seq << block_shift,
@@ -84,14 +142,8 @@ __global__ __launch_bounds__(kPrologueThreads) void decode_prologue_kernel(
                                num_blocks);
   if (threadIdx.x == 0) slot_mapping[t] = slot;
   if (slot < 0) return;
-  const int64_t src = (int64_t)t * chunks_per_row;
-  const int64_t dst = (int64_t)slot * chunks_per_row;
-  for (int c = threadIdx.x; c < 2 * chunks_per_row; c += blockDim.x) {
-    if (c < chunks_per_row)
-      key_cache[dst + c] = key[src + c];
-    else
-      value_cache[dst + c - chunks_per_row] = value[src + c - chunks_per_row];
-  }
+  store_token(key, value, key_cache, value_cache, t, slot, chunks_per_row, quant, k_scale,
+              v_scale);
 }
 
 hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
@@ -100,13 +152,12 @@ hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* co
                                   int max_blocks_per_seq, int block_shift, int64_t num_blocks,
                                   int row_bytes, int partition_size, int4* plan_items,
                                   int* plan_count, bool balanced, int* tile_cum, int* tile_hdr,
-                                  hipStream_t stream) {
+                                  int quant, float k_scale, float v_scale, hipStream_t stream) {
   hipLaunchKernelGGL(decode_prologue_kernel, dim3(num_seqs + 1), dim3(kPrologueThreads), 0, stream,
-                     block_tables, context_lens, static_cast<const uint4*>(key),
-                     static_cast<const uint4*>(value), static_cast<uint4*>(key_cache),
-                     static_cast<uint4*>(value_cache), slot_mapping, num_seqs, max_blocks_per_seq,
-                     block_shift, num_blocks, row_bytes / 16, partition_size, plan_items,
-                     plan_count, balanced, tile_cum, tile_hdr);
+                     block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping,
+                     num_seqs, max_blocks_per_seq, block_shift, num_blocks, row_bytes / 16,
+                     partition_size, plan_items, plan_count, balanced, tile_cum, tile_hdr, quant,
+                     k_scale, v_scale);
   return hipGetLastError();
 }
 
@@ -130,6 +181,18 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
                      static_cast<const uint4*>(key), static_cast<const uint4*>(value),
                      static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache),
                      slot_mapping, chunks, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write_fp8(const void* key, const void* value, void* key_cache,
+                                  void* value_cache, const int32_t* slot_mapping, int num_tokens,
+                                  int row_elems, int64_t num_slots, bool in_bf16, float k_scale,
+                                  float v_scale, hipStream_t stream) {
+  const int chunks = row_elems / 16;
+  const int threads = chunks * 2 >= 256 ? 256 : ((chunks * 2 + 63) / 64) * 64;
+  hipLaunchKernelGGL(cache_write_fp8_kernel, dim3(num_tokens), dim3(threads), 0, stream, key,
+                     value, key_cache, value_cache, slot_mapping, chunks, num_slots,
+                     in_bf16 ? 2 : 1, k_scale, v_scale);
   return hipGetLastError();
 }
 

@@ -49,11 +49,10 @@
 #include "pkv_tile.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace pkv {
 
-#define PKV_AS_GLOBAL(p) ((const void __attribute__((address_space(1)))*)(p))
-#define PKV_AS_LOCAL(p) ((void __attribute__((address_space(3)))*)(p))
 
 // Reads through the constant address space become scalar loads when the address is
 // wave-uniform; used for data no kernel of this launch writes (tables, lengths, the
@@ -69,11 +68,42 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// One direct-to-LDS copy: lane i's 16 bytes at base + off (base wave-uniform) land at
+// LDS byte lds + 16 i.  Written as assembly so that the compiler, which cannot tell
+// the ring's buffers apart once more than a few copies are in flight, adds no wait
+// for it before LDS reads; the kernel waits for the copies itself (s_waitcnt vmcnt)
+// before the barrier that hands a tile to the readers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// Waits until at most N of this wave's copies are outstanding; copies retire in
+// order, so every copy issued before the last N has landed in LDS.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <typename T, int D, int HW, int TOK>
 struct Stage {
   static constexpr int kRowBytes = HW * D * T::kElemBytes;   // one token row of the HW heads
   static constexpr int kSlots = kRowBytes / 16;               // 16-byte slots per row
   static constexpr int kSwz = kSlots >= 16 ? 15 : kSlots - 1;
+  // The XOR pattern of row r.  E4M3 rows are read as 8-byte value pieces, 16 lanes
+  // per row and two rows (r, r ^ 1) per 32-lane half of a read: their patterns differ
+  // in the top bit, so the two rows' 128 bytes land in different bank halves.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (T::kElemBytes == 1)
+      return ((r & 1) ? (kSwz + 1) >> 1 : 0) | ((r & kSwz) >> 1);
+    else
+      return r & kSwz;
+  }
   static constexpr int kTileBytes = TOK * kRowBytes;          // per cache
   static constexpr int kTileSlots = kTileBytes / 16;
   static constexpr int kCopies = kTileBytes / (HW * 1024);    // 1 KiB wave copies per cache
@@ -95,19 +125,43 @@ __device__ __forceinline__ bool share_nonempty(int w, int nwg, int total) {
 #ifndef PKV_STREAM_NBUF
 #define PKV_STREAM_NBUF 2
 #endif
+// E4M3 caches: a tile is half the bytes, and the per-tile compute no longer hides
+// under its copies with one workgroup per compute unit; two workgroups of 8 waves
+// share one when the registers allow it (WPE: waves per SIMD the register budget
+// must allow; measured on MI355X, Llama-3-8B-shaped batch: 192 us with one
+// workgroup per CU, 178 us with two; a third or fourth ring buffer did not help).
+#ifndef PKV_STREAM_NBUF_FP8
+#define PKV_STREAM_NBUF_FP8 2
+#endif
+#ifndef PKV_STREAM_WPE_FP8
+#define PKV_STREAM_WPE_FP8 4
+#endif
+
+template <typename T>
+constexpr int stream_nbuf() { return T::kElemBytes == 1 ? PKV_STREAM_NBUF_FP8 : PKV_STREAM_NBUF; }
+// GQA groups of 8 need more registers than a 4-wave-per-SIMD budget holds
+template <typename T, int G>
+constexpr int stream_wpe() { return T::kElemBytes == 1 && G <= 4 ? PKV_STREAM_WPE_FP8 : 1; }
 
 template <typename T, int D, int G, int HW, int NBUF>
-__global__ __launch_bounds__(HW * kWave)
+__global__ __launch_bounds__(HW * kWave) __attribute__((amdgpu_waves_per_eu(stream_wpe<T, G>())))
 void paged_attention_stream_kernel(AttentionArgs a) {
   constexpr int TOK = kTileTokens;
-  using Geo = Geometry<T, D, G>;
   using St = Stage<T, D, HW, TOK>;
-  constexpr int EPL = Geo::kEPL;
-  constexpr int NCH = Geo::kChunksPerRow;   // 16-byte chunks of one head's row
-  constexpr int QKC = Geo::kQkChunks;
-  constexpr int RPS = Geo::kRowsPerStep;
-  constexpr int STEPS = TOK / RPS;
+  constexpr bool kF8 = T::kElemBytes == 1;  // E4M3 caches, bfloat16 queries
+  using QT = typename std::conditional<kF8, BF16, T>::type;   // query and MFMA operand type
   constexpr int EB = T::kElemBytes;
+  constexpr int QEB = QT::kElemBytes;
+  constexpr int NCH = D * EB / 16;          // 16-byte chunks of one head's cache row
+  constexpr int QKC = D * QEB / 64;         // query chunks per lane = MFMAs per tile
+  constexpr int KCH = kF8 ? D / 64 : QKC;   // 16-byte key chunks a lane reads per tile
+  constexpr int PB = kF8 ? 8 : 16;          // bytes of one lane's piece of a value row
+  constexpr int EPL = PB / EB;              // value elements per piece
+  constexpr int NPC = D * EB / PB;          // pieces per head's value row
+  constexpr int RPS = kWave / NPC;          // value rows per wave read
+  constexpr int STEPS = TOK / RPS;
+  constexpr int kQuarters = (G + 3) / 4;    // MFMA output quarters holding real heads
+  static_assert(NCH % 4 == 0 || kF8, "row shape");
   constexpr int L = 2 * St::kCopies;        // copy instructions per wave per tile
   constexpr int NS = St::kTileSlots;
   static_assert(TOK % RPS == 0 && TOK <= 16, "tile rows");
@@ -119,6 +173,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   __shared__ uint4 kb2[NBUF > 2 ? NS : 1], vb2[NBUF > 2 ? NS : 1];
   __shared__ uint4 kb3[NBUF > 3 ? NS : 1], vb3[NBUF > 3 ? NS : 1];
   __shared__ float p_lds[HW][16][G];
+  // the query rows of each wave's GQA group, copied in like the tiles
+  constexpr int QB = G * D * QEB;
+  __shared__ uint4 q_lds[HW][QB / 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -155,8 +212,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
 
   const int quarter = lane >> 4;   // MFMA operand k-group / output row group
   const int col = lane & 15;       // MFMA A row (head) and B column (token)
-  const int rg = lane / NCH;       // value row within a step
-  const int li = lane % NCH;       // 16-byte chunk within a head's value row
+  const int rg = lane / NPC;       // value row within a step
+  const int li = lane % NPC;       // piece within a head's value row
 
   // Copy geometry.  Copy instruction i of this wave fills LDS slots
   // [(i*HW + wave)*64, +64) of the tile image; this lane's slot is row r, slot p,
@@ -168,7 +225,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     const int s = (i * HW + wave) * kWave + lane;
     const int r = s / St::kSlots;
     const int p = s % St::kSlots;
-    copy_off[i] = (uint32_t)(r * row_stride) + (uint32_t)((p ^ (r & St::kSwz)) * 16);
+    copy_off[i] = (uint32_t)(r * row_stride) + (uint32_t)((p ^ St::swz(r)) * 16);
   }
   const char* kcache = static_cast<const char*>(a.key_cache) + (int64_t)hg * St::kRowBytes;
   const char* vcache = static_cast<const char*>(a.value_cache) + (int64_t)hg * St::kRowBytes;
@@ -187,19 +244,24 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     int s, t, nt, stop;
   };
   // Moves c to the next sequence with real tiles in this share, or invalidates it.
+  // The cursor is wave-uniform; readfirstlane keeps it in scalar registers, so the
+  // plan is read with scalar loads whose waits leave the copies in flight alone.
   auto next_seq = [&](Cursor& c) {
-    int cs = cum[c.s + 1];
+    int s = uniform(c.s);
+    int cs = cum[s + 1];
     for (;;) {
-      ++c.s;
-      if (c.s >= B || cs + kSeqCost >= end) {
+      ++s;
+      if (s >= B || cs + kSeqCost >= end) {
+        c.s = s;
         c.t = c.stop = 0;
         return;
       }
-      const int cn = cum[c.s + 1];
+      const int cn = uniform(cum[s + 1]);
       if (cn > cs) {
+        c.s = s;
         c.t = 0;
         c.nt = cn - cs - kSeqCost;
-        c.stop = min(c.nt, (int)(end - cs - kSeqCost));
+        c.stop = uniform(min(c.nt, (int)(end - cs - kSeqCost)));
         return;
       }
       cs = cn;
@@ -208,9 +270,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   auto first_cursor = [&](Cursor& c) {
     const int cs = cum[seq0];
     c.s = seq0;
-    c.nt = cum[seq0 + 1] - cs - kSeqCost;
-    c.t = max(0, (int)(start - cs - kSeqCost));
-    c.stop = min(c.nt, (int)(end - cs - kSeqCost));
+    c.nt = uniform(cum[seq0 + 1] - cs - kSeqCost);
+    c.t = uniform(max(0, (int)(start - cs - kSeqCost)));
+    c.stop = uniform(min(c.nt, (int)(end - cs - kSeqCost)));
     if (c.t >= c.stop) next_seq(c);
   };
   auto advance = [&](Cursor& c) {
@@ -230,25 +292,24 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     int64_t base = 0;
     bad_pipe <<= 1;
     if (ic.t < ic.stop) {
-      const int tok0 = ic.t * TOK;
+      const int tok0 = uniform(ic.t * TOK);
       // a tile past the table (possible only with a stale plan) counts as invalid
-      const int32_t blk = tok0 < max_ctx ? tables[(int64_t)ic.s * MB + (tok0 >> shift)] : -1;
+      const int32_t blk =
+          uniform(tok0 < max_ctx ? tables[(int64_t)uniform(ic.s) * MB + (tok0 >> shift)] : -1);
       if (blk >= 0 && blk < num_blocks)
         base = (((int64_t)blk << shift) + (tok0 & bs_mask)) * row_stride;
       else
         bad_pipe |= 1u;
       advance(ic);
     }
-    char* kd = reinterpret_cast<char*>(kb) + wave * 1024;
-    char* vd = reinterpret_cast<char*>(vb) + wave * 1024;
+    const uint32_t kd = lds_addr(kb) + wave * 1024;
+    const uint32_t vd = lds_addr(vb) + wave * 1024;
+    const char* kbase = kcache + base;
+    const char* vbase = vcache + base;
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i)
-      __builtin_amdgcn_global_load_lds(PKV_AS_GLOBAL(kcache + base + copy_off[i]),
-                                       PKV_AS_LOCAL(kd + i * HW * 1024), 16, 0, 0);
+    for (int i = 0; i < St::kCopies; ++i) dma16(kbase, copy_off[i], kd + i * HW * 1024);
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i)
-      __builtin_amdgcn_global_load_lds(PKV_AS_GLOBAL(vcache + base + copy_off[i]),
-                                       PKV_AS_LOCAL(vd + i * HW * 1024), 16, 0, 0);
+    for (int i = 0; i < St::kCopies; ++i) dma16(vbase, copy_off[i], vd + i * HW * 1024);
   };
 
   // ---- compute side ------------------------------------------------------------------
@@ -259,18 +320,30 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   bool seg_from_zero = cc.t == 0;        // the segment began at the sequence's first tile
   int seg_bad = 0;
 
-  // Query rows of this kv head's group as the MFMA A operand.  Row m holds query
-  // head m % G: the rows past G repeat real ones and their scores are never used,
-  // so every lane loads unconditionally and the load's wait can stay where the
-  // first MFMA needs it (a masked load would be waited for at once, draining the
-  // copies in flight).
+  // Query rows of this kv head's group as the MFMA A operand.  A new sequence's G
+  // rows (contiguous in the query) are copied into q_lds with the tiles' copies, and
+  // read into registers at its first tile; row m of the operand holds query head
+  // m % G (the rows past G repeat real ones and their scores are never used).
+  // MFMA c takes the k-range [32c, 32c + 32) of the products (8c and 16c for fp32,
+  // in its steps of 4) in row chunks 4c + quarter.  With an E4M3 cache a lane instead
+  // takes the contiguous query chunks QKC * quarter + c, matching the contiguous key
+  // bytes it reads; a dot product may sum its terms in any order.
   uint4 qa[QKC];
+  bool q_fresh = false;   // a query copy was issued after the last step's copies
   auto load_query = [&](int s) {
-    const char* qrow = static_cast<const char*>(a.query) +
-                       ((int64_t)s * H + g * G + col % G) * D * EB;
+    q_fresh = true;
+    const char* src =
+        static_cast<const char*>(a.query) + ((int64_t)s * H + g * G) * (D * QEB);
 #pragma unroll
-    for (int c = 0; c < QKC; ++c)
-      qa[c] = *reinterpret_cast<const uint4*>(qrow + (4 * c + quarter) * 16);
+    for (int i = 0; i < (QB + 1023) / 1024; ++i) {
+      if (QB >= (i + 1) * 1024 || lane * 16 < QB - i * 1024)
+        dma16(src, (uint32_t)((i * kWave + lane) * 16), lds_addr(q_lds[wave]) + i * 1024);
+    }
+  };
+  auto read_query = [&]() {
+    const uint4* q = q_lds[wave] + (col % G) * (D * QEB / 16);
+#pragma unroll
+    for (int c = 0; c < QKC; ++c) qa[c] = q[kF8 ? QKC * quarter + c : 4 * c + quarter];
   };
 
   float m_run[G];
@@ -302,10 +375,22 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     // repeat rows; they are masked out below)
     const int kr = col & (TOK - 1);
     uint4 kk[QKC];
+    if constexpr (kF8) {
+      // 16 codes per chunk -> two bfloat16 operands (exact)
 #pragma unroll
-    for (int c = 0; c < QKC; ++c)
-      kk[c] = kb[kr * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ (kr & St::kSwz))];
-    const floatx4 s4 = tile_scores<T, QKC>(qa, kk);
+      for (int j = 0; j < KCH; ++j) {
+        const uint4 c8 = kb[kr * St::kSlots + ((wave * NCH + KCH * quarter + j) ^ St::swz(kr))];
+        const uint2 b0 = e4m3x4_to_bf16(c8.x), b1 = e4m3x4_to_bf16(c8.y);
+        const uint2 b2 = e4m3x4_to_bf16(c8.z), b3 = e4m3x4_to_bf16(c8.w);
+        kk[2 * j] = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        kk[2 * j + 1] = make_uint4(b2.x, b2.y, b3.x, b3.y);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < QKC; ++c)
+        kk[c] = kb[kr * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ St::swz(kr))];
+    }
+    const floatx4 s4 = tile_scores<QT, QKC>(qa, kk);
     const bool live = col < ntok;
     float sc[4];
     int gkey[4];
@@ -344,7 +429,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
     }
-    if (quarter < Geo::kQuarters) {
+    if (quarter < kQuarters) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (4 * quarter + j < G) p_lds[wave][col][(4 * quarter + j) % G] = sc[j];
@@ -358,7 +443,14 @@ void paged_attention_stream_kernel(AttentionArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) pv[h] = p_lds[wave][n][h];
       float v[EPL];
-      unpack_chunk<T>(vb[n * St::kSlots + ((wave * NCH + li) ^ (n & St::kSwz))], v);
+      if constexpr (kF8) {
+        const int slot = (wave * NCH + (li >> 1)) ^ St::swz(n);
+        const uint2 c8 = reinterpret_cast<const uint2*>(vb)[2 * (n * St::kSlots + slot) + (li & 1)];
+        e4m3x4_to_f32(c8.x, v);
+        e4m3x4_to_f32(c8.y, v + 4);
+      } else {
+        unpack_chunk<T>(vb[n * St::kSlots + ((wave * NCH + li) ^ St::swz(n))], v);
+      }
       if (!full && n >= ntok) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
@@ -375,7 +467,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   // a whole sequence, else the record under label w + sequence), 16 bytes at a time.
   auto finish = [&](bool whole) {
 #pragma unroll
-    for (int off = NCH; off < kWave; off <<= 1)
+    for (int off = NPC; off < kWave; off <<= 1)
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -385,11 +477,11 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     float l_head[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) l_head[h] = readlane(l_lane[h & 3], 16 * (h >> 2));
-    if (lane >= NCH) return;
+    if (lane >= NPC) return;
     float res[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float inv = 1.f / l_head[h];
+      const float inv = (kF8 ? a.v_scale : 1.f) / l_head[h];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) res[h][e] = seg_bad ? __builtin_nanf("") : acc[h][e] * inv;
     }
@@ -443,14 +535,24 @@ void paged_attention_stream_kernel(AttentionArgs a) {
 
   // One step of the ring: issue the copies of the tile NBUF - 1 ahead into the
   // buffer freed at the end of the previous step, wait for this wave's copies of
-  // tile j (the later tiles stay in flight), barrier (every wave's copies of tile j
-  // have landed), compute tile j, barrier (every wave is done reading its buffer),
-  // close the segment where it ends.
+  // tile j and its query loads (the later tiles stay in flight), barrier (every
+  // wave's copies of tile j have landed), compute tile j, barrier (every wave is
+  // done reading its buffer), close the segment where it ends.  The copies and the
+  // query loads are invisible to the compiler, so these are the only waits.
 #define PKV_STREAM_STEP(KB, VB, KF, VF)                                   \
   if (cc.t >= cc.stop) break;                                             \
   issue(KF, VF);                                                          \
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NBUF - 1) * L));                 \
+  if (NBUF > 2 && q_fresh) {                                              \
+    /* a new query's copy is newer than the previous steps' copies */     \
+    wait_copies<L>();                                                     \
+  } else {                                                                \
+    wait_copies<(NBUF - 1) * L>();                                        \
+  }                                                                       \
   bare_barrier();                                                         \
+  if (q_fresh) {                                                          \
+    read_query();                                                         \
+    q_fresh = false;                                                      \
+  }                                                                       \
   compute(KB, VB, (bad_pipe >> (NBUF - 1)) & 1u);                         \
   bare_barrier();                                                         \
   if (cc.t == cc.stop - 1) {                                              \
@@ -494,11 +596,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   }
 #undef PKV_STREAM_STEP
   // the ring's last copies (of block 0) land before the wave ends
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  wait_copies<0>();
 }
 
-#undef PKV_AS_GLOBAL
-#undef PKV_AS_LOCAL
 
 // ---- tile plan ---------------------------------------------------------------------
 
@@ -618,7 +718,7 @@ static int device_cus() {
 
 template <typename T, int D, int G, int HW>
 static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream) {
-  auto kernel = paged_attention_stream_kernel<T, D, G, HW, PKV_STREAM_NBUF>;
+  auto kernel = paged_attention_stream_kernel<T, D, G, HW, stream_nbuf<T>()>;
   // Workgroups one compute unit holds at once, from the kernel's own resource use.
   static const int per_cu = [&] {
     int n = 0;
@@ -639,7 +739,8 @@ static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream
 #endif
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides the kv heads and keeps
-// a token row of the group within PKV_STREAM_MAX_ROW bytes.
+// a token row of the group within PKV_STREAM_MAX_ROW bytes (and at 128 bytes or
+// more: 64-element E4M3 heads pair up).
 template <typename T, int D, int G>
 static hipError_t launch_stream_hw(const AttentionArgs& a, hipStream_t stream) {
   constexpr int kRow = D * T::kElemBytes;
@@ -647,8 +748,12 @@ static hipError_t launch_stream_hw(const AttentionArgs& a, hipStream_t stream) {
     if (a.num_kv_heads % 8 == 0) return launch_stream_shape<T, D, G, 8>(a, stream);
   if constexpr (4 * kRow <= PKV_STREAM_MAX_ROW)
     if (a.num_kv_heads % 4 == 0) return launch_stream_shape<T, D, G, 4>(a, stream);
+  // a tile row spans at least 128 bytes
   if (a.num_kv_heads % 2 == 0) return launch_stream_shape<T, D, G, 2>(a, stream);
-  return launch_stream_shape<T, D, G, 1>(a, stream);
+  if constexpr (kRow >= 128)
+    return launch_stream_shape<T, D, G, 1>(a, stream);
+  else
+    return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
@@ -663,7 +768,10 @@ static hipError_t launch_stream_g(const AttentionArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream) {
-  if (a.kv_bf16) {
+  if (a.kv_fp8) {
+    if (a.head_dim == 64) return launch_stream_g<FP8, 64>(a, stream);
+    if (a.head_dim == 128) return launch_stream_g<FP8, 128>(a, stream);
+  } else if (a.kv_bf16) {
     if (a.head_dim == 64) return launch_stream_g<BF16, 64>(a, stream);
     if (a.head_dim == 128) return launch_stream_g<BF16, 128>(a, stream);
   } else {

@@ -19,9 +19,15 @@ int log2_exact(int64_t x) {
   return s;
 }
 
-size_t elem_bytes(pkv_dtype t) { return t == PKV_BF16 ? 2 : 4; }
+size_t elem_bytes(int32_t t) { return t == PKV_FP8_E4M3 ? 1 : t == PKV_BF16 ? 2 : 4; }
 
+// Arithmetic types (queries, outputs, the inputs of a quantised write).
 bool valid_dtype(int32_t t) { return t == PKV_F32 || t == PKV_BF16; }
+// Types a cache may hold (bit copies).
+bool valid_storage(int32_t t) { return valid_dtype(t) || t == PKV_FP8_E4M3; }
+
+// A cache scale: positive and finite.
+bool valid_scale(float x) { return std::isfinite(x) && x > 0.f; }
 
 // Multiplication of non-negative sizes with an overflow check against a limit.
 bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
@@ -101,12 +107,22 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
                                int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                int32_t partition_size, int32_t kv_dtype, int32_t out_dtype,
                                void* workspace, size_t workspace_bytes, bool need_inputs,
-                               pkv::AttentionArgs* a) {
+                               pkv::AttentionArgs* a, float k_scale = 1.f,
+                               float v_scale = 1.f) {
   AttnShape s;
   pkv_status st = check_attention_shape(num_seqs, num_heads, head_dim, block_size,
                                         max_blocks_per_seq, partition_size, &s);
   if (st != PKV_OK) return st;
-  if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_INVALID_ARG;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  if (!(valid_dtype(kv_dtype) || fp8) || !valid_dtype(out_dtype)) return PKV_ERR_INVALID_ARG;
+  if (fp8) {
+    if (!valid_scale(k_scale) || !valid_scale(v_scale) ||
+        !std::isfinite(static_cast<float>(static_cast<double>(scale) * k_scale * 1.4426950408889634)))
+      return PKV_ERR_INVALID_ARG;   // the score factor must stay a finite fp32
+    if (!s.balanced) return PKV_ERR_UNSUPPORTED;   // E4M3 caches use the balanced split
+    if (need_inputs && head_dim == 64 && num_kv_heads % 2 != 0)
+      return PKV_ERR_UNSUPPORTED;                  // a staged row spans at least 128 bytes
+  }
   if (need_inputs) {
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
     if (num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale))
@@ -144,10 +160,14 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   a->block_shift = log2_exact(block_size);
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->num_blocks = num_blocks;
-  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  // scale * log2(e), and the key cache's scale for E4M3 codes
+  a->scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? k_scale : 1.f) *
+                                     1.4426950408889634);
   a->partition_size = s.partition;
   a->max_parts = static_cast<int>(s.max_parts);
   a->kv_bf16 = kv_dtype == PKV_BF16;
+  a->kv_fp8 = fp8;
+  a->v_scale = fp8 ? v_scale : 1.f;
   a->out_bf16 = out_dtype == PKV_BF16;
   a->balanced = s.balanced;
   set_workspace(a, workspace, s.plan_bytes, s.recs);
@@ -155,6 +175,17 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// The three stages of a decode call on one stream.
+pkv_status run_decode(const pkv::AttentionArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pkv_status st = hip_status(pkv::launch_attention_plan(a, s));
+  if (st != PKV_OK) return st;
+  st = hip_status(pkv::launch_attention_partition(a, s));
+  if (st != PKV_OK) return st;
+  if (a.balanced || a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));
+  return st;
+}
 
 }  // namespace
 
@@ -196,7 +227,7 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
                               int64_t num_blocks, pkv_dtype kv_dtype, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!valid_storage(kv_dtype)) return PKV_ERR_INVALID_ARG;
   int64_t row = 0, slots = 0;
   if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row))
     return PKV_ERR_INVALID_ARG;
@@ -211,13 +242,36 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
                                             static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, void* key_cache,
+                                  void* value_cache, const int32_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, pkv_dtype in_dtype,
+                                  float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_scale(k_scale) || !valid_scale(v_scale))
+    return PKV_ERR_INVALID_ARG;
+  int64_t row = 0, slots = 0, cache_bytes = 0;   // row: elements = cache bytes
+  if (!mul_ok(num_kv_heads, head_dim, INT32_MAX / 8, &row) ||
+      !mul_ok(num_blocks, block_size, INT64_MAX / 4096, &slots) ||
+      !mul_ok(slots, row, INT64_MAX / 2, &cache_bytes))
+    return PKV_ERR_INVALID_ARG;
+  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  return hip_status(pkv::launch_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping,
+                                                num_tokens, static_cast<int>(row), slots,
+                                                in_dtype == PKV_BF16, k_scale, v_scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                            int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
                            void* stream) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!valid_storage(kv_dtype)) return PKV_ERR_INVALID_ARG;
   int64_t row = 0, block = 0, cache_bytes = 0;
   if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row) ||
       !mul_ok(row, block_size, INT32_MAX / 2, &block) ||
@@ -240,17 +294,25 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, 
   return s.ws_bytes;
 }
 
-pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
-                               const void* key, const void* value, void* key_cache,
-                               void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
-                               int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
-                               int32_t partition_size, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_decode_prologue and its E4M3 form: quant 0 copies the rows of the cache's own
+// type (kv_dtype), quant != 0 stores the E4M3 codes of in_dtype rows.
+pkv_status prologue(const int32_t* block_tables, const int32_t* context_lens, const void* key,
+                    const void* value, void* key_cache, void* value_cache,
+                    int32_t* slot_mapping, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t kv_dtype, bool quant, int32_t in_dtype,
+                    float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (!valid_dtype(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!valid_storage(kv_dtype)) return PKV_ERR_INVALID_ARG;
+  if (quant && (!valid_dtype(in_dtype) || !valid_scale(k_scale) || !valid_scale(v_scale)))
+    return PKV_ERR_INVALID_ARG;
   AttnShape s;
   pkv_status st = check_attention_shape(num_seqs, 1, 64, block_size, max_blocks_per_seq,
                                         partition_size, &s);
@@ -268,11 +330,42 @@ pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* conte
   if (!workspace || workspace_bytes < s.plan_bytes) return PKV_ERR_WORKSPACE;
   pkv::AttentionArgs a{};
   set_workspace(&a, workspace, s.plan_bytes, 0);
+  const int q = !quant ? 0 : in_dtype == PKV_BF16 ? 2 : 1;
   return hip_status(pkv::launch_decode_prologue(
       block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping, num_seqs,
       max_blocks_per_seq, log2_exact(block_size), num_blocks, static_cast<int>(row), s.partition,
-      a.plan_items, a.plan_count, s.balanced, a.tile_cum, a.tile_hdr,
+      a.plan_items, a.plan_count, s.balanced, a.tile_cum, a.tile_hdr, q, k_scale, v_scale,
       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
+                               const void* key, const void* value, void* key_cache,
+                               void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, pkv_dtype kv_dtype,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return prologue(block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping,
+                  num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, block_size, num_blocks,
+                  kv_dtype, false, kv_dtype, 1.f, 1.f, partition_size, workspace,
+                  workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_prologue_fp8(const int32_t* block_tables, const int32_t* context_lens,
+                                   const void* key, const void* value, void* key_cache,
+                                   void* value_cache, int32_t* slot_mapping, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   pkv_dtype in_dtype, float k_scale, float v_scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return prologue(block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping,
+                  num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, block_size, num_blocks,
+                  PKV_FP8_E4M3, true, in_dtype, k_scale, v_scale, 0, workspace,
+                  workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
@@ -307,6 +400,7 @@ pkv_status pkv_paged_attention_partition(void* out, const void* query, const voi
                                          float scale, int32_t partition_size,
                                          pkv_dtype kv_dtype, pkv_dtype out_dtype,
                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;   // the _fp8 entry carries scales
   pkv::AttentionArgs a;
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
@@ -339,6 +433,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
                                       int64_t num_blocks, float scale, int32_t partition_size,
                                       pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
+  if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;   // the _fp8 entry carries scales
   pkv::AttentionArgs a;
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
@@ -346,13 +441,46 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
                                       partition_size, kv_dtype, out_dtype, workspace,
                                       workspace_bytes, true, &a);
   if (st != PKV_OK || num_seqs == 0) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(pkv::launch_attention_plan(a, s));
-  if (st != PKV_OK) return st;
-  st = hip_status(pkv::launch_attention_partition(a, s));
-  if (st != PKV_OK) return st;
-  if (a.balanced || a.max_parts > 1) st = hip_status(pkv::launch_attention_reduce(a, s));
-  return st;
+  return run_decode(a, stream);
+}
+
+pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
+                                             const void* key_cache, const void* value_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size,
+                                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                                             float scale, float k_scale, float v_scale,
+                                             pkv_dtype out_dtype, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  pkv::AttentionArgs a;
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale, 0,
+                                      PKV_FP8_E4M3, out_dtype, workspace, workspace_bytes, true,
+                                      &a, k_scale, v_scale);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return hip_status(pkv::launch_attention_partition(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                                          float scale, float k_scale, float v_scale,
+                                          pkv_dtype out_dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  pkv::AttentionArgs a;
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale, 0,
+                                      PKV_FP8_E4M3, out_dtype, workspace, workspace_bytes, true,
+                                      &a, k_scale, v_scale);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return run_decode(a, stream);
 }
 
 }  // extern "C"

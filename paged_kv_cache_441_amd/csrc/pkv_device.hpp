@@ -24,6 +24,48 @@ struct BF16 {
   static constexpr int kPerChunk = 8;
 };
 
+// An 8-bit float cache (OCP E4M3: sign, 4 exponent bits biased by 7, 3 mantissa
+// bits, no infinities, S.1111.111 the NaN, 448 the largest finite value).  Queries
+// beside such a cache are bfloat16.
+struct FP8 {
+  using storage = uint8_t;
+  static constexpr int kElemBytes = 1;
+  static constexpr int kPerChunk = 16;
+};
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 code of x, rounded to the nearest value with ties to the even code; finite
+// magnitudes of 448 and beyond (and infinities) give +-448, NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                  // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;          // |x| >= 448
+  if (a < 0x3c800000u)                                // |x| < 2^-6: codes m * 2^-9
+    return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.f));
+  // normal: move the exponent bias from 127 to 7, then round the 23 mantissa bits
+  // to 3, ties to even (a carry out of the mantissa raises the exponent)
+  uint32_t b = a - (120u << 23);
+  b += 0x7ffffu + ((b >> 20) & 1u);
+  return sign | (b >> 20);
+}
+
+// Four E4M3 codes (one 32-bit word, lowest byte first) to fp32 or bfloat16; every
+// E4M3 value is exact in both.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* v) {
+  const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+}
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
 // bfloat16 -> fp32 is exact: the 16 bits are the top half of the fp32 pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -15,15 +15,22 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
                               void* value_cache, const int32_t* slot_mapping, int num_tokens,
                               int row_bytes, int64_t num_slots, hipStream_t stream);
 
+// E4M3 cache rows from fp32 or bfloat16 inputs divided by k_scale / v_scale.
+hipError_t launch_cache_write_fp8(const void* key, const void* value, void* key_cache,
+                                  void* value_cache, const int32_t* slot_mapping, int num_tokens,
+                                  int row_elems, int64_t num_slots, bool in_bf16, float k_scale,
+                                  float v_scale, hipStream_t stream);
+
 // Builds the fixed-partition plan (plan_items, plan_count) or, when balanced, the
-// tile plan (tile_cum, tile_hdr).
+// tile plan (tile_cum, tile_hdr).  quant: 0 copies the new rows, 1 and 2 store the
+// E4M3 codes of fp32 or bfloat16 rows (row_bytes are then the cache row's bytes).
 hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
                                   const void* key, const void* value, void* key_cache,
                                   void* value_cache, int32_t* slot_mapping, int num_seqs,
                                   int max_blocks_per_seq, int block_shift, int64_t num_blocks,
                                   int row_bytes, int partition_size, int4* plan_items,
                                   int* plan_count, bool balanced, int* tile_cum, int* tile_hdr,
-                                  hipStream_t stream);
+                                  int quant, float k_scale, float v_scale, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                               int num_pairs, int64_t block_bytes, int64_t num_blocks,
@@ -47,7 +54,9 @@ struct AttentionArgs {
   int partition_size;
   int max_parts;            // ceil(max_blocks_per_seq * block_size / partition_size)
   bool kv_bf16;
+  bool kv_fp8;              // E4M3 caches (queries bfloat16); scale_log2 includes k_scale
   bool out_bf16;
+  float v_scale;            // E4M3 caches: multiplies the value rows
   int* plan_count;          // number of work items in the plan
   int4* plan_items;         // [num_seqs * max_parts] (seq, partition, context length, partitions)
   float* ws_m;              // [num_seqs][num_heads][max_parts]

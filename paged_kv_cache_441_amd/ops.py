@@ -17,6 +17,8 @@ import torch
 from . import _lib
 
 _KV_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+# E4M3 caches hold raw codes: uint8, or torch's float8_e4m3fn (the same format)
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _dev(t: torch.Tensor, name: str) -> None:
@@ -39,6 +41,20 @@ def _kv(t: torch.Tensor, name: str) -> int:
     if t.dtype not in _KV_DTYPES:
         raise TypeError(f"{name} must be float32 or bfloat16 (got {t.dtype})")
     return _KV_DTYPES[t.dtype]
+
+
+def _fp8(t: torch.Tensor, name: str) -> None:
+    _dev(t, name)
+    if t.dtype not in _FP8_DTYPES:
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn; got {t.dtype})")
+
+
+def _storage(t: torch.Tensor, name: str) -> int:
+    """Cache element type for bit copies: float32, bfloat16 or E4M3 codes."""
+    if isinstance(t, torch.Tensor) and t.dtype in _FP8_DTYPES:
+        _dev(t, name)
+        return _lib.PKV_FP8_E4M3
+    return _kv(t, name)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -251,12 +267,136 @@ def decode_step(query, key, value, key_cache, value_cache, block_tables, context
                                   workspace=workspace)
 
 
+# ---- E4M3 (FP8) caches ---------------------------------------------------------------
+
+def _fp8_caches(key_cache, value_cache):
+    _fp8(key_cache, "key_cache")
+    _fp8(value_cache, "value_cache")
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("caches must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    return key_cache.shape
+
+
+def kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                       v_scale: float) -> None:
+    """reshape_and_cache into E4M3 caches: each token's rows divided by the cache's
+    scale, rounded to E4M3 (ties to even, saturating at 448)."""
+    dt = _kv(key, "key")
+    if _kv(value, "value") != dt:
+        raise TypeError("value dtype differs from key")
+    NB, BS, Hkv, D = _fp8_caches(key_cache, value_cache)
+    _i32(slot_mapping, "slot_mapping")
+    _same_device(key, value, key_cache, value_cache, slot_mapping)
+    T = slot_mapping.shape[0]
+    if key.shape != (T, Hkv, D) or value.shape != (T, Hkv, D):
+        raise ValueError(f"key/value must be [{T}, {Hkv}, {D}]")
+    lib = _lib.load_library()
+    st = lib.pkv_kv_cache_write_fp8(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                    _ptr(slot_mapping), T, Hkv, D, BS, NB, dt, float(k_scale),
+                                    float(v_scale), _stream(key))
+    _lib.check(st, "pkv_kv_cache_write_fp8")
+
+
+def decode_prologue_fp8(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, workspace: torch.Tensor, k_scale: float,
+                        v_scale: float, slot_mapping: Optional[torch.Tensor] = None
+                        ) -> torch.Tensor:
+    """decode_prologue for E4M3 caches (balanced-split plan); returns the slots."""
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    dt = _kv(key, "key")
+    if _kv(value, "value") != dt:
+        raise TypeError("value dtype differs from key")
+    NB, BS, Hkv, D = _fp8_caches(key_cache, value_cache)
+    _dev(workspace, "workspace")
+    B = context_lens.shape[0]
+    if key.shape != (B, Hkv, D) or value.shape != (B, Hkv, D):
+        raise ValueError(f"key/value must be [{B}, {Hkv}, {D}]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(B, dtype=torch.int32, device=key.device)
+    _i32(slot_mapping, "slot_mapping")
+    _same_device(block_tables, context_lens, key, value, key_cache, value_cache, workspace,
+                 slot_mapping)
+    lib = _lib.load_library()
+    st = lib.pkv_decode_prologue_fp8(_ptr(block_tables), _ptr(context_lens), _ptr(key),
+                                     _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                     _ptr(slot_mapping), B, block_tables.shape[1], Hkv, D, BS, NB,
+                                     dt, float(k_scale), float(v_scale), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(key))
+    _lib.check(st, "pkv_decode_prologue_fp8")
+    return slot_mapping
+
+
+def _fp8_attention_args(query, key_cache, value_cache, block_tables, context_lens, out,
+                        out_dtype, workspace):
+    _dev(query, "query")
+    if query.dtype != torch.bfloat16:
+        raise TypeError("query must be bfloat16 beside E4M3 caches")
+    NB, BS, Hkv, Dk = _fp8_caches(key_cache, value_cache)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if query.dim() != 3:
+        raise ValueError("query [B, H, D]")
+    B, H, D = query.shape
+    if Dk != D or context_lens.shape != (B,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype, device=query.device)
+    if out.dtype not in _KV_DTYPES or out.shape != (B, H, D):
+        raise ValueError("out must be float32/bfloat16 [B, H, D]")
+    _dev(out, "out")
+    if workspace is None:
+        workspace = alloc_workspace(query, block_tables, BS, 0)
+    _dev(workspace, "workspace")
+    _same_device(query, key_cache, value_cache, block_tables, context_lens, out, workspace)
+    return out, workspace, workspace.numel() * workspace.element_size(), B, H, Hkv, D, BS, NB
+
+
+def paged_attention_decode_fp8(query: torch.Tensor, key_cache: torch.Tensor,
+                               value_cache: torch.Tensor, block_tables: torch.Tensor,
+                               context_lens: torch.Tensor, scale: float, k_scale: float,
+                               v_scale: float, out: Optional[torch.Tensor] = None,
+                               out_dtype: torch.dtype = torch.float32,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention over E4M3 caches (bf16 queries, balanced split)."""
+    out, ws, wsb, B, H, Hkv, D, BS, NB = _fp8_attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        float(k_scale), float(v_scale), _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
+    _lib.check(st, "pkv_paged_attention_decode_fp8")
+    return out
+
+
+def paged_attention_partition_fp8(query, key_cache, value_cache, block_tables, context_lens,
+                                  scale, k_scale, v_scale, out=None, out_dtype=torch.float32,
+                                  workspace=None):
+    """Stage 2 over E4M3 caches (needs a balanced plan in ``workspace``); returns
+    (out, workspace)."""
+    out, ws, wsb, B, H, Hkv, D, BS, NB = _fp8_attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_partition_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        float(k_scale), float(v_scale), _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
+    _lib.check(st, "pkv_paged_attention_partition_fp8")
+    return out, ws
+
+
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                 pairs: torch.Tensor) -> None:
     """Copy-on-write copies: block dst of both caches becomes block src, for every
     (src, dst) row of ``pairs`` (int32 [n, 2] on the caches' device)."""
-    dt = _kv(key_cache, "key_cache")
-    if _kv(value_cache, "value_cache") != dt:
+    dt = _storage(key_cache, "key_cache")
+    if _storage(value_cache, "value_cache") != dt:
         raise TypeError("value_cache dtype differs from key_cache")
     _i32(pairs, "pairs")
     _same_device(key_cache, value_cache, pairs)

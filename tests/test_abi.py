@@ -190,3 +190,74 @@ def test_binding_fails_loudly_without_gpu_tensors():
     cl = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         pkv.slot_mapping(bt, cl, 16, 64)
+
+
+FP8 = _lib.PKV_FP8_E4M3
+
+
+def _decode_fp8(lib, B=4, H=32, Hkv=8, D=128, BS=16, MB=64, NB=1024, scale=0.1, ks=0.5, vs=0.5,
+                outd=F32, out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, ws=FAKE,
+                wsb=1 << 30, fn="pkv_paged_attention_decode_fp8"):
+    return getattr(lib, fn)(out, query, kc, vc, bt, cl, B, H, Hkv, D, BS, MB, NB, scale, ks, vs,
+                            outd, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("fn", ["pkv_paged_attention_decode_fp8",
+                                "pkv_paged_attention_partition_fp8"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), INV),
+    (dict(vs=-1.0), INV),
+    (dict(ks=float("nan")), INV),
+    (dict(vs=float("inf")), INV),
+    (dict(scale=1e30, ks=1e30), INV),   # scale * k_scale overflows
+    (dict(outd=FP8), INV),
+    (dict(query=NULL), INV),
+    (dict(D=64, H=12, Hkv=3), UNS),     # 64-byte rows need an even kv-head count
+    (dict(D=96), UNS),
+    (dict(H=24), UNS),
+    (dict(wsb=16), WS),
+])
+def test_fp8_attention_rejects(lib, cpu_only, fn, kw, status):
+    assert _decode_fp8(lib, fn=fn, **kw) == status
+
+
+def test_fp8_workspace_is_the_balanced_one_and_unscaled_entries_reject_fp8(lib, cpu_only):
+    need = _ws_balanced(4, 32, 128)
+    assert _decode_fp8(lib, wsb=need - 1) == WS
+    assert _decode(lib, kvd=FP8) == INV
+    assert lib.pkv_paged_attention_partition(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 128,
+                                             16, 64, 1024, 0.1, 0, FP8, F32, FAKE, 1 << 30,
+                                             NULL) == INV
+    assert _decode_fp8(lib, B=0, out=NULL, query=NULL, kc=NULL, vc=NULL, bt=NULL, cl=NULL,
+                       ws=NULL, wsb=0) == OK
+
+
+def test_fp8_write_and_prologue_reject(lib, cpu_only):
+    w = lib.pkv_kv_cache_write_fp8
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 1024, BF16, 0.5, 0.5, NULL]
+    bad = list(args); bad[10] = FP8                                    # input must be f32/bf16
+    assert w(*bad) == INV
+    bad = list(args); bad[11] = 0.0
+    assert w(*bad) == INV
+    bad = list(args); bad[12] = float("nan")
+    assert w(*bad) == INV
+    bad = list(args); bad[6], bad[7] = 1, 8                            # 8-byte rows
+    assert w(*bad) == UNS
+    bad = list(args); bad[4] = NULL
+    assert w(*bad) == INV
+    empty = list(args); empty[5] = 0
+    assert w(*[NULL if i < 5 else x for i, x in enumerate(empty)]) == OK
+    p = lib.pkv_decode_prologue_fp8
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 8, 128, 16, 1024, BF16, 0.5, 0.5,
+            FAKE, 1 << 20, NULL]
+    bad = list(args); bad[13] = FP8
+    assert p(*bad) == INV
+    bad = list(args); bad[15] = -0.5
+    assert p(*bad) == INV
+    bad = list(args); bad[17] = 100
+    assert p(*bad) == WS
+    # the plain cache write and block copies take E4M3 caches as bit copies
+    assert lib.pkv_kv_cache_write(NULL, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 1024, FP8,
+                                  NULL) == INV
+    assert lib.pkv_kv_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 8, 16, 1024, FP8,
+                                  NULL) == UNS                         # 8-byte rows

@@ -69,3 +69,35 @@ def test_poison_placement_tiny():
                 assert (row != P).all()
             else:
                 assert (row == P).all()
+
+
+def test_fp8_batch_codes_and_poison():
+    from workloads import make_fp8_config
+    from workloads.decode_batches import FP8_POISON
+    b = make_fp8_config("tiny_fp8")
+    a = make_fp8_config("tiny_fp8")
+    assert b.key_cache.dtype == torch.uint8 and b.query.dtype == torch.bfloat16
+    assert torch.equal(a.key_cache, b.key_cache) and torch.equal(a.value, b.value)
+    assert b.kv_bytes() == int(b.context_lens.sum()) * 4 * 64 * 2
+    BS = b.spec.block_size
+    used = set(b.referenced_blocks().tolist())
+    for cache in (b.key_cache.numpy(), b.value_cache.numpy()):
+        for blk in range(b.spec.num_blocks):
+            if blk not in used:
+                assert (cache[blk] == FP8_POISON).all()
+        hist = []
+        for i in range(b.num_seqs):
+            ctx = int(b.context_lens[i])
+            for t in range(-(-ctx // BS) * BS):
+                row = cache[b.block_tables[i, t // BS], t % BS]
+                if t < ctx - 1:
+                    hist.append(row)
+                else:
+                    assert (row == FP8_POISON).all()
+        hist = np.concatenate(hist)
+        # history rows: finite codes only (no 0x7F / 0xFF), every sign and exponent
+        assert not np.isin(hist, [0x7F, 0xFF]).any()
+        assert len(np.unique(hist >> 3)) == 32
+    # same context draws and tables as the bf16/f32 form of the workload
+    c = make_config("tiny")
+    assert (c.context_lens == b.context_lens).all() and (c.block_tables == b.block_tables).all()

@@ -7,9 +7,12 @@ gather, no attention.  Both the HIP path and the CPU oracle consume what it make
 
 from .decode_batches import (  # noqa: F401
     CONFIGS,
+    FP8_CONFIGS,
     DecodeBatch,
     build_batch,
+    build_fp8_batch,
     make_config,
+    make_fp8_config,
     permute_physical_blocks,
     poison_bits,
     unshare_prefix_blocks,

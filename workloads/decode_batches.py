@@ -32,6 +32,7 @@ import torch
 
 BF16_POISON = 0x7FA5          # a quiet NaN in bfloat16 with a payload
 F32_POISON = 0x7FC0DEAD       # a quiet NaN in float32 with a payload
+FP8_POISON = 0x7F             # the E4M3 NaN code
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _INT_VIEW = {"f32": torch.int32, "bf16": torch.int16}
@@ -120,7 +121,7 @@ class DecodeBatch:
 
     def kv_bytes(self) -> int:
         """Bytes of K and V one decode step must read: sum(ctx) * Hkv * D * 2 * elem."""
-        elem = 4 if self.spec.kv_dtype == "f32" else 2
+        elem = {"f32": 4, "bf16": 2, "fp8": 1}[self.spec.kv_dtype]
         return int(self.context_lens.astype(np.int64).sum()) * self.spec.num_kv_heads * \
             self.spec.head_dim * 2 * elem
 
@@ -130,9 +131,12 @@ class DecodeBatch:
 
     # --- host views for the CPU side -------------------------------------------
     def numpy_storage(self, t: torch.Tensor) -> np.ndarray:
-        """Raw storage of a tensor as numpy: float32 for f32, uint16 bit patterns for bf16."""
+        """Raw storage of a tensor as numpy: float32 for f32, uint16 bit patterns for
+        bf16, uint8 codes for an E4M3 cache."""
         t = t.detach().cpu().contiguous()
-        if self.spec.kv_dtype == "f32":
+        if t.dtype == torch.float32:
+            return t.numpy()
+        if t.dtype == torch.uint8:
             return t.numpy()
         return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -269,6 +273,88 @@ def build_batch(spec: ConfigSpec, context_lens: Sequence[int], device="cpu",
     return DecodeBatch(spec=spec, context_lens=ctx, block_tables=block_tables.astype(np.int32),
                        query=query, key=key, value=value, key_cache=key_cache,
                        value_cache=value_cache, scale=1.0 / math.sqrt(D))
+
+
+# -----------------------------------------------------------------------------------
+# E4M3 (FP8) caches
+# -----------------------------------------------------------------------------------
+# The history rows hold codes drawn uniformly from the 254 finite E4M3 codes (every
+# sign, exponent and mantissa), so that every decode case is exercised; with the
+# cache scales below the values they stand for span about 1e-6 .. 4 in magnitude.
+# Queries and the new tokens' rows are bfloat16 N(0, 1); the write quantises the new
+# rows.  The scales are not powers of two, so the fp32 quotient x / scale rounds.
+FP8_K_SCALE = 0.0089
+FP8_V_SCALE = 0.0113
+
+
+def _finite_codes(gen: torch.Generator, shape, device) -> torch.Tensor:
+    r = torch.randint(0, 254, shape, generator=gen, dtype=torch.int32, device=device)
+    return (r + (r >= FP8_POISON).to(torch.int32)).to(torch.uint8)   # skip 0x7F; 0xFF unreachable
+
+
+def build_fp8_batch(spec: ConfigSpec, context_lens: Sequence[int], device="cpu",
+                    seed: Optional[int] = None, block_tables: Optional[np.ndarray] = None,
+                    max_blocks_per_seq: Optional[int] = None) -> DecodeBatch:
+    """One decode batch with E4M3 caches (uint8 codes) for ``spec`` (kv_dtype "fp8");
+    ``extra`` holds k_scale and v_scale."""
+    assert spec.kv_dtype == "fp8"
+    seed = spec.seed if seed is None else seed
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    assert ctx.ndim == 1 and (ctx >= 1).all()
+    spec = replace(spec, num_seqs=int(ctx.shape[0]),
+                   max_context=max(spec.max_context, int(ctx.max())))
+    if block_tables is None:
+        block_tables = deal_block_tables(spec, ctx, seed, max_blocks_per_seq)
+    B, H, Hkv, D = spec.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim
+    BS, NB = spec.block_size, spec.num_blocks
+    device = torch.device(device)
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1_000_003 + 29)
+    query = _randn(gen, (B, H, D), "bf16", device)
+    key = _randn(gen, (B, Hkv, D), "bf16", device)
+    value = _randn(gen, (B, Hkv, D), "bf16", device)
+
+    key_cache = torch.full((NB, BS, Hkv, D), FP8_POISON, dtype=torch.uint8, device=device)
+    value_cache = torch.full((NB, BS, Hkv, D), FP8_POISON, dtype=torch.uint8, device=device)
+    ids = block_tables[block_tables >= 0]
+    _, first = np.unique(ids, return_index=True)
+    ids = ids[np.sort(first)]
+    chunk = 8192
+    for c0 in range(0, ids.shape[0], chunk):
+        idx = torch.as_tensor(ids[c0:c0 + chunk].astype(np.int64), device=device)
+        n = int(idx.shape[0])
+        key_cache[idx] = _finite_codes(gen, (n, BS, Hkv, D), device)
+        value_cache[idx] = _finite_codes(gen, (n, BS, Hkv, D), device)
+    for i in range(B):
+        history = int(ctx[i]) - 1
+        j = -(-int(ctx[i]) // BS) - 1
+        b = int(block_tables[i, j])
+        key_cache[b, history - j * BS:].fill_(FP8_POISON)
+        value_cache[b, history - j * BS:].fill_(FP8_POISON)
+    return DecodeBatch(spec=spec, context_lens=ctx, block_tables=block_tables.astype(np.int32),
+                       query=query, key=key, value=value, key_cache=key_cache,
+                       value_cache=value_cache, scale=1.0 / math.sqrt(D),
+                       extra={"k_scale": FP8_K_SCALE, "v_scale": FP8_V_SCALE})
+
+
+# E4M3-cache forms of the named workloads: same shapes, context draws and tables.
+FP8_CONFIGS = {
+    "tiny_fp8": replace(CONFIGS["tiny"], name="tiny_fp8", kv_dtype="fp8"),
+    "llama3_8b_fp8": replace(CONFIGS["llama3_8b"], name="llama3_8b_fp8", kv_dtype="fp8"),
+    "long_ctx_fp8": replace(CONFIGS["long_ctx"], name="long_ctx_fp8", kv_dtype="fp8",
+                            partition_size=0),
+}
+
+
+def make_fp8_config(name: str, device="cpu", seed: Optional[int] = None,
+                    num_seqs: Optional[int] = None) -> DecodeBatch:
+    spec = FP8_CONFIGS[name]
+    ctx = draw_context_lens(spec, seed)
+    tables = deal_block_tables(spec, ctx, seed)
+    if num_seqs is not None:
+        ctx, tables = ctx[:num_seqs], tables[:num_seqs]
+    return build_fp8_batch(spec, ctx, device=device, seed=seed, block_tables=tables)
 
 
 def make_config(name: str, device="cpu", seed: Optional[int] = None,
