@@ -8,11 +8,14 @@ gather, no attention.  Both the HIP path and the CPU oracle consume what it make
 from .decode_batches import (  # noqa: F401
     CONFIGS,
     FP8_CONFIGS,
+    MULTI_CONFIGS,
     DecodeBatch,
     build_batch,
     build_fp8_batch,
+    build_multi_batch,
     make_config,
     make_fp8_config,
+    make_multi_config,
     permute_physical_blocks,
     poison_bits,
     unshare_prefix_blocks,

@@ -276,6 +276,98 @@ def build_batch(spec: ConfigSpec, context_lens: Sequence[int], device="cpu",
 
 
 # -----------------------------------------------------------------------------------
+# several new tokens per sequence (chunked prefill, verification of speculated tokens)
+# -----------------------------------------------------------------------------------
+# A step hands sequence i q_len_i new tokens, packed into one flat batch in sequence
+# order (query_start_loc[i] .. query_start_loc[i+1]); context_lens[i] counts them, so
+# the cache holds ctx_i - q_len_i tokens of history.  Values and poison as for decode:
+# every row at or after the first new position is poisoned until the step writes it.
+
+def build_multi_batch(spec: ConfigSpec, context_lens: Sequence[int], query_lens: Sequence[int],
+                      device="cpu", seed: Optional[int] = None,
+                      block_tables: Optional[np.ndarray] = None) -> DecodeBatch:
+    """A multi-token step; query/key/value are [T, ...] over the flat token batch and
+    ``extra`` holds query_lens and query_start_loc (int32 numpy arrays)."""
+    seed = spec.seed if seed is None else seed
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    ql = np.asarray(query_lens, dtype=np.int32)
+    assert ctx.ndim == 1 and ql.shape == ctx.shape and (ql >= 0).all() and (ctx >= 1).all()
+    assert (ql <= ctx).all()
+    spec = replace(spec, num_seqs=int(ctx.shape[0]),
+                   max_context=max(spec.max_context, int(ctx.max())))
+    if block_tables is None:
+        block_tables = deal_block_tables(spec, ctx, seed)
+    B, H, Hkv, D = spec.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim
+    BS, NB = spec.block_size, spec.num_blocks
+    dt = spec.kv_dtype
+    T = int(ql.sum())
+    qsl = np.zeros(B + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(ql)
+    device = torch.device(device)
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1_000_003 + 41)
+    query = _randn(gen, (T, H, D), dt, device)
+    key = _randn(gen, (T, Hkv, D), dt, device)
+    value = _randn(gen, (T, Hkv, D), dt, device)
+
+    key_cache = _poisoned((NB, BS, Hkv, D), dt, device)
+    value_cache = _poisoned((NB, BS, Hkv, D), dt, device)
+    ids = block_tables[block_tables >= 0]
+    _, first = np.unique(ids, return_index=True)
+    ids = ids[np.sort(first)]
+    chunk = 4096
+    for c0 in range(0, ids.shape[0], chunk):
+        idx = torch.as_tensor(ids[c0:c0 + chunk].astype(np.int64), device=device)
+        n = int(idx.shape[0])
+        key_cache[idx] = _randn(gen, (n, BS, Hkv, D), dt, device)
+        value_cache[idx] = _randn(gen, (n, BS, Hkv, D), dt, device)
+    # history ends at ctx - q_len: poison every row from there to the end of the table
+    kv_int = (key_cache.view(_INT_VIEW[dt]), value_cache.view(_INT_VIEW[dt]))
+    for i in range(B):
+        hist = int(ctx[i]) - int(ql[i])
+        nblk = -(-int(ctx[i]) // BS)
+        for j in range(hist // BS, nblk):
+            b = int(block_tables[i, j])
+            r0 = max(0, hist - j * BS)
+            for t in kv_int:
+                t[b, r0:].fill_(poison_bits(dt))
+    return DecodeBatch(spec=spec, context_lens=ctx, block_tables=block_tables.astype(np.int32),
+                       query=query, key=key, value=value, key_cache=key_cache,
+                       value_cache=value_cache, scale=1.0 / math.sqrt(D),
+                       extra={"query_lens": ql, "query_start_loc": qsl})
+
+
+# Multi-token workloads on the Llama-3-8B layer shape (GQA 32/8, D = 128, bf16, block
+# size 16):
+#  - spec_verify: 256 sequences with lognormal contexts (as llama3_8b), each verifying
+#    5 speculated tokens (the draft length on the pages);
+#  - chunked_prefill: a 2048-token step budget (the pages' default) spent on 4
+#    prompts' 512-token chunks, after histories uniform in [0, 8192].
+MULTI_CONFIGS = {
+    "tiny_multi": (ConfigSpec("tiny_multi", 4, 4, 4, 64, 16, 64, "f32", 100,
+                              ("fixed", (17, 33, 64, 100)), 5), ("fixed", (1, 5, 16, 40))),
+    "spec_verify": (replace(CONFIGS["llama3_8b"], name="spec_verify", seed=6),
+                    ("fixed_all", 5)),
+    "chunked_prefill": (ConfigSpec("chunked_prefill", 4, 32, 8, 128, 16, 16384, "bf16",
+                                   8192 + 512, ("uniform", 512, 8192 + 512), 7,
+                                   partition_size=0), ("fixed_all", 512)),
+}
+
+
+def make_multi_config(name: str, device="cpu", seed: Optional[int] = None) -> DecodeBatch:
+    spec, qdist = MULTI_CONFIGS[name]
+    ctx = draw_context_lens(spec, seed)
+    if qdist[0] == "fixed":
+        ql = np.asarray(qdist[1], dtype=np.int32)
+    else:
+        ql = np.full(ctx.shape, qdist[1], dtype=np.int32)
+    ctx = np.maximum(ctx, ql)        # a sequence holds at least its new tokens
+    tables = deal_block_tables(spec, ctx, seed)
+    return build_multi_batch(spec, ctx, ql, device=device, seed=seed, block_tables=tables)
+
+
+# -----------------------------------------------------------------------------------
 # E4M3 (FP8) caches
 # -----------------------------------------------------------------------------------
 # The history rows hold codes drawn uniformly from the 254 finite E4M3 codes (every
