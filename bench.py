@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 # Sources the partition kernel is built from: stored traffic counters are used only
 # while these are unchanged.
 KERNEL_SOURCES = ("paged_attention.hip", "paged_attention_stream.hip", "pkv_device.hpp",
-                  "pkv_launch.hpp", "pkv_plan.hpp", "pkv_tile.hpp")
+                  "pkv_launch.hpp", "pkv_plan.hpp", "pkv_tile.hpp", "pkv_stream.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
 
 

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum {
   PKV_OK = 0,
@@ -269,6 +269,74 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
                                              float scale, float k_scale, float v_scale,
                                              pkv_dtype out_dtype, void* workspace,
                                              size_t workspace_bytes, void* stream);
+
+/*
+ * ---- Steps with several new tokens per sequence -------------------------------------
+ *
+ * Chunked prefill and the verification of speculated tokens hand each sequence a
+ * number of new tokens in one step.  (Page "读一个真实 serving 系统 · vLLM 架构巡礼",
+ * section 3: the scheduler has no separate prefill and decode phases, every request
+ * just gets new tokens; page "vLLM PagedAttention 原理与源码深度解析", sections 8.1 and
+ * 8.2: a long prompt is cut into chunks, a draft model proposes 5 tokens for the main
+ * model to verify; page "vllm源码剖析", section 一.3: the requests' tokens are packed
+ * into one flat batch with a start and a length each.)  The pages print no kernel for
+ * this step; the reading here:
+ *
+ *   query_start_loc  device int32 [num_seqs + 1]: sequence i owns the new tokens
+ *                    query_start_loc[i] .. query_start_loc[i+1] - 1 of the flat batch
+ *                    (non-decreasing from 0 to num_tokens);
+ *   context_lens     device int32 [num_seqs]: every token of sequence i after the step,
+ *                    its new ones included, so new token j sits at position
+ *                    p = context_lens[i] - q_len_i + j;
+ *   new token j attends to positions 0 .. p of its sequence (causal within the step):
+ *     out[t][h] = sum_{u <= p} softmax_u(scale * <q_{t,h}, k_u>) v_u,
+ *   with kv head h / (num_heads / num_kv_heads).  One new token per sequence is a
+ *   decode step.
+ *
+ * pkv_slot_mapping_multi_query -- slot_mapping[t] (device int32 [num_tokens]) of every
+ * new token: block_tables[i][p / block_size] * block_size + p % block_size, or -1 for a
+ * sequence whose new tokens do not fit (q_len > context_len, a context past its table,
+ * a range outside the flat batch) or a block id outside [0, num_blocks).  The rows
+ * are then stored with pkv_kv_cache_write(key, value, ..., slot_mapping, num_tokens,
+ * ...), key/value being [num_tokens][num_kv_heads][head_dim].
+ *
+ * pkv_paged_attention_multi_query -- out [num_tokens][num_heads][head_dim] (out_dtype)
+ * from query [num_tokens][num_heads][head_dim] (kv_dtype) over the paged caches, the
+ * new tokens' rows already written.  Accumulation fp32; scores and probabilities fp32
+ * throughout (no reduced-precision P).  Supported: kv_dtype PKV_F32 or PKV_BF16,
+ * head_dim 64 or 128, block_size 16 or 32, num_heads / num_kv_heads in {1, 2, 4, 8},
+ * num_tokens * num_heads * head_dim * sizeof(kv_dtype) below 2^31.  Workspace:
+ * pkv_paged_attention_multi_query_workspace_bytes() bytes, no initialisation needed.
+ * With U = ceil(num_tokens / (16 / G)) + num_seqs (G = num_heads / num_kv_heads) it
+ * holds a 256-byte header, the unit plan (U + 1, U and num_seqs + 1 int32, each
+ * rounded up to 256 bytes) and (1024 + U) * num_kv_heads * 16 records of
+ * (head_dim + 2) fp32.  Device-side contract: rows of a sequence that does not fit
+ * (as for the slot mapping), or that lists a block id outside [0, num_blocks) within
+ * its context, are NaN; a query_start_loc that is not a non-decreasing cut of the
+ * flat batch may make every row NaN; nothing outside the listed blocks and the flat
+ * batch is read.  num_tokens == 0 is a no-op.
+ */
+pkv_status pkv_slot_mapping_multi_query(const int32_t* block_tables, const int32_t* context_lens,
+                                        const int32_t* query_start_loc, int32_t* slot_mapping,
+                                        int32_t num_seqs, int32_t num_tokens,
+                                        int32_t max_blocks_per_seq, int32_t block_size,
+                                        int64_t num_blocks, void* stream);
+
+size_t pkv_paged_attention_multi_query_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                                       int32_t num_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t block_size,
+                                                       int32_t max_blocks_per_seq);
+
+pkv_status pkv_paged_attention_multi_query(void* out, const void* query, const void* key_cache,
+                                           const void* value_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens,
+                                           const int32_t* query_start_loc, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int64_t num_blocks, float scale, pkv_dtype kv_dtype,
+                                           pkv_dtype out_dtype, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /*
  * pkv_decode_prologue -- the steps of a decode step that come before attention,

@@ -15,12 +15,15 @@ from .ops import (  # noqa: F401
     decode_step,
     kv_cache_write,
     kv_cache_write_fp8,
+    multi_query_workspace_bytes,
     paged_attention_decode,
     paged_attention_decode_fp8,
     paged_attention_partition,
+    paged_attention_multi_query,
     paged_attention_partition_fp8,
     paged_attention_plan,
     paged_attention_reduce,
     slot_mapping,
+    slot_mapping_multi_query,
     workspace_bytes,
 )

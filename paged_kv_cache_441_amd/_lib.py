@@ -42,6 +42,12 @@ SIGNATURES = {
     "pkv_paged_attention_partition_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                                  _i32, _i32, _i32, _i64, _f32, _f32, _f32, _i32,
                                                  _vp, _sz, _vp]),
+    "pkv_slot_mapping_multi_query": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
+    "pkv_paged_attention_multi_query_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                             _i32]),
+    "pkv_paged_attention_multi_query": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
+                                               _vp, _sz, _vp]),
     "pkv_decode_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i64, _i32, _i32, _vp, _sz, _vp]),
     "pkv_block_pool_create": (_i32, [_i32, _vp]),
@@ -65,7 +71,7 @@ SIGNATURES = {
                                           _sz, _vp]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lock = threading.Lock()
 _lib = None

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["pkv_api.cpp", "block_pool.cpp", "cache_write.hip", "paged_attention.hip", "paged_attention_stream.hip"]
+SOURCES = ["pkv_api.cpp", "block_pool.cpp", "cache_write.hip", "paged_attention.hip", "paged_attention_stream.hip",
+           "paged_attention_multi.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -1,0 +1,664 @@
+// Paged attention for steps that hand each sequence several new tokens: a chunk of a
+// long prompt, or the tokens a draft model proposed, to be verified.
+//
+// What is computed (page "读一个真实 serving 系统 · vLLM 架构巡礼", section 3: one
+// scheduler for all steps, each request getting some new tokens; page "vLLM
+// PagedAttention 原理与源码深度解析", sections 8.1 and 8.2, chunked prefill and
+// speculative decoding; page "vllm源码剖析", section 一.3, the requests packed into one
+// flat token batch with a start and a length each): sequence i's new tokens are
+// query_start_loc[i] .. query_start_loc[i+1] - 1 of the flat batch; context_lens[i]
+// counts them, so new token j sits at position p = ctx - q_len + j, and it attends
+// to positions 0 .. p of its sequence.  A step with one new token per sequence is a
+// decode step.
+//
+// Work split.  Rows are (new token, query head) pairs; the rows of one sequence and
+// kv head are cut into units of kMqRows = 16 (16 / G consecutive new tokens with the
+// G query heads of the kv head each), so a unit is exactly one MFMA operand.  A unit
+// reads the tiles of its sequence up to its last token's position.  As in the
+// balanced decode split, all (unit, tile) pairs form one list, each unit preceded
+// by kSeqCost positions, and a one-round grid takes equal shares of it; the run of
+// one unit inside a share is a segment, written directly when it is the whole unit
+// and as records under the label w + unit otherwise, merged afterwards in share order.
+//
+// Per tile (16 tokens of the HW kv heads of the workgroup, staged whole through LDS
+// with direct-to-LDS copies as in the decode stream kernel):
+//  - S^T = K . Q^T on the matrix cores: the key tile is the A operand and the unit's
+//    16 query rows the B operand, so lane (row n, quarter q) receives row n's scores
+//    for tokens 4q .. 4q + 3.  Those four values are already the lane's part of the
+//    P operand of P.V, so no transpose through LDS is needed.
+//  - causal mask (token t visible to a row at position p when t <= p), online
+//    softmax per row in the base-2 domain with the lazy rebase of the decode kernel;
+//    row maxima and sums across the four lanes of a row by lane shuffles.
+//  - P.V on fp32 matrix instructions (v_mfma_f32_16x16x4_f32, P kept in fp32): k-step
+//    s takes token 4q + s from each lane quarter q, and each lane reads 8 (D / 16)
+//    consecutive value columns of that token row in one LDS read, one column per
+//    output block, so the value tile needs no transpose either (the output columns
+//    of block e are e, e + D/16, ... permuted back at the store).
+#include "pkv_device.hpp"
+#include "pkv_launch.hpp"
+#include "pkv_stream.hpp"
+#include "pkv_tile.hpp"
+
+namespace pkv {
+
+// ---- slot mapping of every new token ---------------------------------------------
+
+// Sequence owning flat token t: the last i with query_start_loc[i] <= t (binary search
+// over num_seqs + 1 entries; the caller checks the answer).
+__device__ __forceinline__ int owner_of(const int32_t* __restrict__ qsl, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;   // qsl[lo] <= t is assumed for lo = 0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Whether sequence i is a well-formed part of the step: its tokens lie inside the
+// flat batch, there is at least one, and its context holds them and fits its table.
+__device__ __forceinline__ bool seq_valid(int q0, int q1, int ctx, int num_tokens, int max_ctx) {
+  return q0 >= 0 && q1 > q0 && q1 <= num_tokens && ctx >= q1 - q0 && ctx <= max_ctx;
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_multi_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ qsl, int32_t* __restrict__ slot_mapping, int num_seqs,
+    int num_tokens, int max_blocks_per_seq, int block_shift, int64_t num_blocks) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  const int i = owner_of(qsl, num_seqs, t);
+  const int q0 = qsl[i], q1 = qsl[i + 1], ctx = context_lens[i];
+  int32_t slot = -1;
+  if (seq_valid(q0, q1, ctx, num_tokens, max_blocks_per_seq << block_shift) && t >= q0 &&
+      t < q1) {
+    const int pos = ctx - (q1 - q0) + (t - q0);
+    const int32_t phys = block_tables[(int64_t)i * max_blocks_per_seq + (pos >> block_shift)];
+    if (phys >= 0 && (int64_t)phys < num_blocks)
+      slot = (phys << block_shift) + (pos & ((1 << block_shift) - 1));
+  }
+  slot_mapping[t] = slot;
+}
+
+hipError_t launch_slot_mapping_multi(const int32_t* block_tables, const int32_t* context_lens,
+                                     const int32_t* query_start_loc, int32_t* slot_mapping,
+                                     int num_seqs, int num_tokens, int max_blocks_per_seq,
+                                     int block_shift, int64_t num_blocks, hipStream_t stream) {
+  const int grid = (num_tokens + 255) / 256;
+  hipLaunchKernelGGL(slot_mapping_multi_kernel, dim3(grid), dim3(256), 0, stream, block_tables,
+                     context_lens, query_start_loc, slot_mapping, num_seqs, num_tokens,
+                     max_blocks_per_seq, block_shift, num_blocks);
+  return hipGetLastError();
+}
+
+// ---- the unit plan ---------------------------------------------------------------
+// hdr[0]: positions of the list; hdr[1]: workgroups per kv-head group (written by the
+// attention kernel); hdr[2]: units.  seq_unit[i]: first unit of sequence i (units of
+// invalid sequences: none); unit_seq[u]: the sequence of unit u; cum[u]: positions
+// before unit u.  If the units would exceed the workspace (possible only when
+// query_start_loc is not a non-decreasing cut of the flat batch), the plan has none
+// and every output row is NaN.
+
+constexpr int kMqPlanThreads = 1024;
+
+size_t multi_plan_bytes(int64_t num_seqs, int64_t max_units) {
+  auto r256 = [](int64_t b) { return (size_t)((b + 255) / 256 * 256); };
+  return 256 + r256((max_units + 1) * 4) + r256(max_units * 4) + r256((num_seqs + 1) * 4);
+}
+
+// Exclusive prefix sum over the workgroup of x(k) for k < n into out[k]; returns the
+// total.  NT threads; every thread calls it.
+template <int NT, typename F>
+__device__ int block_scan(int n, F x_of, int* __restrict__ out) {
+  __shared__ int part[NT / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int carry = 0;
+  for (int c0 = 0; c0 < n; c0 += NT) {
+    const int k = c0 + threadIdx.x;
+    const int x = k < n ? x_of(k) : 0;
+    int inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int v = 0; v < NT / kWave; ++v) {
+      const int t = part[v];
+      before += v < wave ? t : 0;
+      total += t;
+    }
+    if (k < n) out[k] = carry + before + inc - x;
+    carry += total;
+    __syncthreads();
+  }
+  return carry;
+}
+
+__global__ __launch_bounds__(kMqPlanThreads) void multi_plan_kernel(AttentionArgs a) {
+  const int B = a.num_seqs;
+  const int G = a.num_heads / a.num_kv_heads;
+  const int tpb = kMqRows / G;   // new tokens per unit
+  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+  const int32_t* qsl = a.query_start_loc;
+  auto units_of = [&](int i) {
+    const int q0 = qsl[i], q1 = qsl[i + 1];
+    return seq_valid(q0, q1, a.context_lens[i], a.num_tokens, max_ctx) ? (q1 - q0 + tpb - 1) / tpb
+                                                                       : 0;
+  };
+  int U = block_scan<kMqPlanThreads>(B, units_of, a.seq_unit);
+  const bool fits = U <= a.max_units;
+  if (!fits) U = 0;
+  if (threadIdx.x == 0) a.seq_unit[B] = U;
+  __syncthreads();
+  if (!fits) {
+    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) a.seq_unit[i] = 0;
+  } else {
+    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) {
+      const int n = units_of(i), u0 = a.seq_unit[i];
+      for (int k = 0; k < n; ++k) a.unit_seq[u0 + k] = i;
+    }
+  }
+  __syncthreads();
+  // positions of unit u: the tiles up to its last token's position, plus kSeqCost
+  auto positions_of = [&](int u) {
+    const int i = a.unit_seq[u];
+    const int q0 = qsl[i], qlen = qsl[i + 1] - q0;
+    const int j_end = min(qlen, (u - a.seq_unit[i] + 1) * tpb);
+    const int last = a.context_lens[i] - qlen + j_end;   // positions 0 .. last - 1
+    return (last + kTileTokens - 1) / kTileTokens + kSeqCost;
+  };
+  const int total = block_scan<kMqPlanThreads>(U, positions_of, a.tile_cum);
+  if (threadIdx.x == 0) {
+    a.tile_cum[U] = total;
+    a.tile_hdr[0] = total;
+    a.tile_hdr[2] = U;
+  }
+}
+
+hipError_t launch_multi_plan(const AttentionArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(multi_plan_kernel, dim3(1), dim3(kMqPlanThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---- the attention kernel ----------------------------------------------------------
+
+template <typename T, int D, int G, int HW>
+__global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(AttentionArgs a) {
+  constexpr int TOK = kTileTokens;
+  constexpr int NBUF = 2;
+  using St = Stage<T, D, HW, TOK>;
+  constexpr int EB = T::kElemBytes;
+  constexpr int NCH = D * EB / 16;          // 16-byte chunks of a head's row
+  constexpr int QKC = D * EB / 64;          // key / query chunks per lane = MFMAs per tile
+  constexpr int TPB = kMqRows / G;          // new tokens per unit
+  constexpr int CPL = D / 16;               // value columns per lane per k-step
+  constexpr int L = 2 * St::kCopies;        // tile copies per wave per step
+  constexpr int QROW = D * EB;              // bytes of one query row
+  constexpr int QNI = kMqRows * QROW / 1024;  // query copies per wave per unit
+  constexpr int NS = St::kTileSlots;
+  static_assert(TOK == 16, "tile rows");
+  static_assert(kMqRows * QROW % 1024 == 0, "query rows in 1 KiB wave copies");
+
+  __shared__ uint4 kb0[NS], vb0[NS], kb1[NS], vb1[NS];
+  __shared__ uint4 q_lds[HW][kMqRows * QROW / 16];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwg = gridDim.x;
+  const int w = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int Hkv = a.num_kv_heads;
+  const int H = Hkv * G;
+  const int g = hg * HW + wave;             // this wave's kv head
+
+  cint32* cum = (cint32*)a.tile_cum;
+  cint32* ctx_of = (cint32*)a.context_lens;
+  cint32* tables = (cint32*)a.block_tables;
+  cint32* qsl = (cint32*)a.query_start_loc;
+  cint32* unit_seq = (cint32*)a.unit_seq;
+  cint32* seq_unit = (cint32*)a.seq_unit;
+  const int total = ((cint32*)a.tile_hdr)[0];
+  const int U = ((cint32*)a.tile_hdr)[2];
+  if (w == 0 && hg == 0 && threadIdx.x == 0) a.tile_hdr[1] = nwg;
+  const int64_t start = (int64_t)w * total / nwg;
+  const int64_t end = (int64_t)(w + 1) * total / nwg;
+  if (start >= end) return;
+
+  // the unit holding position `start` (64-way search over cum[0 .. U])
+  int lo = 0, len = U + 1;
+  while (len > 1) {
+    const int step = (len + kWave - 1) / kWave;
+    const int i = lo + lane * step;
+    const bool ok = i < lo + len && a.tile_cum[i] <= start;
+    const int k = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
+    const int nlo = lo + (k - 1) * step;
+    len = min(step, lo + len - nlo);
+    lo = nlo;
+  }
+  const int unit0 = lo;
+
+  const int quarter = lane >> 4;
+  const int col = lane & 15;                // MFMA row of the key tile / column of Q^T
+
+  const int64_t row_stride = (int64_t)Hkv * D * EB;
+  uint32_t copy_off[St::kCopies];
+#pragma unroll
+  for (int i = 0; i < St::kCopies; ++i) {
+    const int s = (i * HW + wave) * kWave + lane;
+    const int r = s / St::kSlots;
+    const int p = s % St::kSlots;
+    copy_off[i] = (uint32_t)(r * row_stride) + (uint32_t)((p ^ St::swz(r)) * 16);
+  }
+  const char* kcache = static_cast<const char*>(a.key_cache) + (int64_t)hg * St::kRowBytes;
+  const char* vcache = static_cast<const char*>(a.value_cache) + (int64_t)hg * St::kRowBytes;
+  const int shift = a.block_shift;
+  const int bs_mask = (1 << shift) - 1;
+  const int MB = a.max_blocks_per_seq;
+  const int max_ctx = MB << shift;
+  const int num_blocks = (int)a.num_blocks;
+  const float kNegInf = -__builtin_inff();
+
+  struct Cursor {
+    int u, t, nt, stop;
+  };
+  // Moves a cursor to the next unit that starts in this share, or invalidates it
+  // (every unit has at least one tile).  Cursors are values, kept wave-uniform.
+  auto next_unit = [&](Cursor c) -> Cursor {
+    const int u = uniform(c.u) + 1;
+    const int cs = uniform(cum[u]);
+    c.u = u;
+    c.t = 0;
+    if (u >= U || cs + kSeqCost >= end) {
+      c.nt = c.stop = 0;
+      return c;
+    }
+    c.nt = uniform(cum[u + 1] - cs - kSeqCost);
+    c.stop = uniform(min(c.nt, (int)(end - cs - kSeqCost)));
+    return c;
+  };
+  auto first_cursor = [&]() -> Cursor {
+    const int cs = cum[unit0];
+    Cursor c;
+    c.u = unit0;
+    c.nt = uniform(cum[unit0 + 1] - cs - kSeqCost);
+    c.t = uniform(max(0, (int)(start - cs - kSeqCost)));
+    c.stop = uniform(min(c.nt, (int)(end - cs - kSeqCost)));
+    if (c.t >= c.stop) c = next_unit(c);
+    return c;
+  };
+
+  // ---- issue side ----
+  Cursor ic = first_cursor();
+  unsigned bad_pipe = 0;
+  auto issue = [&](uint4* kb, uint4* vb) {
+    int64_t base = 0;
+    bad_pipe <<= 1;
+    if (ic.t < ic.stop) {
+      const int tok0 = uniform(ic.t * TOK);
+      const int seq = uniform(unit_seq[uniform(ic.u)]);
+      const int32_t blk =
+          uniform(tok0 < max_ctx ? tables[(int64_t)seq * MB + (tok0 >> shift)] : -1);
+      if (blk >= 0 && blk < num_blocks)
+        base = (((int64_t)blk << shift) + (tok0 & bs_mask)) * row_stride;
+      else
+        bad_pipe |= 1u;
+      if (++ic.t == ic.stop) ic = next_unit(ic);
+    }
+    const uint32_t kd = lds_addr(kb) + wave * 1024;
+    const uint32_t vd = lds_addr(vb) + wave * 1024;
+    const char* kbase = kcache + base;
+    const char* vbase = vcache + base;
+#pragma unroll
+    for (int i = 0; i < St::kCopies; ++i) dma16(kbase, copy_off[i], kd + i * HW * 1024);
+#pragma unroll
+    for (int i = 0; i < St::kCopies; ++i) dma16(vbase, copy_off[i], vd + i * HW * 1024);
+  };
+
+  // ---- compute side ----
+  Cursor cc = first_cursor();
+  if (cc.t >= cc.stop) return;
+
+  // the unit under the compute cursor
+  int useq = 0, uq0 = 0, uqlen = 0, uctx = 0, uj0 = 0;
+  auto unit_info = [&]() {
+    useq = uniform(unit_seq[cc.u]);
+    uq0 = uniform(qsl[useq]);
+    uqlen = uniform(qsl[useq + 1] - uq0);
+    uctx = uniform(ctx_of[useq]);
+    uj0 = uniform((cc.u - seq_unit[useq]) * TPB);
+  };
+  bool seg_from_zero = cc.t == 0;
+  int seg_bad = 0;
+
+  // The unit's 16 query rows: row r is new token j0 + r / G (repeated from the
+  // unit's first token past the sequence's last, never stored) with query head
+  // g * G + r % G.  Copied into q_lds like the tiles, read at the unit's first tile.
+  uint4 qa[QKC];
+  bool q_fresh = false;
+  auto load_query = [&]() {
+    q_fresh = true;
+    const char* base = static_cast<const char*>(a.query);
+#pragma unroll
+    for (int i = 0; i < QNI; ++i) {
+      const int b = i * 1024 + lane * 16;
+      const int r = b / QROW;
+      const int jq = uj0 + r / G < uqlen ? uj0 + r / G : uj0;
+      const uint32_t off =
+          (uint32_t)(((int64_t)(uq0 + jq) * H + g * G + r % G) * QROW + b % QROW);
+      dma16(base, off, lds_addr(q_lds[wave]) + i * 1024);
+    }
+  };
+  auto read_query = [&]() {
+    const uint4* q = q_lds[wave] + col * NCH;
+#pragma unroll
+    for (int c = 0; c < QKC; ++c) qa[c] = q[4 * c + quarter];
+  };
+
+  // row col of the unit (this lane's score row): its position, and whether it exists
+  float m_run;          // running maximum of the lane's row (base-2 domain)
+  float l_lane;         // the lane's share of the row's sum
+  floatx4 acc[CPL];     // output rows 4 * quarter + j, columns col * CPL + e of block e
+  auto reset = [&]() {
+    m_run = kNegInf;
+    l_lane = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    seg_bad = 0;
+  };
+
+  auto compute = [&](const uint4* kb, const uint4* vb, bool bad) {
+    constexpr float kRebase = 8.f;
+    const int tok0 = cc.t * TOK;
+    seg_bad |= bad;
+    uint4 kk[QKC];
+#pragma unroll
+    for (int c = 0; c < QKC; ++c)
+      kk[c] = kb[col * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ St::swz(col))];
+    const floatx4 s4 = tile_scores<T, QKC>(kk, qa);   // S^T: row col, tokens 4q + j
+    const int jrow = min(uj0 + col / G, uqlen - 1);
+    const int prow = uctx - uqlen + jrow;              // last position row col sees
+    float sc[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tok0 + 4 * quarter + j;
+      sc[j] = t <= prow ? s4[j] * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, sc[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > m_run + kRebase;
+    if (__ballot(up)) {
+      const float alpha = up ? fast_exp2(m_run - mx) : 1.f;   // 0 when m_run is -inf
+      m_run = up ? mx : m_run;
+      l_lane *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * quarter + j);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[e][j] *= aj;
+      }
+    }
+    const float mref = m_run == kNegInf ? 0.f : m_run;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(sc[j] - mref);   // 0 for masked tokens
+      l_lane += p[j];
+    }
+    // P.V: k-step s takes token 4q + s of lane quarter q
+    const bool full = tok0 + TOK <= uctx;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int vr = 4 * quarter + s;
+      float v[CPL];
+      if constexpr (CPL * EB == 16) {
+        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + col) ^ St::swz(vr))], v);
+      } else if constexpr (CPL * EB == 32) {
+        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + 2 * col) ^ St::swz(vr))], v);
+        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + 2 * col + 1) ^ St::swz(vr))],
+                        v + CPL / 2);
+      } else {
+        static_assert(CPL * EB == 8, "value piece");
+        const int slot = (wave * NCH + (col >> 1)) ^ St::swz(vr);
+        const uint2 c8 = reinterpret_cast<const uint2*>(vb)[2 * (vr * St::kSlots + slot) + (col & 1)];
+        v[0] = bf16_lo(c8.x); v[1] = bf16_hi(c8.x);
+        v[2] = bf16_lo(c8.y); v[3] = bf16_hi(c8.y);
+      }
+      if (!full && tok0 + vr >= uctx) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[s], v[e], acc[e], 0, 0, 0);
+    }
+  };
+
+  // End of a segment: sums across the four lanes of each row, normalise, store rows
+  // 4 * quarter + j (output or record).
+  auto finish = [&](bool whole) {
+    float l_row = l_lane + __shfl_xor(l_lane, 16);
+    l_row += __shfl_xor(l_row, 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * quarter + j;
+      const float lr = __shfl(l_row, r);
+      const float mr = __shfl(m_run, r);
+      const int jq = uj0 + r / G;
+      if (jq >= uqlen) continue;
+      const float inv = seg_bad ? __builtin_nanf("") : (lr > 0.f ? 1.f / lr : 0.f);
+      float o[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) o[e] = acc[e][j] * inv;
+      if (whole) {
+        const int64_t orow = ((int64_t)(uq0 + jq) * H + g * G + r % G) * D + col * CPL;
+        if (a.out_bf16) {
+          uint16_t* dst = static_cast<uint16_t*>(a.out) + orow;
+#pragma unroll
+          for (int e = 0; e < CPL; e += 4) {
+            uint2 v;
+            v.x = f32_to_bf16_rne(o[e]) | (uint32_t)f32_to_bf16_rne(o[e + 1]) << 16;
+            v.y = f32_to_bf16_rne(o[e + 2]) | (uint32_t)f32_to_bf16_rne(o[e + 3]) << 16;
+            *reinterpret_cast<uint2*>(dst + e) = v;
+          }
+        } else {
+          float* dst = static_cast<float*>(a.out) + orow;
+#pragma unroll
+          for (int e = 0; e < CPL; e += 4)
+            *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+        }
+      } else {
+        const int64_t rec = (((int64_t)w + cc.u) * Hkv + g) * kMqRows + r;
+        float* dst = a.ws_o + rec * D + col * CPL;
+#pragma unroll
+        for (int e = 0; e < CPL; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+        if (col == 0) {
+          a.ws_m[rec] = mr;
+          a.ws_l[rec] = seg_bad ? __builtin_nanf("") : lr;
+        }
+      }
+    }
+  };
+
+  reset();
+  unit_info();
+  load_query();
+
+#define PKV_MULTI_STEP(KB, VB, KF, VF)                                    \
+  if (cc.t >= cc.stop) break;                                             \
+  issue(KF, VF);                                                          \
+  wait_copies<(NBUF - 1) * L>();                                          \
+  bare_barrier();                                                         \
+  if (q_fresh) {                                                          \
+    read_query();                                                         \
+    q_fresh = false;                                                      \
+  }                                                                       \
+  compute(KB, VB, (bad_pipe >> (NBUF - 1)) & 1u);                         \
+  bare_barrier();                                                         \
+  if (cc.t == cc.stop - 1) {                                              \
+    finish(seg_from_zero && cc.stop == cc.nt);                            \
+    reset();                                                              \
+    cc = next_unit(cc);                                                   \
+    seg_from_zero = true;                                                 \
+    if (cc.t < cc.stop) {                                                 \
+      unit_info();                                                        \
+      load_query();                                                       \
+    }                                                                     \
+  } else {                                                                \
+    ++cc.t;                                                               \
+  }
+
+  issue(kb0, vb0);
+  for (;;) {
+    PKV_MULTI_STEP(kb0, vb0, kb1, vb1)
+    PKV_MULTI_STEP(kb1, vb1, kb0, vb0)
+  }
+#undef PKV_MULTI_STEP
+  wait_copies<0>();
+}
+
+// ---- merge of the segments ----------------------------------------------------------
+// One wave per (new token, query head) row; lanes hold D / 16 output columns each
+// (4 for D = 64), read as float4.  Rows of invalid sequences get NaN.
+template <int D>
+__global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(AttentionArgs a) {
+  constexpr int LPR = D / 4;             // lanes per record (float4 each)
+  constexpr int KGW = kWave / LPR;       // records per wave round
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int H = a.num_heads;
+  if (row >= (int64_t)a.num_tokens * H) return;
+  const int t = (int)(row / H);
+  const int h = (int)(row % H);
+  const int Hkv = a.num_kv_heads;
+  const int G = H / Hkv;
+  const int tpb = kMqRows / G;
+  const int kg = lane / LPR;
+  const int lr = lane % LPR;
+  const int B = a.num_seqs;
+  const int i = owner_of(a.query_start_loc, B, t);
+  const int q0 = a.query_start_loc[i], q1 = a.query_start_loc[i + 1];
+  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+  const bool valid = a.tile_hdr[2] > 0 && t >= q0 && t < q1 &&
+                     seq_valid(q0, q1, a.context_lens[i], a.num_tokens, max_ctx);
+  if (!valid) {
+    if (kg == 0) {
+      const float nan = __builtin_nanf("");
+      store_row4(a, row * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
+    }
+    return;
+  }
+  const int jq = t - q0;
+  const int u = a.seq_unit[i] + jq / tpb;
+  const int r = (jq % tpb) * G + h % G;
+  const int g = h / G;
+  const int c0 = a.tile_cum[u], c1 = a.tile_cum[u + 1];
+  const int total = a.tile_hdr[0];
+  const int nwg = a.tile_hdr[1];
+  const int w0 = share_of((int64_t)c0 + kSeqCost, nwg, total);
+  const int w1 = share_of((int64_t)c1 - 1, nwg, total);
+  if (w0 == w1) return;                  // written by the attention kernel
+  // Records of segments in which this row saw no token have l = 0 (and m = -inf);
+  // they weigh nothing.
+  Running acc{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int ww = w0 + kg; ww <= w1; ww += KGW) {
+    if (!share_nonempty(ww, nwg, total)) continue;
+    const int64_t rec = (((int64_t)ww + u) * Hkv + g) * kMqRows + r;
+    const float l = a.ws_l[rec];
+    if (!(l > 0.f) && !(l != l)) continue;   // empty segment (NaN l: keep, marks bad data)
+    Running s{a.ws_m[rec], l, reinterpret_cast<const float4*>(a.ws_o + rec * D)[lr]};
+    s.o.x *= l; s.o.y *= l; s.o.z *= l; s.o.w *= l;
+    merge_into(acc, s);
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    Running s;
+    s.m = __shfl_xor(acc.m, off);
+    s.l = __shfl_xor(acc.l, off);
+    s.o.x = __shfl_xor(acc.o.x, off);
+    s.o.y = __shfl_xor(acc.o.y, off);
+    s.o.z = __shfl_xor(acc.o.z, off);
+    s.o.w = __shfl_xor(acc.o.w, off);
+    if (lane & off) { const Running tmp = acc; acc = s; s = tmp; }
+    merge_into(acc, s);
+  }
+  if (kg == 0) store_row4(a, row * D + lr * 4, acc);
+}
+
+hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_heads * a.num_tokens;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(paged_attention_multi_reduce_kernel<64>, grid, dim3(256), 0, stream, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL(paged_attention_multi_reduce_kernel<128>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---- dispatch ------------------------------------------------------------------
+
+template <typename T, int D, int G, int HW>
+static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream) {
+  auto kernel = paged_attention_multi_kernel<T, D, G, HW>;
+  static const int per_cu = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, HW * kWave, 0) != hipSuccess)
+      n = 1;
+    return n > 0 ? n : 1;
+  }();
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int hgroups = a.num_kv_heads / HW;
+  const int nwg = max(1, min(kMaxStreamWgs, per_cu * cus / hgroups));
+  hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(HW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+#ifndef PKV_MULTI_MAX_ROW
+#define PKV_MULTI_MAX_ROW 1024
+#endif
+
+// Heads per workgroup: the largest of 8, 4, 2, 1 dividing the kv heads with a token
+// row of the group within PKV_MULTI_MAX_ROW bytes and at least 128 bytes.
+template <typename T, int D, int G>
+static hipError_t launch_multi_hw(const AttentionArgs& a, hipStream_t stream) {
+  constexpr int kRow = D * T::kElemBytes;
+  if constexpr (8 * kRow <= PKV_MULTI_MAX_ROW)
+    if (a.num_kv_heads % 8 == 0) return launch_multi_shape<T, D, G, 8>(a, stream);
+  if constexpr (4 * kRow <= PKV_MULTI_MAX_ROW)
+    if (a.num_kv_heads % 4 == 0) return launch_multi_shape<T, D, G, 4>(a, stream);
+  if constexpr (2 * kRow <= PKV_MULTI_MAX_ROW)
+    if (a.num_kv_heads % 2 == 0) return launch_multi_shape<T, D, G, 2>(a, stream);
+  return launch_multi_shape<T, D, G, 1>(a, stream);
+}
+
+template <typename T, int D>
+static hipError_t launch_multi_g(const AttentionArgs& a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_multi_hw<T, D, 1>(a, stream);
+    case 2: return launch_multi_hw<T, D, 2>(a, stream);
+    case 4: return launch_multi_hw<T, D, 4>(a, stream);
+    case 8: return launch_multi_hw<T, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention_multi(const AttentionArgs& a, hipStream_t stream) {
+  if (a.kv_bf16) {
+    if (a.head_dim == 64) return launch_multi_g<BF16, 64>(a, stream);
+    if (a.head_dim == 128) return launch_multi_g<BF16, 128>(a, stream);
+  } else {
+    if (a.head_dim == 64) return launch_multi_g<F32, 64>(a, stream);
+    if (a.head_dim == 128) return launch_multi_g<F32, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

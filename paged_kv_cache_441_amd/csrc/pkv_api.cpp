@@ -484,3 +484,158 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, const void* query, const vo
 }
 
 }  // extern "C"
+
+// ---- multi-token steps ----------------------------------------------------------------
+
+namespace {
+
+struct MultiShape {
+  int64_t max_units = 0;
+  int64_t recs = 0;
+  size_t plan_bytes = 0;
+  size_t ws_bytes = 0;
+};
+
+pkv_status check_multi_shape(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, MultiShape* m) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_heads % num_kv_heads != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
+  int64_t max_ctx = 0;
+  if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX / 2, &max_ctx)) return PKV_ERR_INVALID_ARG;
+  const int G = num_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PKV_ERR_UNSUPPORTED;
+  const int64_t tpb = pkv::kMqRows / G;
+  m->max_units = (int64_t{num_tokens} + tpb - 1) / tpb + num_seqs;
+  // list positions are int32: units x (tiles of the longest context + 1)
+  int64_t pos = 0;
+  if (!mul_ok(m->max_units, (max_ctx + pkv::kTileTokens - 1) / pkv::kTileTokens + pkv::kSeqCost,
+              INT32_MAX / 2, &pos))
+    return PKV_ERR_UNSUPPORTED;
+  if (!mul_ok(m->max_units + pkv::kMaxStreamWgs, int64_t{num_kv_heads} * pkv::kMqRows,
+              INT64_MAX / 1024, &m->recs))
+    return PKV_ERR_INVALID_ARG;
+  m->plan_bytes = pkv::multi_plan_bytes(num_seqs, m->max_units);
+  int64_t bytes = 0;
+  if (!mul_ok(m->recs, int64_t{head_dim} + 2, INT64_MAX / 8, &bytes)) return PKV_ERR_INVALID_ARG;
+  m->ws_bytes = m->plan_bytes + static_cast<size_t>(bytes) * 4;
+  return PKV_OK;
+}
+
+void set_multi_workspace(pkv::AttentionArgs* a, void* workspace, const MultiShape& m,
+                         int32_t num_seqs) {
+  auto r256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+  char* ws = static_cast<char*>(workspace);
+  a->tile_hdr = reinterpret_cast<int*>(ws);
+  a->tile_cum = reinterpret_cast<int*>(ws + 256);
+  a->unit_seq = reinterpret_cast<int*>(ws + 256 + r256((m.max_units + 1) * 4));
+  a->seq_unit = reinterpret_cast<int*>(ws + 256 + r256((m.max_units + 1) * 4) +
+                                        r256(m.max_units * 4));
+  a->max_units = static_cast<int>(m.max_units);
+  float* f = reinterpret_cast<float*>(ws + m.plan_bytes);
+  a->ws_m = f;
+  a->ws_l = f + m.recs;
+  a->ws_o = f + 2 * m.recs;
+  (void)num_seqs;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_slot_mapping_multi_query(const int32_t* block_tables, const int32_t* context_lens,
+                                        const int32_t* query_start_loc, int32_t* slot_mapping,
+                                        int32_t num_seqs, int32_t num_tokens,
+                                        int32_t max_blocks_per_seq, int32_t block_size,
+                                        int64_t num_blocks, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
+  int64_t t = 0;
+  if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX / 2, &t) ||
+      !mul_ok(num_blocks, block_size, INT32_MAX, &t))
+    return PKV_ERR_INVALID_ARG;   // slots are int32
+  if (num_tokens == 0) return PKV_OK;
+  if (num_seqs == 0) return PKV_ERR_INVALID_ARG;   // tokens need a sequence
+  if (!block_tables || !context_lens || !query_start_loc || !slot_mapping)
+    return PKV_ERR_INVALID_ARG;
+  return hip_status(pkv::launch_slot_mapping_multi(
+      block_tables, context_lens, query_start_loc, slot_mapping, num_seqs, num_tokens,
+      max_blocks_per_seq, log2_exact(block_size), num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_paged_attention_multi_query_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                                       int32_t num_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t block_size,
+                                                       int32_t max_blocks_per_seq) {
+  MultiShape m;
+  if (check_multi_shape(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, &m) != PKV_OK)
+    return 0;
+  return m.ws_bytes;
+}
+
+pkv_status pkv_paged_attention_multi_query(void* out, const void* query, const void* key_cache,
+                                           const void* value_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens,
+                                           const int32_t* query_start_loc, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int64_t num_blocks, float scale, pkv_dtype kv_dtype,
+                                           pkv_dtype out_dtype, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  MultiShape m;
+  pkv_status st = check_multi_shape(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
+                                    block_size, max_blocks_per_seq, &m);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(kv_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_INVALID_ARG;
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  int64_t pool = 0, rows = 0;
+  if (!mul_ok(num_blocks, block_size, INT64_MAX / 4096, &pool) ||
+      !mul_ok(pool, int64_t{num_kv_heads} * head_dim, INT64_MAX / 8, &pool))
+    return PKV_ERR_INVALID_ARG;
+  // query and output offsets are 32-bit in the kernels
+  if (!mul_ok(num_tokens, int64_t{num_heads} * head_dim * elem_bytes(kv_dtype), INT32_MAX, &rows))
+    return PKV_ERR_UNSUPPORTED;
+  if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
+  if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (num_seqs == 0) return PKV_ERR_INVALID_ARG;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !query_start_loc)
+    return PKV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < m.ws_bytes) return PKV_ERR_WORKSPACE;
+  pkv::AttentionArgs a{};
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_shift = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.kv_bf16 = kv_dtype == PKV_BF16;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.v_scale = 1.f;
+  set_multi_workspace(&a, workspace, m, num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_multi_plan(a, s));
+  if (st != PKV_OK) return st;
+  st = hip_status(pkv::launch_attention_multi(a, s));
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_attention_multi_reduce(a, s));
+}
+
+}  // extern "C"

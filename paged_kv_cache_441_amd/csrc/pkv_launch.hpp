@@ -67,7 +67,17 @@ struct AttentionArgs {
   bool balanced;
   int* tile_hdr;            // [0] total tiles, [1] workgroups per kv-head group
   int* tile_cum;            // [num_seqs + 1] tiles before each sequence
+  // Multi-token steps: the flat token batch and the units of the work list (a unit is
+  // one sequence's block of kMqRows (new token, query head) rows of one kv head).
+  const int32_t* query_start_loc;   // [num_seqs + 1]
+  int num_tokens;
+  int max_units;            // capacity of the unit arrays
+  int* unit_seq;            // [max_units] sequence of each unit
+  int* seq_unit;            // [num_seqs + 1] first unit of each sequence
 };
+
+// Multi-token steps: query rows per unit (one MFMA operand of (token, head) rows).
+constexpr int kMqRows = 16;
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels
 // (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.
@@ -99,5 +109,17 @@ hipError_t launch_tile_plan(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_stream_reduce(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_reduce(const AttentionArgs& a, hipStream_t stream);
+
+// Multi-token steps (several new tokens per sequence, causal within the step).
+hipError_t launch_slot_mapping_multi(const int32_t* block_tables, const int32_t* context_lens,
+                                     const int32_t* query_start_loc, int32_t* slot_mapping,
+                                     int num_seqs, int num_tokens, int max_blocks_per_seq,
+                                     int block_shift, int64_t num_blocks, hipStream_t stream);
+// Workspace of a multi-token step: plan header (256 B), then the unit plan arrays,
+// each rounded up to 256 bytes; the records follow.
+size_t multi_plan_bytes(int64_t num_seqs, int64_t max_units);
+hipError_t launch_multi_plan(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_attention_multi(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -1,0 +1,93 @@
+// Pieces shared by the streaming attention kernels of libpagedkv (decode and
+// multi-token steps): direct-to-LDS tile copies with explicit waits, the LDS image of
+// a tile, and the equal shares of a work list.
+#pragma once
+
+#include <atomic>
+
+#include "pkv_device.hpp"
+#include "pkv_launch.hpp"
+
+namespace pkv {
+
+// Reads through the constant address space become scalar loads when the address is
+// wave-uniform; used for data no kernel of this launch writes (tables, lengths, the
+// tile plan), so their waits do not hold up the tile copies in flight.
+typedef const int32_t __attribute__((address_space(4))) cint32;
+
+// A workgroup barrier with no memory fence: the fence of __syncthreads would wait
+// for every outstanding copy, including the ones meant to stay in flight.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One direct-to-LDS copy: lane i's 16 bytes at base + off (base wave-uniform) land at
+// LDS byte lds + 16 i.  Written as assembly so that the compiler, which cannot tell
+// the ring's buffers apart once more than a few copies are in flight, adds no wait
+// for it before LDS reads; the kernel waits for the copies itself (s_waitcnt vmcnt)
+// before the barrier that hands a tile to the readers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// Waits until at most N of this wave's copies are outstanding; copies retire in
+// order, so every copy issued before the last N has landed in LDS.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <typename T, int D, int HW, int TOK>
+struct Stage {
+  static constexpr int kRowBytes = HW * D * T::kElemBytes;   // one token row of the HW heads
+  static constexpr int kSlots = kRowBytes / 16;               // 16-byte slots per row
+  static constexpr int kSwz = kSlots >= 16 ? 15 : kSlots - 1;
+  // The XOR pattern of row r.  E4M3 rows are read as 8-byte value pieces, 16 lanes
+  // per row and two rows (r, r ^ 1) per 32-lane half of a read: their patterns differ
+  // in the top bit, so the two rows' 128 bytes land in different bank halves.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (T::kElemBytes == 1)
+      return ((r & 1) ? (kSwz + 1) >> 1 : 0) | ((r & kSwz) >> 1);
+    else
+      return r & kSwz;
+  }
+  static constexpr int kTileBytes = TOK * kRowBytes;          // per cache
+  static constexpr int kTileSlots = kTileBytes / 16;
+  static constexpr int kCopies = kTileBytes / (HW * 1024);    // 1 KiB wave copies per cache
+  static_assert(kTileBytes % (HW * 1024) == 0, "a tile splits into 1 KiB wave copies");
+  static_assert(kSlots >= 8, "rows of at least 128 bytes");
+};
+
+// Share w of the tile list is [floor(w * total / nwg), floor((w + 1) * total / nwg)).
+// The share holding tile j:
+__device__ __forceinline__ int share_of(int64_t j, int nwg, int total) {
+  return (int)(((j + 1) * nwg - 1) / total);
+}
+
+// Shares are empty when there are more workgroups than tiles.
+__device__ __forceinline__ bool share_nonempty(int w, int nwg, int total) {
+  return (int64_t)w * total / nwg < (int64_t)(w + 1) * total / nwg;
+}
+
+// Compute units of the current device, looked up once per device.
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace pkv

@@ -267,6 +267,82 @@ def decode_step(query, key, value, key_cache, value_cache, block_tables, context
                                   workspace=workspace)
 
 
+# ---- steps with several new tokens per sequence ---------------------------------------
+
+def slot_mapping_multi_query(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             query_start_loc: torch.Tensor, num_tokens: int, block_size: int,
+                             num_blocks: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Slot of every new token of the flat batch (-1 where the sequence does not fit)."""
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _i32(t, n)
+    B = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start_loc.shape != (B + 1,):
+        raise ValueError("block_tables [B, MB], context_lens [B], query_start_loc [B + 1]")
+    if out is None:
+        out = torch.empty(int(num_tokens), dtype=torch.int32, device=context_lens.device)
+    _i32(out, "out")
+    _same_device(block_tables, context_lens, query_start_loc, out)
+    lib = _lib.load_library()
+    st = lib.pkv_slot_mapping_multi_query(_ptr(block_tables), _ptr(context_lens),
+                                          _ptr(query_start_loc), _ptr(out), B, int(num_tokens),
+                                          block_tables.shape[1], int(block_size), int(num_blocks),
+                                          _stream(out))
+    _lib.check(st, "pkv_slot_mapping_multi_query")
+    return out
+
+
+def multi_query_workspace_bytes(num_seqs: int, num_tokens: int, num_heads: int,
+                                num_kv_heads: int, head_dim: int, block_size: int,
+                                max_blocks_per_seq: int) -> int:
+    return int(_lib.load_library().pkv_paged_attention_multi_query_workspace_bytes(
+        num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+
+
+def paged_attention_multi_query(query: torch.Tensor, key_cache: torch.Tensor,
+                                value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                                scale: float, out: Optional[torch.Tensor] = None,
+                                out_dtype: torch.dtype = torch.float32,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention of every new token of the flat batch over its sequence's paged
+    context (the new tokens' rows already written)."""
+    dt = _kv(query, "query")
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        if _kv(t, n) != dt:
+            raise TypeError(f"{n} dtype differs from query")
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _i32(t, n)
+    if query.dim() != 3 or key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("query [T, H, D]; caches [NB, BS, Hkv, D]")
+    T, H, D = query.shape
+    NB, BS, Hkv, Dk = key_cache.shape
+    B = context_lens.shape[0]
+    if Dk != D or block_tables.dim() != 2 or block_tables.shape[0] != B or \
+            query_start_loc.shape != (B + 1,):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=out_dtype, device=query.device)
+    if out.dtype not in _KV_DTYPES or out.shape != (T, H, D):
+        raise ValueError("out must be float32/bfloat16 [T, H, D]")
+    _dev(out, "out")
+    if workspace is None:
+        n = multi_query_workspace_bytes(B, T, H, Hkv, D, BS, block_tables.shape[1])
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=query.device)
+    _dev(workspace, "workspace")
+    _same_device(query, key_cache, value_cache, block_tables, context_lens, query_start_loc, out,
+                 workspace)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_multi_query(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start_loc), B, T, H, Hkv, D, BS, block_tables.shape[1], NB,
+        float(scale), dt, _KV_DTYPES[out.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _lib.check(st, "pkv_paged_attention_multi_query")
+    return out
+
+
 # ---- E4M3 (FP8) caches ---------------------------------------------------------------
 
 def _fp8_caches(key_cache, value_cache):
