@@ -1,0 +1,166 @@
+"""Prefix caching on the block pool: pins for the CPU oracle (each against something
+other than itself), the library's C++ pool against the oracle, and an end-to-end GPU
+decode over blocks shared through the cache."""
+
+import random
+
+import numpy as np
+import pytest
+
+from oracle import prefix_cache as opc
+from oracle.block_pool import PoolExhausted
+
+
+# --------------------------------------------------------------------------------
+# H1: the hash
+# --------------------------------------------------------------------------------
+
+def test_fnv1a64_published_vectors():
+    # test vectors published with the FNV hash definition
+    assert opc.fnv1a64(b"") == 0xCBF29CE484222325
+    assert opc.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert opc.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_block_hash_is_fnv_of_parent_then_tokens():
+    # the byte string of H1, written out: parent (8 bytes LE) then int32 tokens LE
+    data = (0x0123456789ABCDEF).to_bytes(8, "little") + b"".join(
+        (t & 0xFFFFFFFF).to_bytes(4, "little") for t in (7, -1, 65536))
+    assert opc.block_hash(0x0123456789ABCDEF, [7, -1, 65536]) == opc.fnv1a64(data)
+
+
+def test_chain_property():
+    rng = np.random.default_rng(0)
+    toks = rng.integers(0, 32000, 64).tolist()
+    h = opc.chain_hashes(toks, 16)
+    assert len(h) == 4 and len(set(h)) == 4
+    assert opc.chain_hashes(toks[:40], 16) == h[:2]          # partial block not hashed
+    changed = list(toks)
+    changed[20] += 1                                          # a token of block 1
+    h2 = opc.chain_hashes(changed, 16)
+    assert h2[0] == h[0] and all(a != b for a, b in zip(h2[1:], h[1:]))
+    # the same block content after a different prefix hashes differently
+    other = rng.integers(0, 32000, 16).tolist() + toks[16:32]
+    assert opc.chain_hashes(other, 16)[1] != h[1]
+
+
+# --------------------------------------------------------------------------------
+# H2-H5: a worked scenario, derived by hand
+# --------------------------------------------------------------------------------
+
+def test_worked_scenario():
+    BS = 4
+    p = opc.PrefixCachingPool(8)
+    A = list(range(1, 11))                       # 10 tokens: 2 full blocks + 2 tokens
+    assert p.match_prefix(A, BS) == []
+    ta = [p.allocate() for _ in range(3)]        # FIFO: 0, 1, 2
+    assert ta == [0, 1, 2]
+    assert p.register(A, ta, BS) == 2            # blocks 0 and 1 enter the map
+    B = list(range(1, 9)) + [20, 21, 22, 23, 24]
+    hits = p.match_prefix(B, BS)                 # the shared 8-token prompt
+    assert hits == [0, 1] and p.ref[0] == 2 and p.ref[1] == 2
+    tb = hits + [p.allocate(), p.allocate()]     # 3, 4
+    assert tb == [0, 1, 3, 4]
+    assert p.register(B, tb, BS) == 1            # block 3 (tokens 20..23)
+    p.release_table(ta)
+    assert list(p.free) == [5, 6, 7, 2]
+    p.release_table(tb)
+    assert list(p.free) == [5, 6, 7, 2, 0, 1, 3, 4]
+    assert len(p.cached) == 3                    # free blocks keep their hashes
+    C = list(A)
+    assert p.match_prefix(C, BS) == [0, 1]       # hit on free blocks: they leave the list
+    assert list(p.free) == [5, 6, 7, 2, 3, 4] and p.ref[0] == 1
+    got = [p.allocate() for _ in range(5)]
+    assert got == [5, 6, 7, 2, 3]                # block 3 is handed out: its hash goes
+    assert len(p.cached) == 2
+    assert p.match_prefix(B, BS) == [0, 1]       # B's third block is no longer cached
+    with pytest.raises(PoolExhausted):
+        for _ in range(3):
+            p.allocate()
+
+
+def test_collisions_never_share_a_block():
+    BS = 4
+    p = opc.PrefixCachingPool(8, hash_fn=lambda parent, toks: 42)   # every hash collides
+    A = list(range(1, 9))
+    ta = [p.allocate(), p.allocate()]
+    assert p.register(A, ta, BS) == 1            # the second block's hash is taken
+    assert p.match_prefix([9, 9, 9, 9, 5, 6, 7, 8], BS) == []   # same hash, other tokens
+    assert p.match_prefix(A, BS) == [ta[0]]      # block 1's parent hash differs
+
+
+def _check_invariants(p, live):
+    held = {}
+    for tbl in live.values():
+        for b in tbl["table"]:
+            held[b] = held.get(b, 0) + 1
+    for b in range(p.num_blocks):
+        assert p.ref[b] == held.get(b, 0)
+    assert len(set(p.free)) == len(p.free)
+    assert set(p.free) == {b for b in range(p.num_blocks) if p.ref[b] == 0}
+    for h, b in p.cached.items():
+        assert p.meta[b][0] == h
+    for tbl in live.values():
+        toks = tbl["tokens"]
+        for j, b in enumerate(tbl["table"][:len(toks) // tbl["bs"]]):
+            if b in p.meta:
+                blk = tuple(toks[j * tbl["bs"]:(j + 1) * tbl["bs"]])
+                assert p.meta[b][2] == blk, "a cached block holds other tokens"
+
+
+def _random_ops(pool_factory, seed, steps=300):
+    """Requests drawn from a few shared system prompts plus random suffixes; each
+    either arrives (match, allocate the rest, register) or leaves."""
+    rng = random.Random(seed)
+    BS = 4
+    prompts = [[rng.randrange(50) for _ in range(rng.choice([4, 8, 12, 13]))] for _ in range(4)]
+    p = pool_factory(64)
+    live, trace, nid = {}, [], 0
+    for _ in range(steps):
+        if live and (rng.random() < 0.4 or p.num_free_blocks() < 8):
+            rid = rng.choice(sorted(live))
+            p.release_table(live.pop(rid)["table"])
+            trace.append(("free", rid))
+        else:
+            toks = rng.choice(prompts) + [rng.randrange(50) for _ in range(rng.randrange(0, 9))]
+            hits = p.match_prefix(toks, BS)
+            need = -(-len(toks) // BS) - len(hits)
+            table = hits + [p.allocate() for _ in range(need)]
+            n = p.register(toks, table, BS)
+            live[nid] = {"table": table, "tokens": toks, "bs": BS}
+            trace.append(("new", nid, tuple(hits), tuple(table), n))
+            nid += 1
+        yield p, live, trace
+
+
+class _Oracle(opc.PrefixCachingPool):
+    def num_free_blocks(self):
+        return len(self.free)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_invariants_under_random_operations(seed):
+    for p, live, _ in _random_ops(_Oracle, seed):
+        _check_invariants(p, live)
+
+
+def test_planted_touch_mistake_breaks_the_invariants(monkeypatch):
+    def touch_without_unlinking(self, tokens, block_size):
+        hits = []
+        parent = 0
+        for j in range(len(tokens) // block_size):
+            blk = tuple(tokens[j * block_size:(j + 1) * block_size])
+            h = self.hash_fn(parent, blk)
+            b = self.cached.get(h)
+            if b is None or self.meta[b][2] != blk:
+                break
+            hits.append(b)
+            parent = h
+        for b in hits:
+            self.ref[b] += 1                 # forgets to take free blocks off the list
+        return hits
+
+    monkeypatch.setattr(_Oracle, "match_prefix", touch_without_unlinking)
+    with pytest.raises(AssertionError):
+        for seed in range(4):
+            test_invariants_under_random_operations(seed)
