@@ -13,6 +13,8 @@ sequences (tokens) per second.
 
 A config named *_fp8 runs the same workload over E4M3 (8-bit float) caches: the
 prologue quantises the new rows, attention decodes the codes (balanced split only).
+The configs spec_verify and chunked_prefill run steps with several new tokens per
+sequence (slot mapping, cache write, causal multi-token attention).
 
 Prints one JSON line.  The fp64 CPU oracle is timed on the same batch (all of it
 unless --cpu-sample-seqs says otherwise), on one host thread, repeated for about
@@ -131,6 +133,9 @@ def main(argv=None) -> int:
         return 2
     if args.component == "copy_blocks":
         return bench_copy_blocks(args)
+    from workloads import MULTI_CONFIGS
+    if args.config in MULTI_CONFIGS:
+        return bench_multi(args)
 
     import torch
     import paged_kv_cache_441_amd as pkv
@@ -320,6 +325,150 @@ def bench_copy_blocks(args) -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
     }), flush=True)
     return 0
+
+
+FP32_MATRIX_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
+
+
+def bench_multi(args) -> int:
+    """Steps with several new tokens per sequence: slot mapping, cache write, causal
+    multi-token attention (plan, attention kernel and merge in one library call)."""
+    import torch
+    import paged_kv_cache_441_amd as pkv
+    from workloads import make_multi_config
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    b = make_multi_config(args.config, device=dev)
+    spec = b.spec
+    B, H, Hkv, D, BS, NB = (b.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim,
+                            spec.block_size, spec.num_blocks)
+    qsl_np = b.extra["query_start_loc"]
+    T = int(qsl_np[-1])
+    bt = torch.as_tensor(b.block_tables, device=dev)
+    cl = torch.as_tensor(b.context_lens, device=dev)
+    qsl = torch.as_tensor(qsl_np, device=dev)
+    kc, vc = b.key_cache, b.value_cache
+    out = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    slots = torch.empty(T, dtype=torch.int32, device=dev)
+    ws = torch.empty(pkv.multi_query_workspace_bytes(B, T, H, Hkv, D, BS, bt.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkv.slot_mapping_multi_query(bt, cl, qsl, T, BS, NB, out=slots)
+        pkv.kv_cache_write(b.key, b.value, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_attention_multi_query(b.query, kc, vc, bt, cl, qsl, b.scale, out=out,
+                                        workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_attn = np.array([e[1].elapsed_time(e[2]) for e in events])
+    attn_s = float(t_attn.mean()) / 1e3
+    elem = {"bf16": 2, "f32": 4}[spec.kv_dtype]
+    ctx = b.context_lens.astype(np.int64)
+    ql = b.extra["query_lens"].astype(np.int64)
+    kv_bytes = int(ctx.sum()) * Hkv * D * 2 * elem
+    # causal: new token j of sequence i sees ctx - q_len + j + 1 positions
+    seen = sum(int((c - q) * q + q * (q + 1) // 2) for c, q in zip(ctx, ql))
+    flops = 4 * H * D * seen               # Q.K^T and P.V, 2 flops per product each
+    pv_flops = flops // 2
+    gbs = kv_bytes / attn_s / 1e9
+    tflops = flops / attn_s / 1e12
+    pv_tflops = pv_flops / attn_s / 1e12
+    hbm_bound = args.config != "chunked_prefill"
+    # The matrix-bound case is priced on its P.V contraction: fp32 operands (P is kept
+    # in fp32) on fp32 matrix instructions, whose peak is 1/16 of bf16's; Q.K^T runs in
+    # bf16 and needs 1/16 of that time at peak.
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)} if hbm_bound else
+            {"bound": "mfma", "achieved": round(pv_tflops, 2), "peak": FP32_MATRIX_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(pv_tflops / FP32_MATRIX_PEAK_TFLOPS, 4),
+             "contraction": "P.V (fp32 x fp32 -> fp32); Q.K^T (bf16) not counted"})
+    roof.update({"kernel": "paged_attention_multi_query (plan + attention + merge)",
+                 "traffic": None})
+    result = {
+        "metric": "multi-token step: KV GB/s, TFLOP/s and new tokens/s, 1 GPU",
+        "value": round(gbs, 1) if hbm_bound else round(tflops, 2),
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.kv_dtype, "data": "synthetic",
+        "config": {"workload": args.config, "num_seqs": B, "num_new_tokens": T,
+                   "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": BS,
+                   "context_sum": int(ctx.sum()), "query_lens": sorted(set(ql.tolist())),
+                   "kv_dtype": spec.kv_dtype, "accumulate": "f32"},
+        "kv_bytes_per_step": kv_bytes, "causal_flops_per_step": flops,
+        "kv_gbs": round(gbs, 1), "tflops": round(tflops, 2), "pv_tflops": round(pv_tflops, 2),
+        "new_tokens_per_s": round(T / (ms_step / 1e3), 1),
+        "kernel_ms": {"slot mapping + cache write": round(float(t_write.mean()), 5),
+                      "attention (plan + kernel + merge)": round(float(t_attn.mean()), 5)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_baseline_multi(b, out)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline_multi(b, gpu_out, min_seconds=10.0):
+    """The oracle, untuned, on one host thread, over whole sequences of the batch taken
+    in order until about ``min_seconds`` of CPU work; rate in new tokens per second."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import multi_query as omq
+
+    qsl = b.extra["query_start_loc"]
+    done, secs, tokens, err = [], 0.0, 0, 0.0
+    with threadpool_limits(limits=1):
+        for i in range(b.num_seqs):
+            if secs >= min_seconds:
+                break
+            bt = b.block_tables[[i]]
+            ids = np.unique(bt[bt >= 0])
+            idx = torch.as_tensor(ids.astype(np.int64), device=b.key_cache.device)
+            kc = b.numpy_storage(b.key_cache.index_select(0, idx))
+            vc = b.numpy_storage(b.value_cache.index_select(0, idx))
+            cbt = np.where(bt >= 0, np.searchsorted(ids, np.maximum(bt, 0)), -1).astype(np.int32)
+            q0, q1 = int(qsl[i]), int(qsl[i + 1])
+            t0 = time.perf_counter()
+            _, _, _, ref = omq.multi_query_step(
+                b.numpy_storage(b.query)[q0:q1], b.numpy_storage(b.key)[q0:q1],
+                b.numpy_storage(b.value)[q0:q1], kc, vc, cbt, b.context_lens[[i]],
+                np.array([0, q1 - q0]), b.scale, b.kv_dtype)
+            secs += time.perf_counter() - t0
+            tokens += q1 - q0
+            done.append(i)
+            g = gpu_out[q0:q1].float().cpu().numpy().astype(np.float64)
+            err = max(err, float(np.abs(g - ref).max()))
+    base = {"value": round(tokens / secs, 2), "unit": "new tokens/s", "cores": 1,
+            "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(secs, 2),
+            "sample": f"the first {len(done)} of {b.num_seqs} sequences ({tokens} new tokens): "
+                      "slot mapping, cache write and fp64 causal attention for all heads, one "
+                      "host thread"}
+    parity = {"tokens": tokens, "max_abs_err_vs_oracle": err, "tolerance": 2e-3,
+              "ok": bool(err <= 2e-3)}
+    return base, parity
 
 
 def cpu_baseline(b, gpu_out, n_sample, min_seconds=10.0, max_reps=20):

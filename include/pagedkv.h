@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 typedef enum {
   PKV_OK = 0,
@@ -195,6 +195,48 @@ pkv_status pkv_block_pool_append_slots(pkv_block_pool* pool, int32_t* tables,
                                        const int32_t* num_tokens, int32_t num_seqs,
                                        int32_t block_size, int32_t* slots, int32_t* copies,
                                        int32_t* num_copies, int32_t* done);
+
+/*
+ * ---- Prefix caching on the pool (host) ---------------------------------------------
+ *
+ * Full blocks of a sequence can be entered into a hash-to-block map and reused by
+ * later requests that start with the same tokens.  (Page "vllm源码剖析", the BlockPool
+ * paragraphs: a logical block's hash is computed from its token content and its
+ * predecessor's hash, cached_block_hash_to_block maps it to the block, a hit only
+ * raises the block's count, and a block whose count reaches 0 rejoins the free queue
+ * with its hash, which is cleared when the block is handed out again; page "读一个真实
+ * serving 系统 · vLLM 架构巡礼", section 2: _block_hash and touch().)  Choices the pages
+ * leave open: the hash is 64-bit FNV-1a over the parent hash (8 bytes, little-endian,
+ * 0 for the first block) followed by the block's token ids (int32, 4 bytes each,
+ * little-endian); a hit also compares the stored tokens and parent hash, so a hash
+ * collision never shares a block.  Token arrays are host int32 arrays owned by the
+ * caller; only full blocks (num_tokens / block_size of them) take part.  The first
+ * call fixes the pool's block size; a later call with another one is INVALID_ARG.
+ *
+ * pkv_prefix_block_hashes       hashes[j] (host uint64) of every full block j.
+ * pkv_block_pool_match_prefix   the longest run of leading full blocks found in the
+ *                               map (at most max_blocks), written to blocks (host
+ *                               int32); each gets one more reference and, if it was
+ *                               free, leaves the free list.
+ * pkv_block_pool_register_prefix  enters the full blocks of a sequence whose K/V are
+ *                               stored in table[0 .. num_tokens / block_size) (blocks
+ *                               in use); a block already cached, or a hash already
+ *                               mapped to another block, is left as it is.
+ *                               INVALID_ARG, nothing changed, for a block not in use.
+ * pkv_block_pool_num_cached     hashes in the map (-1 for a null pool).
+ * pkv_block_pool_allocate (and append_slots) take the front of the free list as
+ * before; a cached block taken there leaves the map.
+ */
+pkv_status pkv_prefix_block_hashes(const int32_t* tokens, int32_t num_tokens,
+                                   int32_t block_size, uint64_t* hashes);
+int32_t pkv_block_pool_num_cached(const pkv_block_pool* pool);
+pkv_status pkv_block_pool_match_prefix(pkv_block_pool* pool, const int32_t* tokens,
+                                       int32_t num_tokens, int32_t block_size,
+                                       int32_t* blocks, int32_t max_blocks, int32_t* num_hit);
+pkv_status pkv_block_pool_register_prefix(pkv_block_pool* pool, const int32_t* tokens,
+                                          int32_t num_tokens, int32_t block_size,
+                                          const int32_t* table, int32_t table_len,
+                                          int32_t* num_registered);
 
 pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                            int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,

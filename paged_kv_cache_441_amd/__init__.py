@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     paged_attention_multi_query,
     paged_attention_partition_fp8,
     paged_attention_plan,
+    prefix_block_hashes,
     paged_attention_reduce,
     slot_mapping,
     slot_mapping_multi_query,

@@ -59,6 +59,10 @@ SIGNATURES = {
     "pkv_block_pool_fork": (_i32, [_vp, _vp, _i32]),
     "pkv_block_pool_append_slots": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
                                            _vp]),
+    "pkv_prefix_block_hashes": (_i32, [_vp, _i32, _i32, _vp]),
+    "pkv_block_pool_num_cached": (_i32, [_vp]),
+    "pkv_block_pool_match_prefix": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _vp]),
+    "pkv_block_pool_register_prefix": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -71,7 +75,7 @@ SIGNATURES = {
                                           _sz, _vp]),
 }
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lock = threading.Lock()
 _lib = None

@@ -487,6 +487,16 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
     _lib.check(st, "pkv_copy_blocks")
 
 
+def prefix_block_hashes(tokens, block_size: int) -> np.ndarray:
+    """Chained hashes (uint64) of the full blocks of a token sequence."""
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    out = np.zeros(t.shape[0] // int(block_size), np.uint64)
+    _lib.check(_lib.load_library().pkv_prefix_block_hashes(
+        t.ctypes.data_as(ctypes.c_void_p), t.shape[0], int(block_size),
+        out.ctypes.data_as(ctypes.c_void_p)), "pkv_prefix_block_hashes")
+    return out
+
+
 class BlockPool:
     """The library's host block pool (free list and reference counts of the physical
     blocks).  Block tables are numpy int32 arrays [num_seqs, capacity] with their
@@ -537,6 +547,32 @@ class BlockPool:
     def fork(self, blocks) -> None:
         a, p = self._ids(blocks)
         _lib.check(self._lib.pkv_block_pool_fork(self._h, p, a.shape[0]), "pkv_block_pool_fork")
+
+    # ---- prefix caching ----
+    @property
+    def num_cached(self) -> int:
+        return self._lib.pkv_block_pool_num_cached(self._h)
+
+    def match_prefix(self, tokens, block_size: int) -> list:
+        """Reused leading full blocks of ``tokens`` (their counts raised)."""
+        t, p = self._ids(tokens)
+        out = np.empty(max(1, t.shape[0] // int(block_size)), np.int32)
+        n = ctypes.c_int32()
+        _lib.check(self._lib.pkv_block_pool_match_prefix(
+            self._h, p, t.shape[0], int(block_size), out.ctypes.data_as(ctypes.c_void_p),
+            t.shape[0] // int(block_size), ctypes.byref(n)), "pkv_block_pool_match_prefix")
+        return out[:n.value].tolist()
+
+    def register_prefix(self, tokens, table, block_size: int) -> int:
+        """Enter the full blocks of a sequence (K/V stored in ``table``) into the map;
+        returns how many entered."""
+        t, p = self._ids(tokens)
+        tb, tp = self._ids(table)
+        n = ctypes.c_int32()
+        _lib.check(self._lib.pkv_block_pool_register_prefix(
+            self._h, p, t.shape[0], int(block_size), tp, tb.shape[0], ctypes.byref(n)),
+            "pkv_block_pool_register_prefix")
+        return n.value
 
     def append_slots(self, tables: np.ndarray, table_lens: np.ndarray, num_tokens,
                      block_size: int):
