@@ -87,9 +87,11 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle runs on (0: the whole batch)")
-    ap.add_argument("--component", default="decode", choices=["decode", "copy_blocks"],
+    ap.add_argument("--component", default="decode",
+                    choices=["decode", "copy_blocks", "prefix_cache"],
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
-                         "block copy kernel alone")
+                         "block copy kernel alone; prefix_cache: the host pool's prefix "
+                         "caching (lookup, allocation, registration, release)")
     ap.add_argument("--copy-pairs", type=int, default=4096,
                     help="block pairs per copy_blocks launch")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -133,6 +135,8 @@ def main(argv=None) -> int:
         return 2
     if args.component == "copy_blocks":
         return bench_copy_blocks(args)
+    if args.component == "prefix_cache":
+        return bench_prefix_cache(args)
     from workloads import MULTI_CONFIGS
     if args.config in MULTI_CONFIGS:
         return bench_multi(args)
@@ -275,6 +279,88 @@ def main(argv=None) -> int:
         result["cpu_baseline"], result["parity"] = cpu_baseline(b, out, args.cpu_sample_seqs)
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def _prefix_requests(n, seed=11):
+    """Synthetic arrivals: 64 system prompts of 512 tokens (popularity falling as 1/k)
+    plus unique suffixes of 16..512 tokens, vocabulary 32000."""
+    rng = np.random.default_rng(seed)
+    systems = rng.integers(0, 32000, (64, 512)).astype(np.int32)
+    w = 1.0 / np.arange(1, 65)
+    pick = rng.choice(64, size=n, p=w / w.sum())
+    lens = rng.integers(16, 513, n)
+    return [np.concatenate([systems[k], rng.integers(0, 32000, m).astype(np.int32)])
+            for k, m in zip(pick, lens)]
+
+
+def bench_prefix_cache(args) -> int:
+    """The host pool with prefix caching, on the Llama-3-8B-shaped pool (200,000 blocks of
+    16 tokens): each request looks up its prompt, allocates the rest, registers its
+    full blocks; 256 requests are live at a time (the oldest leaves).  No GPU work."""
+    import paged_kv_cache_441_amd as pkv
+    from collections import deque
+
+    BS, NB, LIVE = 16, 200_000, 256
+    reqs = _prefix_requests(max(args.steps, 1) * 100)
+    pool = pkv.BlockPool(NB)
+    live = deque()
+    hits = blocks = 0
+
+    def run(rs):
+        nonlocal hits, blocks
+        for toks in rs:
+            h = pool.match_prefix(toks, BS)
+            need = -(-len(toks) // BS) - len(h)
+            table = h + [pool.allocate() for _ in range(need)]
+            pool.register_prefix(toks, table, BS)
+            hits += len(h)
+            blocks += len(table)
+            live.append(table)
+            if len(live) > LIVE:
+                pool.release(live.popleft())
+
+    w = min(len(reqs) // 10, 500)
+    run(reqs[:w])
+    hits = blocks = 0
+    t0 = time.perf_counter()
+    run(reqs[w:])
+    dt = time.perf_counter() - t0
+    n = len(reqs) - w
+    tokens = int(sum(len(t) for t in reqs[w:]))
+    # the oracle, untuned, on the first requests of the same stream (about 10 s)
+    from oracle import prefix_cache as opc
+    ora = opc.PrefixCachingPool(NB)
+    olive = deque()
+    t1, m = time.perf_counter(), 0
+    for toks in reqs:
+        if time.perf_counter() - t1 > 10.0:
+            break
+        tl = toks.tolist()
+        h = ora.match_prefix(tl, BS)
+        table = h + [ora.allocate() for _ in range(-(-len(tl) // BS) - len(h))]
+        ora.register(tl, table, BS)
+        olive.append(table)
+        if len(olive) > LIVE:
+            ora.release_table(olive.popleft())
+        m += 1
+    odt = time.perf_counter() - t1
+    print(json.dumps({
+        "metric": "prefix-cache requests/s on the host pool (lookup, allocate, register, "
+                  "release)",
+        "value": round(n / dt, 1), "unit": "requests/s", "n_gpus": 0, "steps": n,
+        "warmup": w, "ms_per_step": round(dt * 1e3 / n, 5), "higher_is_better": True,
+        "dtype": "int32 tokens, uint64 hashes", "data": "synthetic",
+        "config": {"workload": "prefix_cache", "block_size": BS, "num_blocks": NB,
+                   "live_requests": LIVE, "system_prompts": 64, "system_prompt_tokens": 512,
+                   "suffix_tokens": [16, 512]},
+        "tokens_per_s": round(tokens / dt, 1), "hit_blocks_fraction": round(hits / blocks, 4),
+        "roofline": None,
+        "roofline_note": "host C++ called per request through the ctypes binding; no GPU kernel",
+        "cpu_baseline": {"value": round(m / odt, 1), "unit": "requests/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"the first {m} requests of the same stream, one thread"},
+    }), flush=True)
     return 0
 
 
