@@ -414,6 +414,7 @@ def bench_copy_blocks(args) -> int:
 
 
 FP32_MATRIX_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
+BF16_MATRIX_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
 def bench_multi(args) -> int:
@@ -482,14 +483,16 @@ def bench_multi(args) -> int:
     tflops = flops / attn_s / 1e12
     pv_tflops = pv_flops / attn_s / 1e12
     hbm_bound = args.config != "chunked_prefill"
-    # The matrix-bound case is priced on its P.V contraction: fp32 operands (P is kept
-    # in fp32) on fp32 matrix instructions, whose peak is 1/16 of bf16's; Q.K^T runs in
-    # bf16 and needs 1/16 of that time at peak.
+    # The matrix-bound case is priced on the algorithmic causal flops (Q.K^T and P.V)
+    # against the dense peak of the operand type: bf16 caches run both products on bf16
+    # matrix instructions (P.V as two products, P split into bf16 hi + lo parts, not
+    # counted twice), fp32 caches on fp32 ones.
+    mpeak = BF16_MATRIX_PEAK_TFLOPS if spec.kv_dtype == "bf16" else FP32_MATRIX_PEAK_TFLOPS
     roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(gbs / HBM_PEAK_GBS, 4)} if hbm_bound else
-            {"bound": "mfma", "achieved": round(pv_tflops, 2), "peak": FP32_MATRIX_PEAK_TFLOPS,
-             "unit": "TFLOP/s", "frac": round(pv_tflops / FP32_MATRIX_PEAK_TFLOPS, 4),
-             "contraction": "P.V (fp32 x fp32 -> fp32); Q.K^T (bf16) not counted"})
+            {"bound": "mfma", "achieved": round(tflops, 2), "peak": mpeak,
+             "unit": "TFLOP/s", "frac": round(tflops / mpeak, 4),
+             "contraction": f"Q.K^T and P.V, {spec.kv_dtype} operands, fp32 accumulation"})
     roof.update({"kernel": "paged_attention_multi_query (plan + attention + merge)",
                  "traffic": None})
     result = {

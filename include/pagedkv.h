@@ -349,9 +349,10 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
  * head_dim 64 or 128, block_size 16 or 32, num_heads / num_kv_heads in {1, 2, 4, 8},
  * num_tokens * num_heads * head_dim * sizeof(kv_dtype) below 2^31.  Workspace:
  * pkv_paged_attention_multi_query_workspace_bytes() bytes, no initialisation needed.
- * With U = ceil(num_tokens / (16 / G)) + num_seqs (G = num_heads / num_kv_heads) it
+ * With G = num_heads / num_kv_heads, R = 32 rows per unit when num_tokens * G >
+ * 16 * num_seqs and 16 otherwise, and U = ceil(num_tokens / (R / G)) + num_seqs, it
  * holds a 256-byte header, the unit plan (U + 1, U and num_seqs + 1 int32, each
- * rounded up to 256 bytes) and (1024 + U) * num_kv_heads * 16 records of
+ * rounded up to 256 bytes) and (1024 + U) * num_kv_heads * R records of
  * (head_dim + 2) fp32.  Device-side contract: rows of a sequence that does not fit
  * (as for the slot mapping), or that lists a block id outside [0, num_blocks) within
  * its context, are NaN; a query_start_loc that is not a non-decreasing cut of the

@@ -12,8 +12,8 @@
 // decode step.
 //
 // Work split.  Rows are (new token, query head) pairs; the rows of one sequence and
-// kv head are cut into units of kMqRows = 16 (16 / G consecutive new tokens with the
-// G query heads of the kv head each), so a unit is exactly one MFMA operand.  A unit
+// kv head are cut into units of 16 or 32 rows (R / G consecutive new tokens with the
+// G query heads of the kv head each), one or two MFMA operands.  A unit
 // reads the tiles of its sequence up to its last token's position.  As in the
 // balanced decode split, all (unit, tile) pairs form one list, each unit preceded
 // by kSeqCost positions, and a one-round grid takes equal shares of it; the run of
@@ -29,15 +29,22 @@
 //  - causal mask (token t visible to a row at position p when t <= p), online
 //    softmax per row in the base-2 domain with the lazy rebase of the decode kernel;
 //    row maxima and sums across the four lanes of a row by lane shuffles.
-//  - P.V on fp32 matrix instructions (v_mfma_f32_16x16x4_f32, P kept in fp32): k-step
-//    s takes token 4q + s from each lane quarter q, and each lane reads 8 (D / 16)
-//    consecutive value columns of that token row in one LDS read, one column per
-//    output block, so the value tile needs no transpose either (the output columns
-//    of block e are e, e + D/16, ... permuted back at the store).
+//  - P.V on the matrix cores.  Each lane reads D / 16 consecutive value columns of a
+//    token row in one LDS read, one column per output block, so the value tile needs
+//    no transpose either (output block e holds columns e, e + D/16, ...; undone at
+//    the store).  bf16 caches: v_mfma_f32_16x16x16_bf16 with lane quarter q supplying
+//    tokens 4q .. 4q + 3 (the B operand packed from four token rows) and P split into
+//    bf16 hi + lo parts, together exact to about 2^-17 of p (a single bf16 P could move
+//    outputs by up to ~5e-3); fp32 caches: v_mfma_f32_16x16x4_f32 with fp32 P, k-step
+//    s taking token 4q + s from lane quarter q.
+//  - A unit is one or two MFMA row blocks (16 or 32 rows: two when the sequences
+//    average more than 16 rows), so up to 32 rows share one pass over the tiles.
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
 #include "pkv_stream.hpp"
 #include "pkv_tile.hpp"
+
+#include <type_traits>
 
 namespace pkv {
 
@@ -140,7 +147,7 @@ __device__ int block_scan(int n, F x_of, int* __restrict__ out) {
 __global__ __launch_bounds__(kMqPlanThreads) void multi_plan_kernel(AttentionArgs a) {
   const int B = a.num_seqs;
   const int G = a.num_heads / a.num_kv_heads;
-  const int tpb = kMqRows / G;   // new tokens per unit
+  const int tpb = a.unit_rows / G;   // new tokens per unit
   const int max_ctx = a.max_blocks_per_seq << a.block_shift;
   const int32_t* qsl = a.query_start_loc;
   auto units_of = [&](int i) {
@@ -185,7 +192,7 @@ hipError_t launch_multi_plan(const AttentionArgs& a, hipStream_t stream) {
 
 // ---- the attention kernel ----------------------------------------------------------
 
-template <typename T, int D, int G, int HW>
+template <typename T, int D, int G, int HW, int RB>
 __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(AttentionArgs a) {
   constexpr int TOK = kTileTokens;
   constexpr int NBUF = 2;
@@ -193,17 +200,15 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   constexpr int EB = T::kElemBytes;
   constexpr int NCH = D * EB / 16;          // 16-byte chunks of a head's row
   constexpr int QKC = D * EB / 64;          // key / query chunks per lane = MFMAs per tile
-  constexpr int TPB = kMqRows / G;          // new tokens per unit
+  constexpr int ROWS = 16 * RB;             // rows per unit: RB MFMA row blocks
+  constexpr int TPB = ROWS / G;             // new tokens per unit
   constexpr int CPL = D / 16;               // value columns per lane per k-step
   constexpr int L = 2 * St::kCopies;        // tile copies per wave per step
   constexpr int QROW = D * EB;              // bytes of one query row
-  constexpr int QNI = kMqRows * QROW / 1024;  // query copies per wave per unit
   constexpr int NS = St::kTileSlots;
   static_assert(TOK == 16, "tile rows");
-  static_assert(kMqRows * QROW % 1024 == 0, "query rows in 1 KiB wave copies");
 
   __shared__ uint4 kb0[NS], vb0[NS], kb1[NS], vb1[NS];
-  __shared__ uint4 q_lds[HW][kMqRows * QROW / 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   if (cc.t >= cc.stop) return;
 
   // the unit under the compute cursor
-  int useq = 0, uq0 = 0, uqlen = 0, uctx = 0, uj0 = 0;
+  int uq0 = 0, uqlen = 0, uctx = 0, uj0 = 0;
   auto unit_info = [&]() {
-    useq = uniform(unit_seq[cc.u]);
+    const int useq = uniform(unit_seq[cc.u]);
     uq0 = uniform(qsl[useq]);
     uqlen = uniform(qsl[useq + 1] - uq0);
     uctx = uniform(ctx_of[useq]);
@@ -333,39 +338,39 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   bool seg_from_zero = cc.t == 0;
   int seg_bad = 0;
 
-  // The unit's 16 query rows: row r is new token j0 + r / G (repeated from the
-  // unit's first token past the sequence's last, never stored) with query head
-  // g * G + r % G.  Copied into q_lds like the tiles, read at the unit's first tile.
-  uint4 qa[QKC];
-  bool q_fresh = false;
+  // The unit's rows as the B operand of Q.K^T: row r (block r / 16, lane column
+  // r % 16) is new token j0 + r / G (a row past the sequence's last new token repeats
+  // the unit's first one and is never stored) with query head g * G + r % G.  Loaded
+  // once per unit with ordinary loads and waited for at once, which also waits for
+  // the tile copies in flight: one drain per unit.
+  uint4 qa[RB][QKC];
   auto load_query = [&]() {
-    q_fresh = true;
-    const char* base = static_cast<const char*>(a.query);
 #pragma unroll
-    for (int i = 0; i < QNI; ++i) {
-      const int b = i * 1024 + lane * 16;
-      const int r = b / QROW;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + col;
       const int jq = uj0 + r / G < uqlen ? uj0 + r / G : uj0;
-      const uint32_t off =
-          (uint32_t)(((int64_t)(uq0 + jq) * H + g * G + r % G) * QROW + b % QROW);
-      dma16(base, off, lds_addr(q_lds[wave]) + i * 1024);
-    }
-  };
-  auto read_query = [&]() {
-    const uint4* q = q_lds[wave] + col * NCH;
+      const char* row = static_cast<const char*>(a.query) +
+                        ((int64_t)(uq0 + jq) * H + g * G + r % G) * QROW;
 #pragma unroll
-    for (int c = 0; c < QKC; ++c) qa[c] = q[4 * c + quarter];
+      for (int c = 0; c < QKC; ++c)
+        qa[rb][c] = *reinterpret_cast<const uint4*>(row + (4 * c + quarter) * 16);
+    }
+    // a wait the compiler sees (all vector memory, the copies in flight included), so
+    // that it places none of its own for these loads inside the tile loop
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   };
 
-  // row col of the unit (this lane's score row): its position, and whether it exists
-  float m_run;          // running maximum of the lane's row (base-2 domain)
-  float l_lane;         // the lane's share of the row's sum
-  floatx4 acc[CPL];     // output rows 4 * quarter + j, columns col * CPL + e of block e
+  float m_run[RB];      // running maximum of the lane's row of each block (base-2)
+  float l_lane[RB];     // the lane's share of that row's sum
+  floatx4 acc[RB][CPL]; // rows 16 rb + 4 quarter + j, columns col * CPL + e of block e
   auto reset = [&]() {
-    m_run = kNegInf;
-    l_lane = 0.f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) {
+      m_run[rb] = kNegInf;
+      l_lane[rb] = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[rb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     seg_bad = 0;
   };
 
@@ -377,40 +382,97 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
 #pragma unroll
     for (int c = 0; c < QKC; ++c)
       kk[c] = kb[col * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ St::swz(col))];
-    const floatx4 s4 = tile_scores<T, QKC>(kk, qa);   // S^T: row col, tokens 4q + j
-    const int jrow = min(uj0 + col / G, uqlen - 1);
-    const int prow = uctx - uqlen + jrow;              // last position row col sees
-    float sc[4];
-    float mx = kNegInf;
+    float p[RB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = tok0 + 4 * quarter + j;
-      sc[j] = t <= prow ? s4[j] * a.scale_log2 : kNegInf;
-      mx = fmaxf(mx, sc[j]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool up = mx > m_run + kRebase;
-    if (__ballot(up)) {
-      const float alpha = up ? fast_exp2(m_run - mx) : 1.f;   // 0 when m_run is -inf
-      m_run = up ? mx : m_run;
-      l_lane *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      const floatx4 s4 = tile_scores<T, QKC>(kk, qa[rb]);   // S^T: row col, tokens 4q + j
+      const int jrow = min(uj0 + (rb * 16 + col) / G, uqlen - 1);
+      const int prow = uctx - uqlen + jrow;                  // last position the row sees
+      float sc[4];
+      float mx = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float aj = __shfl(alpha, 4 * quarter + j);
+        const int t = tok0 + 4 * quarter + j;
+        sc[j] = t <= prow ? s4[j] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[j]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool up = mx > m_run[rb] + kRebase;
+      if (__ballot(up)) {
+        const float alpha = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
+        m_run[rb] = up ? mx : m_run[rb];
+        l_lane[rb] *= alpha;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) acc[e][j] *= aj;
+        for (int j = 0; j < 4; ++j) {
+          const float aj = __shfl(alpha, 4 * quarter + j);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[rb][e][j] *= aj;
+        }
+      }
+      const float mref = m_run[rb] == kNegInf ? 0.f : m_run[rb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[rb][j] = fast_exp2(sc[j] - mref);   // 0 for masked tokens
+        l_lane[rb] += p[rb][j];
       }
     }
-    const float mref = m_run == kNegInf ? 0.f : m_run;
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(sc[j] - mref);   // 0 for masked tokens
-      l_lane += p[j];
-    }
-    // P.V: k-step s takes token 4q + s of lane quarter q
     const bool full = tok0 + TOK <= uctx;
+    if constexpr (std::is_same<T, BF16>::value) {
+      // P.V on bf16 matrix instructions (16x16x16): lane quarter q supplies tokens
+      // 4q .. 4q + 3 of its row (A) and of its value columns (B, packed from four token
+      // rows).  P is split into hi + lo bf16 terms, together exact to about 2^-17 of p,
+      // so the products keep fp32-level accuracy.
+      uint32_t w[4][CPL / 2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int vr = 4 * quarter + s;
+        const bool dead = !full && tok0 + vr >= uctx;   // rows past the context may hold NaN
+        if constexpr (CPL == 8) {
+          const uint4 c = vb[vr * St::kSlots + ((wave * NCH + col) ^ St::swz(vr))];
+          w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
+          w[s][2] = dead ? 0u : c.z; w[s][3] = dead ? 0u : c.w;
+        } else {
+          static_assert(CPL == 4, "value piece");
+          const int slot = (wave * NCH + (col >> 1)) ^ St::swz(vr);
+          const uint2 c = reinterpret_cast<const uint2*>(vb)[2 * (vr * St::kSlots + slot) + (col & 1)];
+          w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
+        }
+      }
+      uint2 bv[CPL];   // block e: column col * CPL + e of tokens 4q .. 4q + 3
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int d = e >> 1;
+        if (e & 1) {
+          bv[e].x = (w[0][d] >> 16) | (w[1][d] & 0xffff0000u);
+          bv[e].y = (w[2][d] >> 16) | (w[3][d] & 0xffff0000u);
+        } else {
+          bv[e].x = (w[0][d] & 0xffffu) | (w[1][d] << 16);
+          bv[e].y = (w[2][d] & 0xffffu) | (w[3][d] << 16);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const floatx2 p01 = {p[rb][0], p[rb][1]}, p23 = {p[rb][2], p[rb][3]};
+        const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
+        const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
+        const floatx2 r01 = p01 - __builtin_convertvector(h01, floatx2);
+        const floatx2 r23 = p23 - __builtin_convertvector(h23, floatx2);
+        const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
+        const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
+        const bf16x4 ahi = {h01[0], h01[1], h23[0], h23[1]};
+        const bf16x4 alo = {l01[0], l01[1], l23[0], l23[1]};
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const bf16x4 b = __builtin_bit_cast(bf16x4, bv[e]);
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc[rb][e], 0, 0, 0);
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc[rb][e], 0, 0, 0);
+        }
+      }
+      return;
+    }
+    // fp32 caches: P.V on fp32 matrix instructions; k-step s takes token 4q + s of lane
+    // quarter q; the value row is read once for all row blocks
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int vr = 4 * quarter + s;
@@ -433,53 +495,59 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
         for (int e = 0; e < CPL; ++e) v[e] = 0.f;   // rows past the context may hold NaN
       }
 #pragma unroll
-      for (int e = 0; e < CPL; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[s], v[e], acc[e], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[rb][s], v[e], acc[rb][e], 0, 0, 0);
     }
   };
 
   // End of a segment: sums across the four lanes of each row, normalise, store rows
-  // 4 * quarter + j (output or record).
+  // 16 rb + 4 quarter + j (output or record).
   auto finish = [&](bool whole) {
-    float l_row = l_lane + __shfl_xor(l_lane, 16);
-    l_row += __shfl_xor(l_row, 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * quarter + j;
-      const float lr = __shfl(l_row, r);
-      const float mr = __shfl(m_run, r);
-      const int jq = uj0 + r / G;
-      if (jq >= uqlen) continue;
-      const float inv = seg_bad ? __builtin_nanf("") : (lr > 0.f ? 1.f / lr : 0.f);
-      float o[CPL];
+    for (int rb = 0; rb < RB; ++rb) {
+      float l_row = l_lane[rb] + __shfl_xor(l_lane[rb], 16);
+      l_row += __shfl_xor(l_row, 32);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) o[e] = acc[e][j] * inv;
-      if (whole) {
-        const int64_t orow = ((int64_t)(uq0 + jq) * H + g * G + r % G) * D + col * CPL;
-        if (a.out_bf16) {
-          uint16_t* dst = static_cast<uint16_t*>(a.out) + orow;
+      for (int j = 0; j < 4; ++j) {
+        const int r = rb * 16 + 4 * quarter + j;
+        const float lr = __shfl(l_row, 4 * quarter + j);
+        const float mr = __shfl(m_run[rb], 4 * quarter + j);
+        const int jq = uj0 + r / G;
+        if (jq >= uqlen) continue;
+        const float inv = seg_bad ? __builtin_nanf("") : (lr > 0.f ? 1.f / lr : 0.f);
+        float o[CPL];
 #pragma unroll
-          for (int e = 0; e < CPL; e += 4) {
-            uint2 v;
-            v.x = f32_to_bf16_rne(o[e]) | (uint32_t)f32_to_bf16_rne(o[e + 1]) << 16;
-            v.y = f32_to_bf16_rne(o[e + 2]) | (uint32_t)f32_to_bf16_rne(o[e + 3]) << 16;
-            *reinterpret_cast<uint2*>(dst + e) = v;
+        for (int e = 0; e < CPL; ++e) o[e] = acc[rb][e][j] * inv;
+        if (whole) {
+          const int64_t orow = ((int64_t)(uq0 + jq) * H + g * G + r % G) * D + col * CPL;
+          if (a.out_bf16) {
+            uint16_t* dst = static_cast<uint16_t*>(a.out) + orow;
+#pragma unroll
+            for (int e = 0; e < CPL; e += 4) {
+              uint2 v;
+              v.x = f32_to_bf16_rne(o[e]) | (uint32_t)f32_to_bf16_rne(o[e + 1]) << 16;
+              v.y = f32_to_bf16_rne(o[e + 2]) | (uint32_t)f32_to_bf16_rne(o[e + 3]) << 16;
+              *reinterpret_cast<uint2*>(dst + e) = v;
+            }
+          } else {
+            float* dst = static_cast<float*>(a.out) + orow;
+#pragma unroll
+            for (int e = 0; e < CPL; e += 4)
+              *reinterpret_cast<float4*>(dst + e) =
+                  make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
           }
         } else {
-          float* dst = static_cast<float*>(a.out) + orow;
+          const int64_t rec = (((int64_t)w + cc.u) * Hkv + g) * ROWS + r;
+          float* dst = a.ws_o + rec * D + col * CPL;
 #pragma unroll
           for (int e = 0; e < CPL; e += 4)
             *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-        }
-      } else {
-        const int64_t rec = (((int64_t)w + cc.u) * Hkv + g) * kMqRows + r;
-        float* dst = a.ws_o + rec * D + col * CPL;
-#pragma unroll
-        for (int e = 0; e < CPL; e += 4)
-          *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-        if (col == 0) {
-          a.ws_m[rec] = mr;
-          a.ws_l[rec] = seg_bad ? __builtin_nanf("") : lr;
+          if (col == 0) {
+            a.ws_m[rec] = mr;
+            a.ws_l[rec] = seg_bad ? __builtin_nanf("") : lr;
+          }
         }
       }
     }
@@ -494,10 +562,6 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   issue(KF, VF);                                                          \
   wait_copies<(NBUF - 1) * L>();                                          \
   bare_barrier();                                                         \
-  if (q_fresh) {                                                          \
-    read_query();                                                         \
-    q_fresh = false;                                                      \
-  }                                                                       \
   compute(KB, VB, (bad_pipe >> (NBUF - 1)) & 1u);                         \
   bare_barrier();                                                         \
   if (cc.t == cc.stop - 1) {                                              \
@@ -537,7 +601,8 @@ __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(Atten
   const int h = (int)(row % H);
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
-  const int tpb = kMqRows / G;
+  const int rows = a.unit_rows;
+  const int tpb = rows / G;
   const int kg = lane / LPR;
   const int lr = lane % LPR;
   const int B = a.num_seqs;
@@ -568,7 +633,7 @@ __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(Atten
   Running acc{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   for (int ww = w0 + kg; ww <= w1; ww += KGW) {
     if (!share_nonempty(ww, nwg, total)) continue;
-    const int64_t rec = (((int64_t)ww + u) * Hkv + g) * kMqRows + r;
+    const int64_t rec = (((int64_t)ww + u) * Hkv + g) * rows + r;
     const float l = a.ws_l[rec];
     if (!(l > 0.f) && !(l != l)) continue;   // empty segment (NaN l: keep, marks bad data)
     Running s{a.ws_m[rec], l, reinterpret_cast<const float4*>(a.ws_o + rec * D)[lr]};
@@ -604,9 +669,9 @@ hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t str
 
 // ---- dispatch ------------------------------------------------------------------
 
-template <typename T, int D, int G, int HW>
-static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream) {
-  auto kernel = paged_attention_multi_kernel<T, D, G, HW>;
+template <typename T, int D, int G, int HW, int RB>
+static hipError_t launch_multi_rb(const AttentionArgs& a, hipStream_t stream) {
+  auto kernel = paged_attention_multi_kernel<T, D, G, HW, RB>;
   static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, HW * kWave, 0) != hipSuccess)
@@ -619,6 +684,12 @@ static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream)
   const int nwg = max(1, min(kMaxStreamWgs, per_cu * cus / hgroups));
   hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(HW * kWave), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int G, int HW>
+static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream) {
+  return a.unit_rows == 32 ? launch_multi_rb<T, D, G, HW, 2>(a, stream)
+                           : launch_multi_rb<T, D, G, HW, 1>(a, stream);
 }
 
 #ifndef PKV_MULTI_MAX_ROW

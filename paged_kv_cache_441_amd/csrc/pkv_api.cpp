@@ -490,6 +490,7 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, const void* query, const vo
 namespace {
 
 struct MultiShape {
+  int rows = 16;            // rows per unit: 32 when sequences average more than 16 rows
   int64_t max_units = 0;
   int64_t recs = 0;
   size_t plan_bytes = 0;
@@ -507,14 +508,16 @@ pkv_status check_multi_shape(int32_t num_seqs, int32_t num_tokens, int32_t num_h
   if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX / 2, &max_ctx)) return PKV_ERR_INVALID_ARG;
   const int G = num_heads / num_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PKV_ERR_UNSUPPORTED;
-  const int64_t tpb = pkv::kMqRows / G;
+  m->rows = int64_t{num_tokens} * G > int64_t{pkv::kMqRows} * num_seqs ? 2 * pkv::kMqRows
+                                                                         : pkv::kMqRows;
+  const int64_t tpb = m->rows / G;
   m->max_units = (int64_t{num_tokens} + tpb - 1) / tpb + num_seqs;
   // list positions are int32: units x (tiles of the longest context + 1)
   int64_t pos = 0;
   if (!mul_ok(m->max_units, (max_ctx + pkv::kTileTokens - 1) / pkv::kTileTokens + pkv::kSeqCost,
               INT32_MAX / 2, &pos))
     return PKV_ERR_UNSUPPORTED;
-  if (!mul_ok(m->max_units + pkv::kMaxStreamWgs, int64_t{num_kv_heads} * pkv::kMqRows,
+  if (!mul_ok(m->max_units + pkv::kMaxStreamWgs, int64_t{num_kv_heads} * m->rows,
               INT64_MAX / 1024, &m->recs))
     return PKV_ERR_INVALID_ARG;
   m->plan_bytes = pkv::multi_plan_bytes(num_seqs, m->max_units);
@@ -534,6 +537,7 @@ void set_multi_workspace(pkv::AttentionArgs* a, void* workspace, const MultiShap
   a->seq_unit = reinterpret_cast<int*>(ws + 256 + r256((m.max_units + 1) * 4) +
                                         r256(m.max_units * 4));
   a->max_units = static_cast<int>(m.max_units);
+  a->unit_rows = m.rows;
   float* f = reinterpret_cast<float*>(ws + m.plan_bytes);
   a->ws_m = f;
   a->ws_l = f + m.recs;

@@ -35,6 +35,7 @@ struct FP8 {
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // E4M3 code of x, rounded to the nearest value with ties to the even code; finite
 // magnitudes of 448 and beyond (and infinities) give +-448, NaN gives 0x7F.

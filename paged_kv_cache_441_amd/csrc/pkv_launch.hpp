@@ -68,15 +68,17 @@ struct AttentionArgs {
   int* tile_hdr;            // [0] total tiles, [1] workgroups per kv-head group
   int* tile_cum;            // [num_seqs + 1] tiles before each sequence
   // Multi-token steps: the flat token batch and the units of the work list (a unit is
-  // one sequence's block of kMqRows (new token, query head) rows of one kv head).
+  // one sequence's block of unit_rows (new token, query head) rows of one kv head).
   const int32_t* query_start_loc;   // [num_seqs + 1]
   int num_tokens;
+  int unit_rows;            // 16 or 32: one or two MFMA row blocks per unit
   int max_units;            // capacity of the unit arrays
   int* unit_seq;            // [max_units] sequence of each unit
   int* seq_unit;            // [num_seqs + 1] first unit of each sequence
 };
 
-// Multi-token steps: query rows per unit (one MFMA operand of (token, head) rows).
+// Multi-token steps: rows of one MFMA row block of (token, head) rows; a unit is one
+// or two of them.
 constexpr int kMqRows = 16;
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels

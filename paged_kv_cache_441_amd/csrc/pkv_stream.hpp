@@ -36,6 +36,11 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained (gfx9
+// layout: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  Unlike the
+// assembly waits above, the compiler sees this one.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xf << 8);
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
