@@ -192,15 +192,20 @@ hipError_t launch_multi_plan(const AttentionArgs& a, hipStream_t stream) {
 
 // ---- the attention kernel ----------------------------------------------------------
 
-template <typename T, int D, int G, int HW, int RB>
-__global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(AttentionArgs a) {
+// NW waves per workgroup.  NW == HW: each wave owns one of the HW kv heads of the
+// staged rows and a unit is RB row blocks.  HW == 1 < NW: the waves share one kv
+// head's rows and each takes RB of the unit's NW * RB row blocks, so one pass over
+// the tiles serves NW * RB * 16 rows (long prompts).
+template <typename T, int D, int G, int HW, int RB, int NW, int NBUF>
+__global__ __launch_bounds__(NW * kWave) void paged_attention_multi_kernel(AttentionArgs a) {
   constexpr int TOK = kTileTokens;
-  constexpr int NBUF = 2;
-  using St = Stage<T, D, HW, TOK>;
+  constexpr bool kRowWaves = NW != HW;      // waves split the rows of one head
+  static_assert(!kRowWaves || HW == 1, "row-split waves share a single head");
+  using St = StageW<T, D, HW, TOK, NW>;
   constexpr int EB = T::kElemBytes;
   constexpr int NCH = D * EB / 16;          // 16-byte chunks of a head's row
   constexpr int QKC = D * EB / 64;          // key / query chunks per lane = MFMAs per tile
-  constexpr int ROWS = 16 * RB;             // rows per unit: RB MFMA row blocks
+  constexpr int ROWS = kRowWaves ? NW * 16 * RB : 16 * RB;   // rows per unit
   constexpr int TPB = ROWS / G;             // new tokens per unit
   constexpr int CPL = D / 16;               // value columns per lane per k-step
   constexpr int L = 2 * St::kCopies;        // tile copies per wave per step
@@ -208,16 +213,21 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   constexpr int NS = St::kTileSlots;
   static_assert(TOK == 16, "tile rows");
 
-  __shared__ uint4 kb0[NS], vb0[NS], kb1[NS], vb1[NS];
+  // NBUF tiles rotate through one ring; the copies are assembly the compiler does not
+  // track, so one array indexed at run time costs no extra waits
+  __shared__ uint4 kring[NBUF][NS], vring[NBUF][NS];
+  static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nwg = gridDim.x;
-  const int w = blockIdx.x;
+  const int w = xcd_local_share(blockIdx.x, nwg);
   const int hg = blockIdx.y;
   const int Hkv = a.num_kv_heads;
   const int H = Hkv * G;
-  const int g = hg * HW + wave;             // this wave's kv head
+  const int hw_idx = kRowWaves ? 0 : wave;  // this wave's head within the staged rows
+  const int g = hg * HW + hw_idx;           // this wave's kv head
+  const int row0 = kRowWaves ? wave * 16 * RB : 0;   // this wave's first row of the unit
 
   cint32* cum = (cint32*)a.tile_cum;
   cint32* ctx_of = (cint32*)a.context_lens;
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   uint32_t copy_off[St::kCopies];
 #pragma unroll
   for (int i = 0; i < St::kCopies; ++i) {
-    const int s = (i * HW + wave) * kWave + lane;
+    const int s = (i * NW + wave) * kWave + lane;
     const int r = s / St::kSlots;
     const int p = s % St::kSlots;
     copy_off[i] = (uint32_t)(r * row_stride) + (uint32_t)((p ^ St::swz(r)) * 16);
@@ -317,9 +327,9 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
     const char* kbase = kcache + base;
     const char* vbase = vcache + base;
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16(kbase, copy_off[i], kd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16(kbase, copy_off[i], kd + i * NW * 1024);
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16(vbase, copy_off[i], vd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16(vbase, copy_off[i], vd + i * NW * 1024);
   };
 
   // ---- compute side ----
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   auto load_query = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int r = rb * 16 + col;
+      const int r = row0 + rb * 16 + col;
       const int jq = uj0 + r / G < uqlen ? uj0 + r / G : uj0;
       const char* row = static_cast<const char*>(a.query) +
                         ((int64_t)(uq0 + jq) * H + g * G + r % G) * QROW;
@@ -381,12 +391,12 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
     uint4 kk[QKC];
 #pragma unroll
     for (int c = 0; c < QKC; ++c)
-      kk[c] = kb[col * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ St::swz(col))];
+      kk[c] = kb[col * St::kSlots + ((hw_idx * NCH + 4 * c + quarter) ^ St::swz(col))];
     float p[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const floatx4 s4 = tile_scores<T, QKC>(kk, qa[rb]);   // S^T: row col, tokens 4q + j
-      const int jrow = min(uj0 + (rb * 16 + col) / G, uqlen - 1);
+      const int jrow = min(uj0 + (row0 + rb * 16 + col) / G, uqlen - 1);
       const int prow = uctx - uqlen + jrow;                  // last position the row sees
       float sc[4];
       float mx = kNegInf;
@@ -429,12 +439,12 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
         const int vr = 4 * quarter + s;
         const bool dead = !full && tok0 + vr >= uctx;   // rows past the context may hold NaN
         if constexpr (CPL == 8) {
-          const uint4 c = vb[vr * St::kSlots + ((wave * NCH + col) ^ St::swz(vr))];
+          const uint4 c = vb[vr * St::kSlots + ((hw_idx * NCH + col) ^ St::swz(vr))];
           w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
           w[s][2] = dead ? 0u : c.z; w[s][3] = dead ? 0u : c.w;
         } else {
           static_assert(CPL == 4, "value piece");
-          const int slot = (wave * NCH + (col >> 1)) ^ St::swz(vr);
+          const int slot = (hw_idx * NCH + (col >> 1)) ^ St::swz(vr);
           const uint2 c = reinterpret_cast<const uint2*>(vb)[2 * (vr * St::kSlots + slot) + (col & 1)];
           w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
         }
@@ -478,14 +488,14 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
       const int vr = 4 * quarter + s;
       float v[CPL];
       if constexpr (CPL * EB == 16) {
-        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + col) ^ St::swz(vr))], v);
+        unpack_chunk<T>(vb[vr * St::kSlots + ((hw_idx * NCH + col) ^ St::swz(vr))], v);
       } else if constexpr (CPL * EB == 32) {
-        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + 2 * col) ^ St::swz(vr))], v);
-        unpack_chunk<T>(vb[vr * St::kSlots + ((wave * NCH + 2 * col + 1) ^ St::swz(vr))],
+        unpack_chunk<T>(vb[vr * St::kSlots + ((hw_idx * NCH + 2 * col) ^ St::swz(vr))], v);
+        unpack_chunk<T>(vb[vr * St::kSlots + ((hw_idx * NCH + 2 * col + 1) ^ St::swz(vr))],
                         v + CPL / 2);
       } else {
         static_assert(CPL * EB == 8, "value piece");
-        const int slot = (wave * NCH + (col >> 1)) ^ St::swz(vr);
+        const int slot = (hw_idx * NCH + (col >> 1)) ^ St::swz(vr);
         const uint2 c8 = reinterpret_cast<const uint2*>(vb)[2 * (vr * St::kSlots + slot) + (col & 1)];
         v[0] = bf16_lo(c8.x); v[1] = bf16_hi(c8.x);
         v[2] = bf16_lo(c8.y); v[3] = bf16_hi(c8.y);
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
       l_row += __shfl_xor(l_row, 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = rb * 16 + 4 * quarter + j;
+        const int r = row0 + rb * 16 + 4 * quarter + j;
         const float lr = __shfl(l_row, 4 * quarter + j);
         const float mr = __shfl(m_run[rb], 4 * quarter + j);
         const int jq = uj0 + r / G;
@@ -557,32 +567,31 @@ __global__ __launch_bounds__(HW * kWave) void paged_attention_multi_kernel(Atten
   unit_info();
   load_query();
 
-#define PKV_MULTI_STEP(KB, VB, KF, VF)                                    \
-  if (cc.t >= cc.stop) break;                                             \
-  issue(KF, VF);                                                          \
-  wait_copies<(NBUF - 1) * L>();                                          \
-  bare_barrier();                                                         \
-  compute(KB, VB, (bad_pipe >> (NBUF - 1)) & 1u);                         \
-  bare_barrier();                                                         \
-  if (cc.t == cc.stop - 1) {                                              \
-    finish(seg_from_zero && cc.stop == cc.nt);                            \
-    reset();                                                              \
-    cc = next_unit(cc);                                                   \
-    seg_from_zero = true;                                                 \
-    if (cc.t < cc.stop) {                                                 \
-      unit_info();                                                        \
-      load_query();                                                       \
-    }                                                                     \
-  } else {                                                                \
-    ++cc.t;                                                               \
+  // Tile j sits in ring slot j % NBUF; the copies of tile j + NBUF - 1 are issued
+  // before tile j is waited for and computed.
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) issue(kring[i], vring[i]);
+  for (int j = 0;; ++j) {
+    if (cc.t >= cc.stop) break;
+    const int fill = (j + NBUF - 1) % NBUF;
+    issue(kring[fill], vring[fill]);
+    wait_copies<(NBUF - 1) * L>();
+    bare_barrier();
+    compute(kring[j % NBUF], vring[j % NBUF], (bad_pipe >> (NBUF - 1)) & 1u);
+    bare_barrier();
+    if (cc.t == cc.stop - 1) {
+      finish(seg_from_zero && cc.stop == cc.nt);
+      reset();
+      cc = next_unit(cc);
+      seg_from_zero = true;
+      if (cc.t < cc.stop) {
+        unit_info();
+        load_query();
+      }
+    } else {
+      ++cc.t;
+    }
   }
-
-  issue(kb0, vb0);
-  for (;;) {
-    PKV_MULTI_STEP(kb0, vb0, kb1, vb1)
-    PKV_MULTI_STEP(kb1, vb1, kb0, vb0)
-  }
-#undef PKV_MULTI_STEP
   wait_copies<0>();
 }
 
@@ -669,12 +678,12 @@ hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t str
 
 // ---- dispatch ------------------------------------------------------------------
 
-template <typename T, int D, int G, int HW, int RB>
+template <typename T, int D, int G, int HW, int RB, int NW, int NBUF = 2>
 static hipError_t launch_multi_rb(const AttentionArgs& a, hipStream_t stream) {
-  auto kernel = paged_attention_multi_kernel<T, D, G, HW, RB>;
+  auto kernel = paged_attention_multi_kernel<T, D, G, HW, RB, NW, NBUF>;
   static const int per_cu = [&] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, HW * kWave, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, NW * kWave, 0) != hipSuccess)
       n = 1;
     return n > 0 ? n : 1;
   }();
@@ -682,15 +691,21 @@ static hipError_t launch_multi_rb(const AttentionArgs& a, hipStream_t stream) {
   if (cus <= 0) return hipErrorInvalidDevice;
   const int hgroups = a.num_kv_heads / HW;
   const int nwg = max(1, min(kMaxStreamWgs, per_cu * cus / hgroups));
-  hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(HW * kWave), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int G, int HW>
 static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream) {
-  return a.unit_rows == 32 ? launch_multi_rb<T, D, G, HW, 2>(a, stream)
-                           : launch_multi_rb<T, D, G, HW, 1>(a, stream);
+  return a.unit_rows == 32 ? launch_multi_rb<T, D, G, HW, 2, HW>(a, stream)
+                           : launch_multi_rb<T, D, G, HW, 1, HW>(a, stream);
 }
+
+// Ring depth of the row-split mode: its tiles are one head's rows (a quarter or less
+// of a whole-row tile), so more of them are kept in flight.
+#ifndef PKV_MULTI_ROW_NBUF
+#define PKV_MULTI_ROW_NBUF 2
+#endif
 
 #ifndef PKV_MULTI_MAX_ROW
 #define PKV_MULTI_MAX_ROW 1024
@@ -701,6 +716,10 @@ static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream)
 template <typename T, int D, int G>
 static hipError_t launch_multi_hw(const AttentionArgs& a, hipStream_t stream) {
   constexpr int kRow = D * T::kElemBytes;
+  // long prompts: four waves share one kv head's rows, 128 rows per unit
+  if constexpr (16 * kRow % (kMqRowWaves * 1024) == 0)
+    if (a.unit_rows == kMqRowUnit)
+      return launch_multi_rb<T, D, G, 1, kMqRowRB, kMqRowWaves, PKV_MULTI_ROW_NBUF>(a, stream);
   if constexpr (8 * kRow <= PKV_MULTI_MAX_ROW)
     if (a.num_kv_heads % 8 == 0) return launch_multi_shape<T, D, G, 8>(a, stream);
   if constexpr (4 * kRow <= PKV_MULTI_MAX_ROW)

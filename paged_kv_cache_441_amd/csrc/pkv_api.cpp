@@ -508,8 +508,15 @@ pkv_status check_multi_shape(int32_t num_seqs, int32_t num_tokens, int32_t num_h
   if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX / 2, &max_ctx)) return PKV_ERR_INVALID_ARG;
   const int G = num_heads / num_kv_heads;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PKV_ERR_UNSUPPORTED;
-  m->rows = int64_t{num_tokens} * G > int64_t{pkv::kMqRows} * num_seqs ? 2 * pkv::kMqRows
-                                                                         : pkv::kMqRows;
+  // rows per unit from the average rows per sequence: one MFMA row block, two, or
+  // (long prompts, head_dim 128) kMqRowWaves waves sharing one kv head
+  const int64_t rows_total = int64_t{num_tokens} * G;
+  if (head_dim == 128 && rows_total >= int64_t{pkv::kMqRowUnit} * num_seqs)
+    m->rows = pkv::kMqRowUnit;
+  else if (rows_total > int64_t{pkv::kMqRows} * num_seqs)
+    m->rows = 2 * pkv::kMqRows;
+  else
+    m->rows = pkv::kMqRows;
   const int64_t tpb = m->rows / G;
   m->max_units = (int64_t{num_tokens} + tpb - 1) / tpb + num_seqs;
   // list positions are int32: units x (tiles of the longest context + 1)

@@ -71,7 +71,7 @@ struct AttentionArgs {
   // one sequence's block of unit_rows (new token, query head) rows of one kv head).
   const int32_t* query_start_loc;   // [num_seqs + 1]
   int num_tokens;
-  int unit_rows;            // 16 or 32: one or two MFMA row blocks per unit
+  int unit_rows;            // 16, 32 or kMqRowUnit rows per unit
   int max_units;            // capacity of the unit arrays
   int* unit_seq;            // [max_units] sequence of each unit
   int* seq_unit;            // [num_seqs + 1] first unit of each sequence
@@ -80,6 +80,14 @@ struct AttentionArgs {
 // Multi-token steps: rows of one MFMA row block of (token, head) rows; a unit is one
 // or two of them.
 constexpr int kMqRows = 16;
+// Multi-token steps with long prompts: waves of a workgroup that share one kv head,
+// each taking kMqRowRB row blocks (a unit of kMqRowUnit rows).
+constexpr int kMqRowWaves = 4;
+#ifndef PKV_MULTI_ROW_RB
+#define PKV_MULTI_ROW_RB 2
+#endif
+constexpr int kMqRowRB = PKV_MULTI_ROW_RB;   // row blocks per wave in that mode
+constexpr int kMqRowUnit = kMqRowWaves * 16 * kMqRowRB;
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels
 // (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.

@@ -48,7 +48,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 template <typename T, int D, int HW, int TOK>
-struct Stage {
+struct Stage;
+
+// The LDS image of one tile: TOK token rows of HW heads, copied by NW waves (NW = HW
+// when each wave owns a head, more when several waves share one head's rows).
+template <typename T, int D, int HW, int TOK, int NW>
+struct StageW {
   static constexpr int kRowBytes = HW * D * T::kElemBytes;   // one token row of the HW heads
   static constexpr int kSlots = kRowBytes / 16;               // 16-byte slots per row
   static constexpr int kSwz = kSlots >= 16 ? 15 : kSlots - 1;
@@ -63,10 +68,25 @@ struct Stage {
   }
   static constexpr int kTileBytes = TOK * kRowBytes;          // per cache
   static constexpr int kTileSlots = kTileBytes / 16;
-  static constexpr int kCopies = kTileBytes / (HW * 1024);    // 1 KiB wave copies per cache
-  static_assert(kTileBytes % (HW * 1024) == 0, "a tile splits into 1 KiB wave copies");
+  static constexpr int kCopies = kTileBytes / (NW * 1024);    // 1 KiB copies per wave and cache
+  static_assert(kTileBytes % (NW * 1024) == 0, "a tile splits into 1 KiB wave copies");
   static_assert(kSlots >= 8, "rows of at least 128 bytes");
 };
+
+template <typename T, int D, int HW, int TOK>
+struct Stage : StageW<T, D, HW, TOK, HW> {};
+
+// Workgroups are handed to the 8 XCDs of an MI355X round-robin (workgroup i to XCD
+// i % 8), and each XCD has its own L2.  This gives the workgroups of one XCD
+// consecutive share indices (XCD x takes shares [x * n / 8, (x + 1) * n / 8)), so
+// that neighbouring shares, which read the same sequence's tiles at about the same
+// time when a sequence spans many units, meet in one L2.  Identity when the grid is
+// not a multiple of 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_local_share(int block, int nwg) {
+  if (nwg % kXcds != 0) return block;
+  return (block % kXcds) * (nwg / kXcds) + block / kXcds;
+}
 
 // Share w of the tile list is [floor(w * total / nwg), floor((w + 1) * total / nwg)).
 // The share holding tile j:
