@@ -202,12 +202,22 @@ hipError_t launch_cache_write_fp8(const void* key, const void* value, void* key_
 // loads all of its 16-byte pieces of both caches before it stores any.  Pairs with
 // an id outside the pool are skipped.  Pairs run in parallel: the caller's contract
 // is that no dst repeats and no dst is also a src.
+//
+// The pieces are native 4 x u32 vectors, and the loads are never conditional: a piece
+// past the block's end (only in a block whose size is not a multiple of kCopyChunk)
+// re-reads the block's last piece and is not stored.  With conditional loads into an
+// array of the struct-typed uint4, the compiler moved the array to LDS and scratch
+// memory, and the scratch round trip cost half as much HBM traffic again as the copy.
+// The stores are non-temporal: the copied blocks are not read again by this launch,
+// and on MI355X (4096 random 32 KiB block pairs of both caches) this took a launch
+// from 115 to 85 us.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCopyThreads = 256;
 constexpr int kCopyPer = 4;                            // pieces per lane per cache
 constexpr int kCopyChunk = kCopyThreads * kCopyPer * 16;
 
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache,
     const int32_t* __restrict__ pairs, int64_t block_chunks, int64_t num_blocks) {
   const int p = blockIdx.x;
   const int32_t src = pairs[2 * p];
@@ -215,21 +225,19 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   const int64_t c0 = (int64_t)blockIdx.y * (kCopyChunk / 16) + threadIdx.x;
   const int64_t s = (int64_t)src * block_chunks, d = (int64_t)dst * block_chunks;
-  uint4 k[kCopyPer], v[kCopyPer];
+  u32x4 k[kCopyPer], v[kCopyPer];
 #pragma unroll
   for (int i = 0; i < kCopyPer; ++i) {
-    const int64_t c = c0 + i * kCopyThreads;
-    if (c < block_chunks) {
-      k[i] = key_cache[s + c];
-      v[i] = value_cache[s + c];
-    }
+    const int64_t c = min(c0 + i * kCopyThreads, block_chunks - 1);
+    k[i] = key_cache[s + c];
+    v[i] = value_cache[s + c];
   }
 #pragma unroll
   for (int i = 0; i < kCopyPer; ++i) {
     const int64_t c = c0 + i * kCopyThreads;
     if (c < block_chunks) {
-      key_cache[d + c] = k[i];
-      value_cache[d + c] = v[i];
+      __builtin_nontemporal_store(k[i], key_cache + d + c);
+      __builtin_nontemporal_store(v[i], value_cache + d + c);
     }
   }
 }
@@ -239,7 +247,7 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
                               hipStream_t stream) {
   const dim3 grid((unsigned)num_pairs, (unsigned)((block_bytes + kCopyChunk - 1) / kCopyChunk));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream,
-                     static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), pairs,
+                     static_cast<u32x4*>(key_cache), static_cast<u32x4*>(value_cache), pairs,
                      block_bytes / 16, num_blocks);
   return hipGetLastError();
 }
