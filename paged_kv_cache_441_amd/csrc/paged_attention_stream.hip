@@ -69,6 +69,13 @@ namespace pkv {
 #define PKV_STREAM_WPE_FP8 4
 #endif
 
+// KV tiles are copied non-temporal (streamed past the caches) unless built with
+// PKV_STREAM_KV_NT=0.
+#ifndef PKV_STREAM_KV_NT
+#define PKV_STREAM_KV_NT 1
+#endif
+constexpr Cpol kKvCpol = PKV_STREAM_KV_NT ? Cpol::kStream : Cpol::kDefault;
+
 template <typename T>
 constexpr int stream_nbuf() { return T::kElemBytes == 1 ? PKV_STREAM_NBUF_FP8 : PKV_STREAM_NBUF; }
 // GQA groups of 8 need more registers than a 4-wave-per-SIMD budget holds
@@ -239,9 +246,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     const char* kbase = kcache + base;
     const char* vbase = vcache + base;
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16(kbase, copy_off[i], kd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16<kKvCpol>(kbase, copy_off[i], kd + i * HW * 1024);
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16(vbase, copy_off[i], vd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16<kKvCpol>(vbase, copy_off[i], vd + i * HW * 1024);
   };
 
   // ---- compute side ------------------------------------------------------------------
