@@ -173,24 +173,21 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
+    # The step's arguments are checked once; each stage is then one C call, so the
+    # host stays ahead of the GPU and the events time the kernels, not the host.
+    ds = pkv.DecodeStep(b.query, b.key, b.value, kc, vc, bt, cl, b.scale, P, out=out,
+                        workspace=ws, slot_mapping=slots, k_scale=ks, v_scale=vs)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        if fp8:
-            pkv.decode_prologue_fp8(bt, cl, b.key, b.value, kc, vc, ws, ks, vs, slot_mapping=slots)
-        else:
-            pkv.decode_prologue(bt, cl, b.key, b.value, kc, vc, ws, P, slot_mapping=slots)
+        ds.prologue()
         if ev is not None:
             ev[1].record()
-        if fp8:
-            pkv.paged_attention_partition_fp8(b.query, kc, vc, bt, cl, b.scale, ks, vs, out=out,
-                                              workspace=ws)
-        else:
-            pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, out=out,
-                                          workspace=ws)
+        ds.partition()
         if ev is not None:
             ev[2].record()
-        pkv.paged_attention_reduce(out, cl, ws, BS, MB, P)
+        ds.reduce()
         if ev is not None:
             ev[3].record()
 

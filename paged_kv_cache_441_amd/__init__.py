@@ -8,6 +8,7 @@ include/pagedkv.h; this package only marshals torch tensors into that ABI.
 from ._lib import LIB_PATH, PkvError, load_library, status_string  # noqa: F401
 from .ops import (  # noqa: F401
     BlockPool,
+    DecodeStep,
     alloc_workspace,
     copy_blocks,
     decode_prologue,

@@ -112,11 +112,12 @@ def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _lib.check(st, "pkv_kv_cache_write")
 
 
-def decode_prologue(block_tables: torch.Tensor, context_lens: torch.Tensor, key: torch.Tensor,
-                    value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                    workspace: torch.Tensor, partition_size: int = 0,
-                    slot_mapping: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Slot mapping + cache write + attention plan in one launch; returns the slots."""
+def _call(name: str, args) -> None:
+    _lib.check(getattr(_lib.load_library(), name)(*args), name)
+
+
+def _prologue_args(block_tables, context_lens, key, value, key_cache, value_cache, workspace,
+                   partition_size, slot_mapping, stream):
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
     dt = _kv(key, "key")
@@ -137,13 +138,22 @@ def decode_prologue(block_tables: torch.Tensor, context_lens: torch.Tensor, key:
     _i32(slot_mapping, "slot_mapping")
     _same_device(block_tables, context_lens, key, value, key_cache, value_cache, workspace,
                  slot_mapping)
-    lib = _lib.load_library()
-    st = lib.pkv_decode_prologue(_ptr(block_tables), _ptr(context_lens), _ptr(key), _ptr(value),
-                                 _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), B,
-                                 block_tables.shape[1], Hkv, D, BS, NB, dt, int(partition_size),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(key))
-    _lib.check(st, "pkv_decode_prologue")
+    args = (_ptr(block_tables), _ptr(context_lens), _ptr(key), _ptr(value), _ptr(key_cache),
+            _ptr(value_cache), _ptr(slot_mapping), B, block_tables.shape[1], Hkv, D, BS, NB, dt,
+            int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            stream if stream is not None else _stream(key))
+    return "pkv_decode_prologue", args, slot_mapping
+
+
+def decode_prologue(block_tables: torch.Tensor, context_lens: torch.Tensor, key: torch.Tensor,
+                    value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    workspace: torch.Tensor, partition_size: int = 0,
+                    slot_mapping: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Slot mapping + cache write + attention plan in one launch; returns the slots."""
+    name, args, slot_mapping = _prologue_args(block_tables, context_lens, key, value, key_cache,
+                                              value_cache, workspace, partition_size,
+                                              slot_mapping, None)
+    _call(name, args)
     return slot_mapping
 
 
@@ -221,37 +231,50 @@ def paged_attention_plan(context_lens: torch.Tensor, workspace: torch.Tensor, bl
     return workspace
 
 
-def paged_attention_partition(query, key_cache, value_cache, block_tables, context_lens, scale,
-                              partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
-    """Stage 2 of paged_attention_decode (needs a plan in ``workspace``); returns (out, workspace)."""
+def _partition_args(query, key_cache, value_cache, block_tables, context_lens, scale,
+                    partition_size, out, out_dtype, workspace, stream):
     dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
         query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
         partition_size)
-    lib = _lib.load_library()
-    st = lib.pkv_paged_attention_partition(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
-        int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
-    _lib.check(st, "pkv_paged_attention_partition")
+    args = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+            int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb,
+            stream if stream is not None else _stream(query))
+    return "pkv_paged_attention_partition", args, out, ws
+
+
+def paged_attention_partition(query, key_cache, value_cache, block_tables, context_lens, scale,
+                              partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
+    """Stage 2 of paged_attention_decode (needs a plan in ``workspace``); returns (out, workspace)."""
+    name, args, out, ws = _partition_args(query, key_cache, value_cache, block_tables,
+                                          context_lens, scale, partition_size, out, out_dtype,
+                                          workspace, None)
+    _call(name, args)
     return out, ws
+
+
+def _reduce_args(out, context_lens, workspace, block_size, max_blocks_per_seq, partition_size,
+                 stream):
+    _dev(out, "out")
+    _i32(context_lens, "context_lens")
+    _dev(workspace, "workspace")
+    if out.dtype not in _KV_DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _same_device(out, context_lens, workspace)
+    B, H, D = out.shape
+    args = (_ptr(out), _ptr(context_lens), B, H, D, int(block_size), int(max_blocks_per_seq),
+            int(partition_size), _KV_DTYPES[out.dtype], _ptr(workspace),
+            workspace.numel() * workspace.element_size(),
+            stream if stream is not None else _stream(out))
+    return "pkv_paged_attention_reduce", args
 
 
 def paged_attention_reduce(out: torch.Tensor, context_lens: torch.Tensor, workspace: torch.Tensor,
                            block_size: int, max_blocks_per_seq: int,
                            partition_size: int = 0) -> torch.Tensor:
     """Stage 3 of paged_attention_decode: merge the partition records into ``out``."""
-    _dev(out, "out")
-    _i32(context_lens, "context_lens")
-    _dev(workspace, "workspace")
-    if out.dtype not in _KV_DTYPES:
-        raise TypeError("out must be float32 or bfloat16")
-    B, H, D = out.shape
-    lib = _lib.load_library()
-    st = lib.pkv_paged_attention_reduce(
-        _ptr(out), _ptr(context_lens), B, H, D, int(block_size), int(max_blocks_per_seq),
-        int(partition_size), _KV_DTYPES[out.dtype], _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(out))
-    _lib.check(st, "pkv_paged_attention_reduce")
+    _call(*_reduce_args(out, context_lens, workspace, block_size, max_blocks_per_seq,
+                        partition_size, None))
     return out
 
 
@@ -374,12 +397,8 @@ def kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.
     _lib.check(st, "pkv_kv_cache_write_fp8")
 
 
-def decode_prologue_fp8(block_tables: torch.Tensor, context_lens: torch.Tensor,
-                        key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
-                        value_cache: torch.Tensor, workspace: torch.Tensor, k_scale: float,
-                        v_scale: float, slot_mapping: Optional[torch.Tensor] = None
-                        ) -> torch.Tensor:
-    """decode_prologue for E4M3 caches (balanced-split plan); returns the slots."""
+def _prologue_fp8_args(block_tables, context_lens, key, value, key_cache, value_cache,
+                       workspace, k_scale, v_scale, slot_mapping, stream):
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
     dt = _kv(key, "key")
@@ -397,13 +416,24 @@ def decode_prologue_fp8(block_tables: torch.Tensor, context_lens: torch.Tensor,
     _i32(slot_mapping, "slot_mapping")
     _same_device(block_tables, context_lens, key, value, key_cache, value_cache, workspace,
                  slot_mapping)
-    lib = _lib.load_library()
-    st = lib.pkv_decode_prologue_fp8(_ptr(block_tables), _ptr(context_lens), _ptr(key),
-                                     _ptr(value), _ptr(key_cache), _ptr(value_cache),
-                                     _ptr(slot_mapping), B, block_tables.shape[1], Hkv, D, BS, NB,
-                                     dt, float(k_scale), float(v_scale), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(key))
-    _lib.check(st, "pkv_decode_prologue_fp8")
+    args = (_ptr(block_tables), _ptr(context_lens), _ptr(key), _ptr(value), _ptr(key_cache),
+            _ptr(value_cache), _ptr(slot_mapping), B, block_tables.shape[1], Hkv, D, BS, NB, dt,
+            float(k_scale), float(v_scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(),
+            stream if stream is not None else _stream(key))
+    return "pkv_decode_prologue_fp8", args, slot_mapping
+
+
+def decode_prologue_fp8(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, workspace: torch.Tensor, k_scale: float,
+                        v_scale: float, slot_mapping: Optional[torch.Tensor] = None
+                        ) -> torch.Tensor:
+    """decode_prologue for E4M3 caches (balanced-split plan); returns the slots."""
+    name, args, slot_mapping = _prologue_fp8_args(block_tables, context_lens, key, value,
+                                                  key_cache, value_cache, workspace, k_scale,
+                                                  v_scale, slot_mapping, None)
+    _call(name, args)
     return slot_mapping
 
 
@@ -451,20 +481,99 @@ def paged_attention_decode_fp8(query: torch.Tensor, key_cache: torch.Tensor,
     return out
 
 
+def _partition_fp8_args(query, key_cache, value_cache, block_tables, context_lens, scale,
+                        k_scale, v_scale, out, out_dtype, workspace, stream):
+    out, ws, wsb, B, H, Hkv, D, BS, NB = _fp8_attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace)
+    args = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+            float(k_scale), float(v_scale), _KV_DTYPES[out.dtype], _ptr(ws), wsb,
+            stream if stream is not None else _stream(query))
+    return "pkv_paged_attention_partition_fp8", args, out, ws
+
+
 def paged_attention_partition_fp8(query, key_cache, value_cache, block_tables, context_lens,
                                   scale, k_scale, v_scale, out=None, out_dtype=torch.float32,
                                   workspace=None):
     """Stage 2 over E4M3 caches (needs a balanced plan in ``workspace``); returns
     (out, workspace)."""
-    out, ws, wsb, B, H, Hkv, D, BS, NB = _fp8_attention_args(
-        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace)
-    lib = _lib.load_library()
-    st = lib.pkv_paged_attention_partition_fp8(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
-        float(k_scale), float(v_scale), _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
-    _lib.check(st, "pkv_paged_attention_partition_fp8")
+    name, args, out, ws = _partition_fp8_args(query, key_cache, value_cache, block_tables,
+                                              context_lens, scale, k_scale, v_scale, out,
+                                              out_dtype, workspace, None)
+    _call(name, args)
     return out, ws
+
+
+class DecodeStep:
+    """One decode step bound to fixed tensors: slot mapping, cache write and plan
+    (``prologue``), the partition stage (``partition``) and the merge (``reduce``).
+
+    The arguments are checked once, here, and each stage is then a single C call with
+    the stored pointers and sizes, on the stream given (default: the current stream of
+    the query's device at construction).  The tensors' contents may change between
+    calls (new tokens, longer contexts, new block tables); their storage, shapes and
+    dtypes must not.  E4M3 caches (uint8 or float8_e4m3fn) take ``k_scale`` and
+    ``v_scale`` and always use the balanced split."""
+
+    def __init__(self, query, key, value, key_cache, value_cache, block_tables, context_lens,
+                 scale, partition_size=0, out=None, out_dtype=torch.float32, workspace=None,
+                 slot_mapping=None, k_scale=None, v_scale=None, stream=None):
+        _dev(query, "query")
+        fp8 = isinstance(key_cache, torch.Tensor) and key_cache.dtype in _FP8_DTYPES
+        if fp8 and (k_scale is None or v_scale is None):
+            raise ValueError("E4M3 caches need k_scale and v_scale")
+        if fp8 and partition_size != 0:
+            raise ValueError("E4M3 caches use the balanced split (partition_size 0)")
+        if stream is None:
+            stream = torch.cuda.current_stream(query.device)
+        st = ctypes.c_void_p(stream.cuda_stream)
+        BS = key_cache.shape[1]
+        if workspace is None:
+            workspace = alloc_workspace(query, block_tables, BS, partition_size)
+        if fp8:
+            self._prologue = _prologue_fp8_args(block_tables, context_lens, key, value,
+                                                key_cache, value_cache, workspace, k_scale,
+                                                v_scale, slot_mapping, st)
+            self._partition = _partition_fp8_args(query, key_cache, value_cache, block_tables,
+                                                  context_lens, scale, k_scale, v_scale, out,
+                                                  out_dtype, workspace, st)
+        else:
+            self._prologue = _prologue_args(block_tables, context_lens, key, value, key_cache,
+                                            value_cache, workspace, partition_size,
+                                            slot_mapping, st)
+            self._partition = _partition_args(query, key_cache, value_cache, block_tables,
+                                              context_lens, scale, partition_size, out,
+                                              out_dtype, workspace, st)
+        self.slot_mapping = self._prologue[2]
+        self.out, self.workspace = self._partition[2], self._partition[3]
+        self._reduce = _reduce_args(self.out, context_lens, workspace, BS, block_tables.shape[1],
+                                    partition_size, st)
+        lib = _lib.load_library()
+        self._fns = [(getattr(lib, c[0]), c[0], c[1])
+                     for c in (self._prologue, self._partition, self._reduce)]
+        # the tensors whose pointers the calls hold
+        self._keep = (query, key, value, key_cache, value_cache, block_tables, context_lens)
+
+    def _run(self, i: int) -> None:
+        fn, name, args = self._fns[i]
+        st = fn(*args)
+        if st:
+            _lib.check(st, name)
+
+    def prologue(self) -> None:
+        self._run(0)
+
+    def partition(self) -> None:
+        self._run(1)
+
+    def reduce(self) -> None:
+        self._run(2)
+
+    def __call__(self) -> torch.Tensor:
+        self._run(0)
+        self._run(1)
+        self._run(2)
+        return self.out
 
 
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,

@@ -190,6 +190,11 @@ def test_binding_fails_loudly_without_gpu_tensors():
     cl = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         pkv.slot_mapping(bt, cl, 16, 64)
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 2, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((64, 16, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.DecodeStep(q, kv, kv, kc, kc, bt, cl, 0.1)
 
 
 FP8 = _lib.PKV_FP8_E4M3

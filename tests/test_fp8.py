@@ -388,3 +388,21 @@ def test_gpu_fp8_copy_blocks_is_a_bit_copy():
     from oracle.block_pool import copy_blocks as ref_copy
     rk, rv = ref_copy(k0.cpu().numpy(), v0.cpu().numpy(), pairs.cpu().numpy())
     assert (kc.cpu().numpy() == rk).all() and (vc.cpu().numpy() == rv).all()
+
+
+@pytest.mark.gpu
+def test_gpu_fp8_prepared_step_equals_per_call_wrappers():
+    from workloads import build_fp8_batch
+    pkv = _gpu()
+    b = build_fp8_batch(_spec(NB=2048), [3, 513, 2000, 5000, 2], device="cuda")
+    s1, k1, v1, o1 = _step(pkv, b, fused=True)
+    kc, vc = b.key_cache.clone(), b.value_cache.clone()
+    bt, cl = _meta(b)
+    ks, vs = b.extra["k_scale"], b.extra["v_scale"]
+    ds = pkv.DecodeStep(b.query, b.key, b.value, kc, vc, bt, cl, b.scale, k_scale=ks, v_scale=vs)
+    o2 = ds()
+    torch.cuda.synchronize()
+    assert torch.equal(s1, ds.slot_mapping) and torch.equal(k1, kc) and torch.equal(v1, vc)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    with pytest.raises(ValueError):
+        pkv.DecodeStep(b.query, b.key, b.value, kc, vc, bt, cl, b.scale)

@@ -362,3 +362,32 @@ def test_prologue_equals_separate_calls(nseq):
     o2 = pkv.paged_attention_decode(b.query, kc2, vc2, bt, cl, b.scale, P)
     torch.cuda.synchronize()
     assert torch.equal(bits(o1), bits(o2))
+
+
+@pytest.mark.parametrize("P", [512, 0])
+def test_prepared_step_equals_per_call_wrappers(P):
+    """DecodeStep (arguments checked once, one C call per stage) gives the bits of the
+    per-call wrappers, also on a second call after the contexts changed in place."""
+    rng = np.random.default_rng(23 + P)
+    ctx = rng.integers(2, 3000, size=9)
+    ctx[:3] = [2, 16, 17]
+    b = build_batch(spec_of(NB=9 * 200 + 64), ctx, device="cuda")
+    bt, cl = device_meta(b)
+    NB, BS = b.key_cache.shape[:2]
+    kc1, vc1 = b.key_cache.clone(), b.value_cache.clone()
+    kc2, vc2 = b.key_cache.clone(), b.value_cache.clone()
+    ws1 = pkv.alloc_workspace(b.query, bt, BS, P)
+    ds = pkv.DecodeStep(b.query, b.key, b.value, kc2, vc2, bt, cl, b.scale, P)
+    for _ in range(2):
+        s1 = pkv.decode_prologue(bt, cl, b.key, b.value, kc1, vc1, ws1, P)
+        o1, _ = pkv.paged_attention_partition(b.query, kc1, vc1, bt, cl, b.scale, P,
+                                              workspace=ws1)
+        pkv.paged_attention_reduce(o1, cl, ws1, BS, bt.shape[1], P)
+        o2 = ds()
+        torch.cuda.synchronize()
+        assert torch.equal(s1, ds.slot_mapping)
+        assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+        assert torch.equal(bits(o1), bits(o2))
+        cl.sub_(1)   # the bound tensors' contents change between calls
+    with pytest.raises(ValueError):
+        pkv.DecodeStep(b.query, b.key[:4], b.value, kc2, vc2, bt, cl, b.scale, P)
