@@ -604,77 +604,95 @@ __global__ __launch_bounds__(NW * kWave) void paged_attention_multi_kernel(Atten
 }
 
 // ---- merge of the segments ----------------------------------------------------------
-// One wave per (new token, query head) row; lanes hold D / 16 output columns each
-// (4 for D = 64), read as float4.  Rows of invalid sequences get NaN.
+// One workgroup per new token.  The token's sequence, its unit and the shares that hold
+// the unit are found once per workgroup, with wave-uniform scalar loads; the threads
+// then cover the token's query heads, 256 / (D / 4) heads per pass, each lane a float4
+// of one head's output row, and fold the head's records in share order.  Rows of
+// invalid sequences get NaN; rows whose unit lies in one share were written by the
+// attention kernel.
 template <int D>
 __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(AttentionArgs a) {
-  constexpr int LPR = D / 4;             // lanes per record (float4 each)
-  constexpr int KGW = kWave / LPR;       // records per wave round
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  constexpr int LPR = D / 4;             // lanes per head row (float4 each)
+  constexpr int HPP = 256 / LPR;         // heads per pass
+  const int t = blockIdx.x;
   const int H = a.num_heads;
-  if (row >= (int64_t)a.num_tokens * H) return;
-  const int t = (int)(row / H);
-  const int h = (int)(row % H);
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
-  const int rows = a.unit_rows;
-  const int tpb = rows / G;
-  const int kg = lane / LPR;
-  const int lr = lane % LPR;
-  const int B = a.num_seqs;
-  const int i = owner_of(a.query_start_loc, B, t);
-  const int q0 = a.query_start_loc[i], q1 = a.query_start_loc[i + 1];
+  const int hl = threadIdx.x / LPR;
+  const int lr = threadIdx.x % LPR;
+  cint32* qsl = (cint32*)a.query_start_loc;
+  cint32* hdr = (cint32*)a.tile_hdr;
+  int lo = 0, hi = a.num_seqs;           // the sequence holding token t (qsl[0] <= t)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int i = lo;
+  const int q0 = qsl[i], q1 = qsl[i + 1];
   const int max_ctx = a.max_blocks_per_seq << a.block_shift;
-  const bool valid = a.tile_hdr[2] > 0 && t >= q0 && t < q1 &&
-                     seq_valid(q0, q1, a.context_lens[i], a.num_tokens, max_ctx);
+  const bool valid = hdr[2] > 0 && t >= q0 && t < q1 &&
+                     seq_valid(q0, q1, ((cint32*)a.context_lens)[i], a.num_tokens, max_ctx);
+  const int64_t row0 = (int64_t)t * H;
   if (!valid) {
-    if (kg == 0) {
-      const float nan = __builtin_nanf("");
-      store_row4(a, row * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
-    }
+    const float nan = __builtin_nanf("");
+    for (int h = hl; h < H; h += HPP)
+      store_row4(a, (row0 + h) * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
     return;
   }
+  const int rows = a.unit_rows;
+  const int tpb = rows / G;
   const int jq = t - q0;
-  const int u = a.seq_unit[i] + jq / tpb;
-  const int r = (jq % tpb) * G + h % G;
-  const int g = h / G;
-  const int c0 = a.tile_cum[u], c1 = a.tile_cum[u + 1];
-  const int total = a.tile_hdr[0];
-  const int nwg = a.tile_hdr[1];
+  const int u = ((cint32*)a.seq_unit)[i] + jq / tpb;
+  const int c0 = ((cint32*)a.tile_cum)[u], c1 = ((cint32*)a.tile_cum)[u + 1];
+  const int total = hdr[0];
+  const int nwg = hdr[1];
   const int w0 = share_of((int64_t)c0 + kSeqCost, nwg, total);
   const int w1 = share_of((int64_t)c1 - 1, nwg, total);
-  if (w0 == w1) return;                  // written by the attention kernel
-  // Records of segments in which this row saw no token have l = 0 (and m = -inf);
-  // they weigh nothing.
-  Running acc{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-  for (int ww = w0 + kg; ww <= w1; ww += KGW) {
-    if (!share_nonempty(ww, nwg, total)) continue;
-    const int64_t rec = (((int64_t)ww + u) * Hkv + g) * rows + r;
-    const float l = a.ws_l[rec];
-    if (!(l > 0.f) && !(l != l)) continue;   // empty segment (NaN l: keep, marks bad data)
-    Running s{a.ws_m[rec], l, reinterpret_cast<const float4*>(a.ws_o + rec * D)[lr]};
-    s.o.x *= l; s.o.y *= l; s.o.z *= l; s.o.w *= l;
-    merge_into(acc, s);
-  }
+  if (w0 == w1) return;
+  const int rq = (jq % tpb) * G;
+  // KH heads per thread at a time, so that each share's records of all of them are
+  // loaded before any is merged (one round trip per share, not one per head).  Heads
+  // past H load head H - 1's records and store nothing.
+  constexpr int KH = 4;
+  for (int hb = hl; hb < H; hb += KH * HPP) {
+    int64_t in_label[KH];   // record of head h under label L: (L * Hkv + h / G) * rows + rq + h % G
+    Running acc[KH];
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
-    Running s;
-    s.m = __shfl_xor(acc.m, off);
-    s.l = __shfl_xor(acc.l, off);
-    s.o.x = __shfl_xor(acc.o.x, off);
-    s.o.y = __shfl_xor(acc.o.y, off);
-    s.o.z = __shfl_xor(acc.o.z, off);
-    s.o.w = __shfl_xor(acc.o.w, off);
-    if (lane & off) { const Running tmp = acc; acc = s; s = tmp; }
-    merge_into(acc, s);
+    for (int k = 0; k < KH; ++k) {
+      const int h = min(hb + k * HPP, H - 1);
+      in_label[k] = (int64_t)(h / G) * rows + rq + h % G;
+      acc[k] = Running{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    }
+    for (int ww = w0; ww <= w1; ++ww) {
+      if (!share_nonempty(ww, nwg, total)) continue;
+      const int64_t lab = ((int64_t)ww + u) * Hkv * rows;
+      float l[KH], m[KH];
+      floatx4 o[KH];
+#pragma unroll
+      for (int k = 0; k < KH; ++k) {
+        const int64_t rec = lab + in_label[k];
+        l[k] = a.ws_l[rec];
+        m[k] = a.ws_m[rec];
+        o[k] = reinterpret_cast<const floatx4*>(a.ws_o + rec * D)[lr];
+      }
+      // Records of segments in which this row saw no token have l = 0 (and m = -inf);
+      // they weigh nothing.  A NaN l marks bad data and is kept.
+#pragma unroll
+      for (int k = 0; k < KH; ++k) {
+        if (!(l[k] > 0.f) && !(l[k] != l[k])) continue;
+        const Running sg{m[k], l[k], make_float4(o[k][0] * l[k], o[k][1] * l[k], o[k][2] * l[k],
+                                                 o[k][3] * l[k])};
+        merge_into(acc[k], sg);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+      if (hb + k * HPP < H) store_row4(a, (row0 + hb + k * HPP) * D + lr * 4, acc[k]);
   }
-  if (kg == 0) store_row4(a, row * D + lr * 4, acc);
 }
 
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.num_heads * a.num_tokens;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)a.num_tokens);
   if (a.head_dim == 64)
     hipLaunchKernelGGL(paged_attention_multi_reduce_kernel<64>, grid, dim3(256), 0, stream, a);
   else if (a.head_dim == 128)
