@@ -28,6 +28,9 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 VALU forms stay off; scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix instructions accumulate in ordinary VGPRs: with the accumulators in AGPRs,
+    # the multi-token kernels copied all of them to VGPRs and back on every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
