@@ -204,8 +204,21 @@ constexpr Cpol multi_kv_cpol() { return HW == NW ? Cpol::kStream : Cpol::kDefaul
 // staged rows and a unit is RB row blocks.  HW == 1 < NW: the waves share one kv
 // head's rows and each takes RB of the unit's NW * RB row blocks, so one pass over
 // the tiles serves NW * RB * 16 rows (long prompts).
+// Waves per SIMD the register budget must allow.  bf16 row mode: three (168
+// registers; the few values that no longer fit wait in scratch for the end of a
+// segment).  Measured on MI355X, 4 prompts' 512-token chunks: 617 us at two waves per
+// SIMD, 563 us at three, 1.32 ms at four (spills inside the tile loop).
+#ifndef PKV_MULTI_ROW_WPE
+#define PKV_MULTI_ROW_WPE 3
+#endif
+template <typename T, int D, int HW, int NW>
+constexpr int multi_wpe() {
+  return HW == 1 && NW > 1 && D == 128 && std::is_same<T, BF16>::value ? PKV_MULTI_ROW_WPE : 1;
+}
+
 template <typename T, int D, int G, int HW, int RB, int NW, int NBUF>
-__global__ __launch_bounds__(NW * kWave) void paged_attention_multi_kernel(AttentionArgs a) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(multi_wpe<T, D, HW, NW>())))
+void paged_attention_multi_kernel(AttentionArgs a) {
   constexpr int TOK = kTileTokens;
   constexpr bool kRowWaves = NW != HW;      // waves split the rows of one head
   static_assert(!kRowWaves || HW == 1, "row-split waves share a single head");
@@ -400,24 +413,30 @@ __global__ __launch_bounds__(NW * kWave) void paged_attention_multi_kernel(Atten
 #pragma unroll
     for (int c = 0; c < QKC; ++c)
       kk[c] = kb[col * St::kSlots + ((hw_idx * NCH + 4 * c + quarter) ^ St::swz(col))];
+    // A tile that ends at or before the first position any row of this wave sees
+    // needs no causal mask (a wave-uniform test).
+    const bool unmasked = tok0 + TOK - 1 <= uctx - uqlen + min(uj0 + row0 / G, uqlen - 1);
     float p[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const floatx4 s4 = tile_scores<T, QKC>(kk, qa[rb]);   // S^T: row col, tokens 4q + j
-      const int jrow = min(uj0 + (row0 + rb * 16 + col) / G, uqlen - 1);
-      const int prow = uctx - uqlen + jrow;                  // last position the row sees
       float sc[4];
-      float mx = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = tok0 + 4 * quarter + j;
-        sc[j] = t <= prow ? s4[j] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, sc[j]);
+      for (int j = 0; j < 4; ++j) sc[j] = s4[j] * a.scale_log2;
+      if (!unmasked) {
+        keep_branch();
+        const int jrow = min(uj0 + (row0 + rb * 16 + col) / G, uqlen - 1);
+        const int prow = uctx - uqlen + jrow;                // last position the row sees
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (tok0 + 4 * quarter + j > prow) sc[j] = kNegInf;
       }
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool up = mx > m_run[rb] + kRebase;
       if (__ballot(up)) {
+        keep_branch();
         const float alpha = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
         m_run[rb] = up ? mx : m_run[rb];
         l_lane[rb] *= alpha;
@@ -445,29 +464,32 @@ __global__ __launch_bounds__(NW * kWave) void paged_attention_multi_kernel(Atten
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int vr = 4 * quarter + s;
-        const bool dead = !full && tok0 + vr >= uctx;   // rows past the context may hold NaN
         if constexpr (CPL == 8) {
           const uint4 c = vb[vr * St::kSlots + ((hw_idx * NCH + col) ^ St::swz(vr))];
-          w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
-          w[s][2] = dead ? 0u : c.z; w[s][3] = dead ? 0u : c.w;
+          w[s][0] = c.x; w[s][1] = c.y; w[s][2] = c.z; w[s][3] = c.w;
         } else {
           static_assert(CPL == 4, "value piece");
           const int slot = (hw_idx * NCH + (col >> 1)) ^ St::swz(vr);
           const uint2 c = reinterpret_cast<const uint2*>(vb)[2 * (vr * St::kSlots + slot) + (col & 1)];
-          w[s][0] = dead ? 0u : c.x; w[s][1] = dead ? 0u : c.y;
+          w[s][0] = c.x; w[s][1] = c.y;
         }
+      }
+      if (!full) {   // rows past the context may hold NaN
+        keep_branch();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (tok0 + 4 * quarter + s >= uctx)
+#pragma unroll
+            for (int d = 0; d < CPL / 2; ++d) w[s][d] = 0u;
       }
       uint2 bv[CPL];   // block e: column col * CPL + e of tokens 4q .. 4q + 3
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
+        // even e: the low bf16 of two rows' words, odd e: the high ones
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const int d = e >> 1;
-        if (e & 1) {
-          bv[e].x = (w[0][d] >> 16) | (w[1][d] & 0xffff0000u);
-          bv[e].y = (w[2][d] >> 16) | (w[3][d] & 0xffff0000u);
-        } else {
-          bv[e].x = (w[0][d] & 0xffffu) | (w[1][d] << 16);
-          bv[e].y = (w[2][d] & 0xffffu) | (w[3][d] << 16);
-        }
+        bv[e].x = __builtin_amdgcn_perm(w[1][d], w[0][d], sel);
+        bv[e].y = __builtin_amdgcn_perm(w[3][d], w[2][d], sel);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {

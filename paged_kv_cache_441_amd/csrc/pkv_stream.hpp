@@ -38,6 +38,11 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// An empty statement with side effects: the block holding it stays a real branch,
+// instead of being executed on every path and selected away (the compiler does that
+// to short blocks), for rare paths such as a rescale or a partial tile.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 // Waits until at most N of this wave's copies are outstanding; copies retire in
 // order, so every copy issued before the last N has landed in LDS.
 template <int N>
