@@ -432,8 +432,7 @@ void paged_attention_multi_kernel(AttentionArgs a) {
           if (tok0 + 4 * quarter + j > prow) sc[j] = kNegInf;
       }
       float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const bool up = mx > m_run[rb] + kRebase;
       if (__ballot(up)) {
         keep_branch();
@@ -547,8 +546,7 @@ void paged_attention_multi_kernel(AttentionArgs a) {
   auto finish = [&](bool whole) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float l_row = l_lane[rb] + __shfl_xor(l_lane[rb], 16);
-      l_row += __shfl_xor(l_row, 32);
+      const float l_row = sum_xor32(sum_xor16(l_lane[rb]));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = row0 + rb * 16 + 4 * quarter + j;

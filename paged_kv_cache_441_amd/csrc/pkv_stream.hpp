@@ -38,6 +38,26 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// Reductions of x over lanes l and l ^ 16, or l and l ^ 32, by gfx950's lane-row swaps
+// (no LDS round trip): swapping a register with itself hands each lane, in its two
+// results, its own value and its partner's, so max and sum need no select.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // An empty statement with side effects: the block holding it stays a real branch,
 // instead of being executed on every path and selected away (the compiler does that
 // to short blocks), for rare paths such as a rescale or a partial tile.
