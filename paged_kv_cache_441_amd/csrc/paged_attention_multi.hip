@@ -595,18 +595,19 @@ void paged_attention_multi_kernel(AttentionArgs a) {
   unit_info();
   load_query();
 
-  // Tile j sits in ring slot j % NBUF; the copies of tile j + NBUF - 1 are issued
-  // before tile j is waited for and computed.
+  // Tile j sits in ring slot j % NBUF.  Per step: wait for this wave's copies of tile
+  // j, one barrier (every wave's copies of tile j have landed, and every wave is done
+  // with tile j - 1), issue tile j + NBUF - 1 into the slot of tile j - 1, compute
+  // tile j.  One barrier per tile.
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i) issue(kring[i], vring[i]);
   for (int j = 0;; ++j) {
     if (cc.t >= cc.stop) break;
+    wait_copies<(NBUF - 2) * L>();
+    bare_barrier();
     const int fill = (j + NBUF - 1) % NBUF;
     issue(kring[fill], vring[fill]);
-    wait_copies<(NBUF - 1) * L>();
-    bare_barrier();
     compute(kring[j % NBUF], vring[j % NBUF], (bad_pipe >> (NBUF - 1)) & 1u);
-    bare_barrier();
     if (cc.t == cc.stop - 1) {
       finish(seg_from_zero && cc.stop == cc.nt);
       reset();
