@@ -100,6 +100,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   constexpr int RPS = kWave / NPC;          // value rows per wave read
   constexpr int STEPS = TOK / RPS;
   constexpr int kQuarters = (G + 3) / 4;    // MFMA output quarters holding real heads
+  // P.V on bf16 matrix instructions (bf16 and E4M3 caches, D = 128); fp32 caches and
+  // D = 64 use fp32 FMAs on the VALU
+  constexpr bool kMfmaPV = (kF8 || std::is_same<T, BF16>::value) && D == 128;
   static_assert(NCH % 4 == 0 || kF8, "row shape");
   constexpr int L = 2 * St::kCopies;        // copy instructions per wave per tile
   constexpr int NS = St::kTileSlots;
@@ -111,7 +114,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   __shared__ uint4 kb0[NS], vb0[NS], kb1[NS], vb1[NS];
   __shared__ uint4 kb2[NBUF > 2 ? NS : 1], vb2[NBUF > 2 ? NS : 1];
   __shared__ uint4 kb3[NBUF > 3 ? NS : 1], vb3[NBUF > 3 ? NS : 1];
-  __shared__ float p_lds[HW][16][G];
+  // probabilities of the tile: [token][head], or [head][token] for the matrix P.V
+  __shared__ float p_lds[HW][kMfmaPV ? G : 16][kMfmaPV ? 16 : G];
   // the query rows of each wave's GQA group, copied in like the tiles
   constexpr int QB = G * D * QEB;
   __shared__ uint4 q_lds[HW][QB / 16];
@@ -287,13 +291,22 @@ void paged_attention_stream_kernel(AttentionArgs a) {
 
   float m_run[G];
   float acc[G][EPL];
+  // matrix P.V: acc8[e] holds head 4 quarter + j (rows past G are padding), value
+  // column col * 8 + e
+  floatx4 acc8[8];
   float l_lane[4];
   auto reset = [&]() {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m_run[h] = kNegInf;
+      if constexpr (!kMfmaPV) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+      }
+    }
+    if constexpr (kMfmaPV) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc8[e] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) l_lane[j] = 0.f;
@@ -309,6 +322,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     constexpr float kRebase = 8.f;
     const int tok0 = cc.t * TOK;
     const int ntok = min(TOK, cctx - tok0);
+    const bool full = ntok == TOK;
     seg_bad |= bad;
     // key operand: this lane's column is token kr of the tile (columns past TOK
     // repeat rows; they are masked out below)
@@ -363,18 +377,77 @@ void paged_attention_stream_kernel(AttentionArgs a) {
       l_lane[j] = rebase ? l_lane[j] * arow + sc[j] : l_lane[j] + sc[j];
     }
     if (rebase) {
+      if constexpr (kMfmaPV) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int j = 0; j < 4; ++j) {
+          const float aj = (G > 4 && quarter == 1) ? alpha[(4 + j) % G] : alpha[j % G];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+          for (int e = 0; e < 8; ++e) acc8[e][j] *= aj;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+      }
     }
     if (quarter < kQuarters) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (4 * quarter + j < G) p_lds[wave][col][(4 * quarter + j) % G] = sc[j];
+        if (4 * quarter + j < G) {
+          if constexpr (kMfmaPV)
+            p_lds[wave][(4 * quarter + j) % G][col] = sc[j];
+          else
+            p_lds[wave][col][(4 * quarter + j) % G] = sc[j];
+        }
     }
     __builtin_amdgcn_wave_barrier();
-    const bool full = ntok == TOK;
+    if constexpr (kMfmaPV) {
+      // P.V on 16x16x16 bf16 matrix instructions.  A: P with the wave's heads as rows
+      // (row col, real for col < G) and tokens 4 quarter .. 4 quarter + 3 as k; B: the
+      // same tokens' value columns col * 8 + e for output block e, packed from four
+      // token rows (a column permutation, undone at the store).  P is split into hi +
+      // lo bf16 terms, together exact to about 2^-17 of p; E4M3 values are exact in
+      // bf16.
+      floatx4 pa = {0.f, 0.f, 0.f, 0.f};
+      if (col < G) pa = *reinterpret_cast<const floatx4*>(&p_lds[wave][col % G][4 * quarter]);
+      const floatx2 p01 = {pa[0], pa[1]}, p23 = {pa[2], pa[3]};
+      const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
+      const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
+      const bf16x2 l01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, floatx2), bf16x2);
+      const bf16x2 l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, floatx2), bf16x2);
+      const bf16x4 ahi = {h01[0], h01[1], h23[0], h23[1]};
+      const bf16x4 alo = {l01[0], l01[1], l23[0], l23[1]};
+      uint32_t wv[4][4];   // token 4 quarter + s: value columns col * 8 .. col * 8 + 7
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int n = 4 * quarter + s;
+        const bool dead = !full && n >= ntok;   // rows past the context may hold NaN
+        if constexpr (kF8) {
+          const int slot = (wave * NCH + (col >> 1)) ^ St::swz(n);
+          const uint2 c8 = reinterpret_cast<const uint2*>(vb)[2 * (n * St::kSlots + slot) + (col & 1)];
+          const uint2 b0 = e4m3x4_to_bf16(dead ? 0u : c8.x), b1 = e4m3x4_to_bf16(dead ? 0u : c8.y);
+          wv[s][0] = b0.x; wv[s][1] = b0.y; wv[s][2] = b1.x; wv[s][3] = b1.y;
+        } else {
+          const uint4 c = vb[n * St::kSlots + ((wave * NCH + col) ^ St::swz(n))];
+          wv[s][0] = dead ? 0u : c.x; wv[s][1] = dead ? 0u : c.y;
+          wv[s][2] = dead ? 0u : c.z; wv[s][3] = dead ? 0u : c.w;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // column col * 8 + e: the low bf16 of word e / 2 for even e, else the high
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint2 bq;
+        bq.x = __builtin_amdgcn_perm(wv[1][e >> 1], wv[0][e >> 1], sel);
+        bq.y = __builtin_amdgcn_perm(wv[3][e >> 1], wv[2][e >> 1], sel);
+        const bf16x4 b = __builtin_bit_cast(bf16x4, bq);
+        acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc8[e], 0, 0, 0);
+        acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc8[e], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       const int n = s * RPS + rg;
@@ -405,6 +478,50 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   // End of a segment: fold the row groups, normalise, store (the output itself for
   // a whole sequence, else the record under label w + sequence), 16 bytes at a time.
   auto finish = [&](bool whole) {
+    if constexpr (kMfmaPV) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) l_lane[j] = row16_sum(l_lane[j]);
+      float l_head[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) l_head[h] = readlane(l_lane[h & 3], 16 * (h >> 2));
+      if (quarter >= kQuarters) return;   // padding rows
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * quarter + j;
+        if (h >= G) continue;
+        const float lh = (G > 4 && quarter == 1) ? l_head[(4 + j) % G] : l_head[j % G];
+        const float mh = (G > 4 && quarter == 1) ? m_run[(4 + j) % G] : m_run[j % G];
+        const float inv = (kF8 ? a.v_scale : 1.f) / lh;
+        float res[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = seg_bad ? __builtin_nanf("") : acc8[e][j] * inv;
+        if (whole) {
+          const int64_t orow = ((int64_t)cc.s * H + g * G + h) * D + col * 8;
+          if (a.out_bf16) {
+            uint4 v;
+            v.x = f32_to_bf16_rne(res[0]) | (uint32_t)f32_to_bf16_rne(res[1]) << 16;
+            v.y = f32_to_bf16_rne(res[2]) | (uint32_t)f32_to_bf16_rne(res[3]) << 16;
+            v.z = f32_to_bf16_rne(res[4]) | (uint32_t)f32_to_bf16_rne(res[5]) << 16;
+            v.w = f32_to_bf16_rne(res[6]) | (uint32_t)f32_to_bf16_rne(res[7]) << 16;
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = v;
+          } else {
+            float* o = static_cast<float*>(a.out) + orow;
+            *reinterpret_cast<float4*>(o) = make_float4(res[0], res[1], res[2], res[3]);
+            *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
+          }
+        } else {
+          const int64_t rec = ((int64_t)w + cc.s) * H + g * G + h;
+          float* o = a.ws_o + rec * D + col * 8;
+          *reinterpret_cast<float4*>(o) = make_float4(res[0], res[1], res[2], res[3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
+          if (col == 0) {
+            a.ws_m[rec] = mh;
+            a.ws_l[rec] = lh;
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int off = NPC; off < kWave; off <<= 1)
 #pragma unroll
