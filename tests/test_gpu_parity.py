@@ -285,23 +285,50 @@ def test_balanced_split_edge_batches(ctx):
     assert np.isfinite(out.cpu().numpy()).all()
 
 
-def test_one_plan_serves_every_layer():
-    b = build_batch(spec_of(NB=2048), [5, 700, 1600, 4000], device="cuda")
+@pytest.mark.parametrize("P", [512, 0])
+def test_one_plan_serves_every_layer(P):
+    # one plan, then the partition and reduce stages once per layer, with new cache
+    # contents each time
+    b = build_batch(spec_of(NB=2048), [5, 700, 1600, 4000, 9, 2500], device="cuda")
     bt, cl = device_meta(b)
-    ws = pkv.alloc_workspace(b.query, bt, 16, 512)
-    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], 512)
-    for layer in range(2):
+    ws = pkv.alloc_workspace(b.query, bt, 16, P)
+    pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], P)
+    for layer in range(3):
         kc = b.key_cache.clone()
         vc = b.value_cache.clone()
-        if layer:
+        if layer == 1:
             kc.copy_(kc.flip(0))
             vc.copy_(vc.flip(-1))
-        ref = pkv.paged_attention_decode(b.query, kc, vc, bt, cl, b.scale, 512)
-        out, _ = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, 512,
+        if layer == 2:
+            vc.mul_(-0.5)
+        ref = pkv.paged_attention_decode(b.query, kc, vc, bt, cl, b.scale, P)
+        out, _ = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P,
                                                workspace=ws)
-        pkv.paged_attention_reduce(out, cl, ws, 16, bt.shape[1], 512)
+        pkv.paged_attention_reduce(out, cl, ws, 16, bt.shape[1], P)
         torch.cuda.synchronize()
         assert torch.equal(bits(out), bits(ref))
+
+
+@pytest.mark.parametrize("ctx", [
+    [100, 3, 50],                 # fewer list positions than workgroups: empty shares
+    [1],                          # a single token
+    [40, 0, 70, 9000, -3],        # invalid lengths among split sequences
+])
+def test_balanced_small_batches_and_empty_shares(ctx):
+    b = build_batch(spec_of(NB=2048), [max(c, 1) for c in ctx], device="cuda")
+    bt, cl = device_meta(b)
+    _, kc, vc, _ = run_step(b, partition_size=0)
+    cl_in = torch.as_tensor(np.array(ctx, np.int32), device="cuda")
+    out = pkv.paged_attention_decode(b.query, kc, vc, bt, cl_in, b.scale, 0)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    good = [i for i, c in enumerate(ctx) if c >= 1]
+    bad = [i for i, c in enumerate(ctx) if c < 1]
+    ref = oracle_outputs(b, good)
+    assert max_err(out, ref, good) <= ATOL
+    if bad:
+        assert np.isnan(o[bad]).all()
+    assert np.isfinite(o[good]).all()
 
 
 def _plan_bytes(ws):
