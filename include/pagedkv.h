@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, inconsistent shapes */
-  PKV_ERR_UNSUPPORTED = 2,  /* a valid combination this build has no kernel for */
+  PKV_ERR_UNSUPPORTED = 2,  /* a valid combination the library has no kernel for */
   PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   PKV_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
   PKV_ERR_NO_BLOCKS = 5     /* the block pool has no free block left */
