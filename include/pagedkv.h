@@ -13,7 +13,8 @@
  *
  * Two ways to split the contexts, chosen by partition_size:
  *  - partition_size P > 0 (fixed partitions): sequence i is cut into partitions of
- *    P tokens; one workgroup per (partition, kv head); longest partitions first.
+ *    P tokens; one workgroup per (sequence, partition) and group of kv heads, which
+ *    streams whole token rows of its heads through LDS; longest partitions first.
  *  - partition_size 0 (balanced split): the (sequence, 16-token tile) pairs of the
  *    whole batch, plus one position per sequence for its fixed cost, form one list
  *    that is cut into equal contiguous shares, one per workgroup of a grid the GPU

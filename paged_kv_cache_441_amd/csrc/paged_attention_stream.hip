@@ -82,9 +82,21 @@ constexpr int stream_nbuf() { return T::kElemBytes == 1 ? PKV_STREAM_NBUF_FP8 : 
 template <typename T, int G>
 constexpr int stream_wpe() { return T::kElemBytes == 1 && G <= 4 ? PKV_STREAM_WPE_FP8 : 1; }
 
-template <typename T, int D, int G, int HW, int NBUF>
+// Cache policy of the KV tile copies in fixed-partition mode (1: non-temporal, as in the
+// balanced split).
+#ifndef PKV_STREAM_FIXED_NT
+#define PKV_STREAM_FIXED_NT 1
+#endif
+
+// FIXED: fixed partitions of a.partition_size tokens instead of the balanced split.
+// Workgroup w then takes work item w of the fixed plan (sequence, partition, context
+// length, partitions), streams that partition's tiles in the same way, and writes the
+// output (a sequence of one partition) or the partition's record in the layout the
+// fixed-partition merge reads: (sequence * H + head) * max_parts + partition.
+template <typename T, int D, int G, int HW, int NBUF, bool FIXED>
 __global__ __launch_bounds__(HW * kWave) __attribute__((amdgpu_waves_per_eu(stream_wpe<T, G>())))
 void paged_attention_stream_kernel(AttentionArgs a) {
+  constexpr Cpol kPol = FIXED && !PKV_STREAM_FIXED_NT ? Cpol::kDefault : kKvCpol;
   constexpr int TOK = kTileTokens;
   using St = Stage<T, D, HW, TOK>;
   constexpr bool kF8 = T::kElemBytes == 1;  // E4M3 caches, bfloat16 queries
@@ -132,26 +144,49 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   cint32* cum = (cint32*)a.tile_cum;
   cint32* ctx_of = (cint32*)a.context_lens;
   cint32* tables = (cint32*)a.block_tables;
-  const int total = ((cint32*)a.tile_hdr)[0];
-  if (w == 0 && hg == 0 && threadIdx.x == 0) a.tile_hdr[1] = nwg;   // for the merge
-  const int64_t start = (int64_t)w * total / nwg;
-  const int64_t end = (int64_t)(w + 1) * total / nwg;
-  if (start >= end) return;
+  int64_t start = 0, end = 0;
+  int seq0 = 0;
+  int fx_p = 0, fx_ctx = 0;   // fixed partitions: the item's partition and context length
+  if constexpr (FIXED) {
+    // Items are checked, so that a stale plan gives wrong numbers but never an
+    // out-of-range access.
+    cint32* items = (cint32*)a.plan_items;
+    const int count = min(((cint32*)a.plan_count)[0], B * a.max_parts);
+    if (w >= count) return;
+    seq0 = items[4 * w];
+    fx_p = items[4 * w + 1];
+    fx_ctx = items[4 * w + 2];
+    if (seq0 < 0 || seq0 >= B || fx_p < 0 || fx_p >= a.max_parts) return;
+    if (fx_ctx < 1 || fx_ctx > (a.max_blocks_per_seq << a.block_shift)) {
+      // invalid context length: NaN rows, written by the item of partition 0
+      if (fx_p == 0)
+        for (int i = lane; i < G * D; i += kWave)
+          store_out(a.out, ((int64_t)seq0 * H + g * G) * D + i, __builtin_nanf(""), a.out_bf16);
+      return;
+    }
+    if ((int64_t)fx_p * a.partition_size >= fx_ctx) return;
+  } else {
+    const int total = ((cint32*)a.tile_hdr)[0];
+    if (w == 0 && hg == 0 && threadIdx.x == 0) a.tile_hdr[1] = nwg;   // for the merge
+    start = (int64_t)w * total / nwg;
+    end = (int64_t)(w + 1) * total / nwg;
+    if (start >= end) return;
 
-  // The sequence holding position `start`: the last i in [0, B] with cum[i] <=
-  // start (sequences without tiles share their cum value with the next one).  A
-  // 64-way search, one vector load per round.
-  int lo = 0, len = B + 1;
-  while (len > 1) {
-    const int step = (len + kWave - 1) / kWave;
-    const int i = lo + lane * step;
-    const bool ok = i < lo + len && a.tile_cum[i] <= start;
-    const int k = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
-    const int nlo = lo + (k - 1) * step;
-    len = min(step, lo + len - nlo);
-    lo = nlo;
+    // The sequence holding position `start`: the last i in [0, B] with cum[i] <=
+    // start (sequences without tiles share their cum value with the next one).  A
+    // 64-way search, one vector load per round.
+    int lo = 0, len = B + 1;
+    while (len > 1) {
+      const int step = (len + kWave - 1) / kWave;
+      const int i = lo + lane * step;
+      const bool ok = i < lo + len && a.tile_cum[i] <= start;
+      const int k = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
+      const int nlo = lo + (k - 1) * step;
+      len = min(step, lo + len - nlo);
+      lo = nlo;
+    }
+    seq0 = lo;
   }
-  const int seq0 = lo;
 
   const int quarter = lane >> 4;   // MFMA operand k-group / output row group
   const int col = lane & 15;       // MFMA A row (head) and B column (token)
@@ -190,6 +225,11 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   // The cursor is wave-uniform; readfirstlane keeps it in scalar registers, so the
   // plan is read with scalar loads whose waits leave the copies in flight alone.
   auto next_seq = [&](Cursor& c) {
+    if constexpr (FIXED) {   // one partition per workgroup
+      c.s = B;
+      c.t = c.stop = 0;
+      return;
+    }
     int s = uniform(c.s);
     int cs = cum[s + 1];
     for (;;) {
@@ -211,6 +251,14 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     }
   };
   auto first_cursor = [&](Cursor& c) {
+    if constexpr (FIXED) {
+      const int tp = a.partition_size / TOK;   // a multiple of 16 tokens
+      c.s = seq0;
+      c.nt = uniform((fx_ctx + TOK - 1) / TOK);
+      c.t = uniform(fx_p * tp);
+      c.stop = uniform(min(c.nt, c.t + tp));
+      return;
+    }
     const int cs = cum[seq0];
     c.s = seq0;
     c.nt = uniform(cum[seq0 + 1] - cs - kSeqCost);
@@ -250,9 +298,9 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     const char* kbase = kcache + base;
     const char* vbase = vcache + base;
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16<kKvCpol>(kbase, copy_off[i], kd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16<kPol>(kbase, copy_off[i], kd + i * HW * 1024);
 #pragma unroll
-    for (int i = 0; i < St::kCopies; ++i) dma16<kKvCpol>(vbase, copy_off[i], vd + i * HW * 1024);
+    for (int i = 0; i < St::kCopies; ++i) dma16<kPol>(vbase, copy_off[i], vd + i * HW * 1024);
   };
 
   // ---- compute side ------------------------------------------------------------------
@@ -475,8 +523,17 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
+  // The record of head h of this wave's group for the current segment: label
+  // w + sequence in the balanced split, the fixed plan's layout with fixed partitions.
+  auto rec_of = [&](int h) -> int64_t {
+    if constexpr (FIXED)
+      return ((int64_t)cc.s * H + g * G + h) * a.max_parts + fx_p;
+    else
+      return ((int64_t)w + cc.s) * H + g * G + h;
+  };
+
   // End of a segment: fold the row groups, normalise, store (the output itself for
-  // a whole sequence, else the record under label w + sequence), 16 bytes at a time.
+  // a whole sequence, else the segment's record), 16 bytes at a time.
   auto finish = [&](bool whole) {
     if constexpr (kMfmaPV) {
 #pragma unroll
@@ -510,7 +567,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
             *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
           }
         } else {
-          const int64_t rec = ((int64_t)w + cc.s) * H + g * G + h;
+          const int64_t rec = rec_of(h);
           float* o = a.ws_o + rec * D + col * 8;
           *reinterpret_cast<float4*>(o) = make_float4(res[0], res[1], res[2], res[3]);
           *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
@@ -564,14 +621,14 @@ void paged_attention_stream_kernel(AttentionArgs a) {
                 make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
       }
     } else {
-      const int64_t rec0 = ((int64_t)w + cc.s) * H + g * G;
-      float* o = a.ws_o + rec0 * D + li * EPL;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h) {
+        float* o = a.ws_o + rec_of(h) * D + li * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<float4*>(o + h * D + e) =
+          *reinterpret_cast<float4*>(o + e) =
               make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
+      }
       if (lane < G) {
         // lane h < G writes head h's (m, l); m_run and l_head are uniform
         float mh = m_run[0], lh = l_head[0];
@@ -580,8 +637,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
           mh = lane == h ? m_run[h] : mh;
           lh = lane == h ? l_head[h] : lh;
         }
-        a.ws_m[rec0 + lane] = mh;
-        a.ws_l[rec0 + lane] = lh;
+        a.ws_m[rec_of(lane)] = mh;
+        a.ws_l[rec_of(lane)] = lh;
       }
     }
   };
@@ -756,9 +813,16 @@ hipError_t launch_attention_stream_reduce(const AttentionArgs& a, hipStream_t st
 
 // ---- dispatch ------------------------------------------------------------------
 
-template <typename T, int D, int G, int HW>
+template <typename T, int D, int G, int HW, bool FIXED>
 static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream) {
-  auto kernel = paged_attention_stream_kernel<T, D, G, HW, stream_nbuf<T>()>;
+  auto kernel = paged_attention_stream_kernel<T, D, G, HW, stream_nbuf<T>(), FIXED>;
+  const int hgroups = a.num_kv_heads / HW;
+  if constexpr (FIXED) {
+    // one workgroup per possible plan item; those past the plan's count exit at once
+    const int64_t items = (int64_t)a.num_seqs * a.max_parts;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)items, hgroups), dim3(HW * kWave), 0, stream, a);
+    return hipGetLastError();
+  }
   // Workgroups one compute unit holds at once, from the kernel's own resource use.
   static const int per_cu = [&] {
     int n = 0;
@@ -768,7 +832,6 @@ static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream
   }();
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
-  const int hgroups = a.num_kv_heads / HW;
   const int nwg = max(1, min(kMaxStreamWgs, per_cu * cus / hgroups));
   hipLaunchKernelGGL(kernel, dim3(nwg, hgroups), dim3(HW * kWave), 0, stream, a);
   return hipGetLastError();
@@ -781,28 +844,28 @@ static hipError_t launch_stream_shape(const AttentionArgs& a, hipStream_t stream
 // Heads per workgroup: the largest of 8, 4, 2, 1 that divides the kv heads and keeps
 // a token row of the group within PKV_STREAM_MAX_ROW bytes (and at 128 bytes or
 // more: 64-element E4M3 heads pair up).
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool FIXED>
 static hipError_t launch_stream_hw(const AttentionArgs& a, hipStream_t stream) {
   constexpr int kRow = D * T::kElemBytes;
   if constexpr (8 * kRow <= PKV_STREAM_MAX_ROW)
-    if (a.num_kv_heads % 8 == 0) return launch_stream_shape<T, D, G, 8>(a, stream);
+    if (a.num_kv_heads % 8 == 0) return launch_stream_shape<T, D, G, 8, FIXED>(a, stream);
   if constexpr (4 * kRow <= PKV_STREAM_MAX_ROW)
-    if (a.num_kv_heads % 4 == 0) return launch_stream_shape<T, D, G, 4>(a, stream);
+    if (a.num_kv_heads % 4 == 0) return launch_stream_shape<T, D, G, 4, FIXED>(a, stream);
   // a tile row spans at least 128 bytes
-  if (a.num_kv_heads % 2 == 0) return launch_stream_shape<T, D, G, 2>(a, stream);
+  if (a.num_kv_heads % 2 == 0) return launch_stream_shape<T, D, G, 2, FIXED>(a, stream);
   if constexpr (kRow >= 128)
-    return launch_stream_shape<T, D, G, 1>(a, stream);
+    return launch_stream_shape<T, D, G, 1, FIXED>(a, stream);
   else
     return hipErrorInvalidValue;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FIXED = false>
 static hipError_t launch_stream_g(const AttentionArgs& a, hipStream_t stream) {
   switch (a.num_heads / a.num_kv_heads) {
-    case 1: return launch_stream_hw<T, D, 1>(a, stream);
-    case 2: return launch_stream_hw<T, D, 2>(a, stream);
-    case 4: return launch_stream_hw<T, D, 4>(a, stream);
-    case 8: return launch_stream_hw<T, D, 8>(a, stream);
+    case 1: return launch_stream_hw<T, D, 1, FIXED>(a, stream);
+    case 2: return launch_stream_hw<T, D, 2, FIXED>(a, stream);
+    case 4: return launch_stream_hw<T, D, 4, FIXED>(a, stream);
+    case 8: return launch_stream_hw<T, D, 8, FIXED>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -817,6 +880,17 @@ hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream) {
   } else {
     if (a.head_dim == 64) return launch_stream_g<F32, 64>(a, stream);
     if (a.head_dim == 128) return launch_stream_g<F32, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_stream_fixed(const AttentionArgs& a, hipStream_t stream) {
+  if (a.kv_bf16) {
+    if (a.head_dim == 64) return launch_stream_g<BF16, 64, true>(a, stream);
+    if (a.head_dim == 128) return launch_stream_g<BF16, 128, true>(a, stream);
+  } else if (!a.kv_fp8) {
+    if (a.head_dim == 64) return launch_stream_g<F32, 64, true>(a, stream);
+    if (a.head_dim == 128) return launch_stream_g<F32, 128, true>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -117,6 +117,8 @@ hipError_t launch_attention_partition(const AttentionArgs& a, hipStream_t stream
 // staged through LDS, equal shares of the tile list per workgroup) and its merge.
 hipError_t launch_tile_plan(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_stream(const AttentionArgs& a, hipStream_t stream);
+// Fixed partitions through the streaming kernel: one workgroup per plan item.
+hipError_t launch_attention_stream_fixed(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_stream_reduce(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_reduce(const AttentionArgs& a, hipStream_t stream);
 
