@@ -570,18 +570,24 @@ void paged_attention_multi_kernel(AttentionArgs a) {
               *reinterpret_cast<uint2*>(dst + e) = v;
             }
           } else {
+            // non-temporal: the next tile's wait also waits for these stores, and they
+            // complete sooner when streamed past the caches (5 speculated tokens per
+            // sequence, Llama-3-8B-shaped batch: 344 -> 332 us per call on MI355X)
             float* dst = static_cast<float*>(a.out) + orow;
 #pragma unroll
-            for (int e = 0; e < CPL; e += 4)
-              *reinterpret_cast<float4*>(dst + e) =
-                  make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+            for (int e = 0; e < CPL; e += 4) {
+              const floatx4 v = {o[e], o[e + 1], o[e + 2], o[e + 3]};
+              __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(dst + e));
+            }
           }
         } else {
           const int64_t rec = (((int64_t)w + cc.u) * Hkv + g) * ROWS + r;
           float* dst = a.ws_o + rec * D + col * CPL;
 #pragma unroll
-          for (int e = 0; e < CPL; e += 4)
-            *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+          for (int e = 0; e < CPL; e += 4) {
+            const floatx4 v = {o[e], o[e + 1], o[e + 2], o[e + 3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(dst + e));
+          }
           if (col == 0) {
             a.ws_m[rec] = mr;
             a.ws_l[rec] = seg_bad ? __builtin_nanf("") : lr;
