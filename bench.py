@@ -282,7 +282,9 @@ def main(argv=None) -> int:
     timer.close()
 
     kv_bytes = b.kv_bytes()
-    kernel = "paged_attention_stream" if P == 0 else "paged_attention_partition"
+    # fixed partitions run in the same streaming kernel (one workgroup per partition);
+    # stored traffic counters exist for the balanced split only
+    kernel = "paged_attention_stream"
     tokens = int(b.context_lens.astype(np.int64).sum())
     step_s = ms_step / 1e3
     kv_gbs_step = kv_bytes / step_s / 1e9
@@ -328,7 +330,7 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{kernel}_kernel",
+            "kernel": f"{kernel}_kernel" + (f" (fixed {P}-token partitions)" if P else ""),
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
