@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
@@ -87,10 +88,18 @@ class PkvError(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} (status {status})")
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """The library, loaded once per process from ``path`` (default: ``LIB_PATH``, read at
+    call time).  Asking for another file after one is loaded raises instead of quietly
+    returning the loaded one."""
     global _lib
     with _lock:
+        if path is None:
+            path = LIB_PATH
         if _lib is not None:
+            if os.path.realpath(path) != os.path.realpath(_lib._name):
+                raise RuntimeError(f"libpagedkv is already loaded from {_lib._name}; "
+                                   f"cannot load {path} in the same process")
             return _lib
         if not os.path.exists(path):
             raise RuntimeError(

@@ -266,3 +266,14 @@ def test_fp8_write_and_prologue_reject(lib, cpu_only):
                                   NULL) == INV
     assert lib.pkv_kv_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 8, 16, 1024, FP8,
                                   NULL) == UNS                         # 8-byte rows
+
+
+def test_load_library_refuses_a_second_file(lib, tmp_path):
+    # one library per process: the loaded one is returned for its own path (or none),
+    # and another path is an error rather than a silent substitution
+    assert _lib.load_library() is lib
+    assert _lib.load_library(_lib.LIB_PATH) is lib
+    other = tmp_path / "libpagedkv_other.so"
+    other.write_bytes(b"")
+    with pytest.raises(RuntimeError, match="already loaded"):
+        _lib.load_library(str(other))
