@@ -90,17 +90,17 @@ class PkvError(RuntimeError):
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     """The library, loaded once per process from ``path`` (default: ``LIB_PATH``, read at
-    call time).  Asking for another file after one is loaded raises instead of quietly
-    returning the loaded one."""
+    call time).  Later calls without a path return the loaded library; naming another
+    file after one is loaded raises instead of quietly returning the loaded one."""
     global _lib
     with _lock:
-        if path is None:
-            path = LIB_PATH
         if _lib is not None:
-            if os.path.realpath(path) != os.path.realpath(_lib._name):
+            if path is not None and os.path.realpath(path) != os.path.realpath(_lib._name):
                 raise RuntimeError(f"libpagedkv is already loaded from {_lib._name}; "
                                    f"cannot load {path} in the same process")
             return _lib
+        if path is None:
+            path = LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(
                 f"libpagedkv.so not found at {path}; build it first with "
