@@ -9,7 +9,7 @@ element size) per second, the same figure as a fraction of the 8 TB/s HBM peak, 
 sequences (tokens) per second.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config llama3_8b]
-                    [--partition-size 512] [--no-cpu-baseline]
+                    [--partition-size 512] [--layout per_head] [--no-cpu-baseline]
 
 A config named *_fp8 runs the same workload over E4M3 (8-bit float) caches: the
 prologue quantises the new rows, attention decodes the codes (balanced split only).
@@ -17,8 +17,11 @@ The configs spec_verify and chunked_prefill run steps with several new tokens pe
 sequence (slot mapping, cache write, causal multi-token attention).
 
 Prints one JSON line.  The fp64 CPU oracle is timed on the same batch (all of it
-unless --cpu-sample-seqs says otherwise), on one host thread, repeated for about
-10 s of CPU work, and its outputs are compared with the GPU's.
+unless --cpu-sample-seqs says otherwise), split by sequence over k worker processes
+of one thread each (k = the host CPUs this process may use, at most 16), repeated for
+about 15 s of CPU work, and its outputs are compared with the GPU's.  In the same
+process, load-only kernels read the batch's blocks, and a plain 2 GiB buffer, to give
+the read ceilings the partition kernel is compared with.
 """
 
 from __future__ import annotations
@@ -42,6 +45,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 KERNEL_SOURCES = ("paged_attention.hip", "paged_attention_stream.hip", "pkv_device.hpp",
                   "pkv_launch.hpp", "pkv_plan.hpp", "pkv_tile.hpp", "pkv_stream.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
+CEILING_LIB = os.path.join(ROOT, "paged_kv_cache_441_amd", "libpkv_ceiling.so")
+# CPU oracle worker processes: the host CPUs this process may use, at most this many
+# (a GPU machine grants one GPU's job 16 CPUs, whatever the machine has)
+CPU_WORKER_CAP = 16
 
 
 def traffic_file(kernel: str, workload: str) -> str:
@@ -136,10 +143,18 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama3_8b")
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="tokens per context partition; 0 selects the balanced split "
-                         "(equal shares of the tile list per workgroup); default: the "
+                    help="tokens per context partition; 0: the library default of 512; "
+                         "-1: the balanced split (equal shares of the tile list per "
+                         "workgroup); default: the workload's own")
+    ap.add_argument("--layout", choices=["stream", "per_head"], default=None,
+                    help="fixed partitions: the streaming kernel (stream) or the per-head "
+                         "layout for batches sharing prefix blocks; default: the "
                          "workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the same-run read-ceiling kernels")
+    ap.add_argument("--oracle-worker", nargs=3, metavar=("DIR", "RANK", "WORKERS"),
+                    help=argparse.SUPPRESS)
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle runs on (0: the whole batch)")
     ap.add_argument("--component", default="decode",
@@ -182,6 +197,8 @@ def cpu_model() -> str:
 
 def main(argv=None) -> int:
     args = parse(argv)
+    if args.oracle_worker:
+        return oracle_worker(*args.oracle_worker)
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
@@ -201,8 +218,10 @@ def main(argv=None) -> int:
     from workloads import FP8_CONFIGS, make_config, make_fp8_config
 
     fp8 = args.config in FP8_CONFIGS
-    if fp8 and args.partition_size not in (None, 0):
-        print(json.dumps({"error": "E4M3 caches run the balanced split only (partition size 0)"}))
+    if fp8 and (args.partition_size not in (None, pkv.PARTITION_BALANCED) or
+                args.layout == "per_head"):
+        print(json.dumps({"error": "E4M3 caches run the balanced split only "
+                                   "(partition size -1)"}))
         return 2
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -215,6 +234,11 @@ def main(argv=None) -> int:
     b = make_fp8_config(args.config, device=dev) if fp8 else make_config(args.config, device=dev)
     spec = b.spec
     P = spec.partition_size if args.partition_size is None else args.partition_size
+    per_head = spec.per_head if args.layout is None else args.layout == "per_head"
+    if per_head and P == pkv.PARTITION_BALANCED:
+        print(json.dumps({"error": "the per-head layout runs fixed partitions only"}))
+        return 2
+    P_tokens = 512 if P == 0 else P     # partition_size 0 is the 512-token default
     ks, vs = b.extra.get("k_scale"), b.extra.get("v_scale")
     B, H, Hkv, D, BS, NB = (b.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim,
                             spec.block_size, spec.num_blocks)
@@ -231,7 +255,8 @@ def main(argv=None) -> int:
     # The step's arguments are checked once; each stage is then one C call, so the
     # host stays ahead of the GPU and the events time the kernels, not the host.
     ds = pkv.DecodeStep(b.query, b.key, b.value, kc, vc, bt, cl, b.scale, P, out=out,
-                        workspace=ws, slot_mapping=slots, k_scale=ks, v_scale=vs)
+                        workspace=ws, slot_mapping=slots, k_scale=ks, v_scale=vs,
+                        per_head=per_head)
 
     # Fence-free HIP events (see HipTimer).  Each still costs about 1.7 us of GPU time
     # on MI355X, so the timed steps carry only the two around the attention kernel
@@ -282,9 +307,12 @@ def main(argv=None) -> int:
     timer.close()
 
     kv_bytes = b.kv_bytes()
-    # fixed partitions run in the same streaming kernel (one workgroup per partition);
-    # stored traffic counters exist for the balanced split only
-    kernel = "paged_attention_stream"
+    unique_bytes = unique_kv_bytes(b)
+    # fixed partitions run in the same streaming kernel (one workgroup per partition)
+    # unless the per-head layout is asked for
+    kernel = "paged_attention_partition" if per_head else "paged_attention_stream"
+    balanced = P == pkv.PARTITION_BALANCED
+    split = "balanced" if balanced else ("fixed_per_head" if per_head else "fixed")
     tokens = int(b.context_lens.astype(np.int64).sum())
     step_s = ms_step / 1e3
     kv_gbs_step = kv_bytes / step_s / 1e9
@@ -309,7 +337,8 @@ def main(argv=None) -> int:
             "workload": spec.name,
             "num_seqs": B, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": BS, "num_blocks": NB, "max_blocks_per_seq": MB,
-            "partition_size": P, "kv_dtype": spec.kv_dtype, "accumulate": "f32",
+            "partition_size": P, "split": split, "kv_dtype": spec.kv_dtype,
+            "accumulate": "f32",
             "out_dtype": "f32", "context": str(spec.ctx),
             **({"query_dtype": "bf16", "k_scale": ks, "v_scale": vs} if fp8 else {}),
             "context_sum": tokens, "context_mean": round(tokens / B, 1),
@@ -319,7 +348,9 @@ def main(argv=None) -> int:
         "tokens_per_s": round(B / step_s, 1),
         "tokens_per_s_32_layers": round(B / (32 * step_s), 1),
         "kv_bytes_per_step": kv_bytes,
+        "kv_bytes_unique_per_step": unique_bytes,
         "attention_kv_gbs": round(kv_bytes / (attn_ms / 1e3) / 1e9, 1),
+        "attention_unique_kv_gbs": round(unique_bytes / (attn_ms / 1e3) / 1e9, 1),
         "kernel_ms": {
             "decode_prologue (slot mapping, cache write, plan)": round(float(t_write.mean()), 5),
             "attention_partition": round(part_ms, 5),
@@ -330,7 +361,8 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{kernel}_kernel" + (f" (fixed {P}-token partitions)" if P else ""),
+            "kernel": f"{kernel}_kernel" + ("" if balanced else
+                                             f" (fixed {P_tokens}-token partitions)"),
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -338,13 +370,19 @@ def main(argv=None) -> int:
             "traffic": stored_traffic(kernel, spec.name, P),
             "traffic_unit": "bytes per launch (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, "
                             "factors from a plain 1 GiB copy)",
+            "achieved_unique": round(unique_bytes / (part_ms / 1e3) / 1e9, 1),
         },
         "device": torch.cuda.get_device_name(dev),
         "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
         "input_generation_s": round(gen_s, 2),
     }
 
-    # ---- CPU oracle on a bounded sample, and a parity spot check -----------------
+    if not args.no_ceiling:
+        ceil = measure_ceilings(b, dev)
+        result["roofline"]["ceiling"] = ceil
+        result["roofline"]["frac_of_ceiling"] = round(part_gbs / ceil["blocks_gbs"], 4)
+
+    # ---- CPU oracle on a bounded sample, and parity over it ------------------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(b, out, args.cpu_sample_seqs)
 
@@ -594,111 +632,343 @@ def bench_multi(args) -> int:
     return 0
 
 
-def cpu_baseline_multi(b, gpu_out, min_seconds=10.0):
-    """The oracle, untuned, on one host thread, over whole sequences of the batch taken
-    in order until about ``min_seconds`` of CPU work; rate in new tokens per second."""
+def unique_kv_bytes(b) -> int:
+    """KV bytes of the distinct cache rows the batch reads: a physical block shared by
+    several sequences counts once, with the most rows any of them uses."""
+    BS = b.spec.block_size
+    rows = {}
+    for i, c in enumerate(b.context_lens.tolist()):
+        for j in range(-(-c // BS)):
+            blk = int(b.block_tables[i, j])
+            rows[blk] = max(rows.get(blk, 0), min(BS, c - j * BS))
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[b.kv_dtype]
+    return sum(rows.values()) * b.spec.num_kv_heads * b.spec.head_dim * 2 * elem
+
+
+def measure_ceilings(b, dev, reps=10) -> dict:
+    """Load-only kernels (libpkv_ceiling.so) in this process: every block the batch
+    references, whole, from both caches in table order with non-temporal 16-byte loads
+    (grid of two workgroups per CU); and a plain 2 GiB buffer streamed the same way
+    (one workgroup per CU, eight loads in flight per lane).  Mean of ``reps`` launches
+    by fence-free HIP events."""
+    import ctypes
     import torch
-    from threadpoolctl import threadpool_limits
 
-    from oracle import multi_query as omq
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} not built (python -m paged_kv_cache_441_amd.build_lib)")
+    lib = ctypes.CDLL(CEILING_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pkv_ceiling_block_read.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp]
+    lib.pkv_ceiling_block_read.restype = ctypes.c_int
+    lib.pkv_ceiling_linear_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.pkv_ceiling_linear_read.restype = ctypes.c_int
+    BS, NB = b.spec.block_size, b.spec.num_blocks
+    seen, ids = set(), []
+    for i, c in enumerate(b.context_lens.tolist()):
+        for j in range(-(-c // BS)):
+            blk = int(b.block_tables[i, j])
+            if blk not in seen:
+                seen.add(blk)
+                ids.append(blk)
+    ids = np.asarray(ids, dtype=np.int32)
+    if ids.size == 0 or ids.min() < 0 or ids.max() >= NB:
+        raise ValueError("block ids outside the pool")
+    ids_t = torch.as_tensor(ids, device=dev)
+    kc, vc = b.key_cache, b.value_cache
+    block_bytes = kc[0].numel() * kc.element_size()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid_blocks, grid_linear = 2 * cus, cus
+    sink = torch.empty(grid_blocks * 256 * 16, dtype=torch.uint8, device=dev)
+    lin_bytes = 2 << 30
+    buf = torch.zeros(lin_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
 
-    qsl = b.extra["query_start_loc"]
-    done, secs, tokens, err = [], 0.0, 0, 0.0
-    with threadpool_limits(limits=1):
-        for i in range(b.num_seqs):
-            if secs >= min_seconds:
-                break
-            bt = b.block_tables[[i]]
-            ids = np.unique(bt[bt >= 0])
-            idx = torch.as_tensor(ids.astype(np.int64), device=b.key_cache.device)
-            kc = b.numpy_storage(b.key_cache.index_select(0, idx))
-            vc = b.numpy_storage(b.value_cache.index_select(0, idx))
-            cbt = np.where(bt >= 0, np.searchsorted(ids, np.maximum(bt, 0)), -1).astype(np.int32)
-            q0, q1 = int(qsl[i]), int(qsl[i + 1])
-            t0 = time.perf_counter()
-            _, _, _, ref = omq.multi_query_step(
-                b.numpy_storage(b.query)[q0:q1], b.numpy_storage(b.key)[q0:q1],
-                b.numpy_storage(b.value)[q0:q1], kc, vc, cbt, b.context_lens[[i]],
-                np.array([0, q1 - q0]), b.scale, b.kv_dtype)
-            secs += time.perf_counter() - t0
-            tokens += q1 - q0
-            done.append(i)
-            g = gpu_out[q0:q1].float().cpu().numpy().astype(np.float64)
-            err = max(err, float(np.abs(g - ref).max()))
-    base = {"value": round(tokens / secs, 2), "unit": "new tokens/s", "cores": 1,
-            "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(secs, 2),
-            "sample": f"the first {len(done)} of {b.num_seqs} sequences ({tokens} new tokens): "
-                      "slot mapping, cache write and fp64 causal attention for all heads, one "
-                      "host thread"}
-    parity = {"tokens": tokens, "max_abs_err_vs_oracle": err, "tolerance": 2e-3,
-              "ok": bool(err <= 2e-3)}
-    return base, parity
+    def blocks():
+        rc = lib.pkv_ceiling_block_read(kc.data_ptr(), vc.data_ptr(), ids_t.data_ptr(),
+                                        int(ids.size), block_bytes, grid_blocks,
+                                        sink.data_ptr(), sp)
+        if rc != 0:
+            raise RuntimeError(f"pkv_ceiling_block_read: hip error {rc}")
+
+    def linear():
+        rc = lib.pkv_ceiling_linear_read(buf.data_ptr(), lin_bytes, grid_linear,
+                                         sink.data_ptr(), sp)
+        if rc != 0:
+            raise RuntimeError(f"pkv_ceiling_linear_read: hip error {rc}")
+
+    timer = HipTimer(stream)
+    res = {}
+    for name, fn, nbytes in (("blocks", blocks, 2 * int(ids.size) * block_bytes),
+                             ("linear", linear, lin_bytes)):
+        for _ in range(3):
+            fn()
+        ev = [timer.event() for _ in range(reps + 1)]
+        for r in range(reps):
+            timer.record(ev[r])
+            fn()
+        timer.record(ev[-1])
+        torch.cuda.synchronize()
+        ms = float(np.mean([timer.ms(ev[r], ev[r + 1]) for r in range(reps)]))
+        res[name] = (nbytes, ms)
+    timer.close()
+    del buf
+    torch.cuda.empty_cache()
+    return {
+        "blocks_gbs": round(res["blocks"][0] / (res["blocks"][1] / 1e3) / 1e9, 1),
+        "blocks_bytes": res["blocks"][0],
+        "blocks_us": round(res["blocks"][1] * 1e3, 2),
+        "linear_gbs": round(res["linear"][0] / (res["linear"][1] / 1e3) / 1e9, 1),
+        "linear_bytes": lin_bytes,
+        "kernel": "read_ceiling.hip: block_read_kernel (every referenced block of both "
+                  "caches, whole, in table order) and linear_read_kernel; non-temporal "
+                  "16-byte loads, no compute",
+    }
 
 
-def cpu_baseline(b, gpu_out, n_sample, min_seconds=10.0, max_reps=20):
-    """The oracle, untuned, on one host thread: slot mapping, cache write and fp64
-    attention over the first ``n_sample`` sequences of the batch (all of them by
-    default), repeated until about ``min_seconds`` of CPU work have run.  The rate
-    is the median repetition's."""
+# ---- the CPU oracle, split by sequence over worker processes ----------------------
+
+def _assign(costs, k):
+    """Sequences to k workers, longest first onto the least loaded (deterministic)."""
+    order = sorted(range(len(costs)), key=lambda i: (-costs[i], i))
+    load = [0] * k
+    out = [[] for _ in range(k)]
+    for i in order:
+        w = min(range(k), key=lambda j: (load[j], j))
+        out[w].append(i)
+        load[w] += costs[i]
+    return [sorted(x) for x in out if x]
+
+
+def _compact(b, seqs):
+    """Host copies of the blocks ``seqs`` reference, with their tables relabelled."""
     import torch
-    from threadpoolctl import threadpool_limits
-
-    import oracle
-
-    B = b.num_seqs
-    n = min(B, n_sample) if n_sample else B
-    bt = b.block_tables[:n]
+    bt = b.block_tables[seqs]
     ids = np.unique(bt[bt >= 0])
     idx = torch.as_tensor(ids.astype(np.int64), device=b.key_cache.device)
     kc = b.numpy_storage(b.key_cache.index_select(0, idx))
     vc = b.numpy_storage(b.value_cache.index_select(0, idx))
     tables = np.where(bt >= 0, np.searchsorted(ids, np.maximum(bt, 0)), -1).astype(np.int32)
-    q = b.numpy_storage(b.query)[:n]
-    k = b.numpy_storage(b.key)[:n]
-    v = b.numpy_storage(b.value)[:n]
-    ctx = b.context_lens[:n]
+    return kc, vc, tables
+
+
+class OracleWorkers:
+    """k worker processes (``bench.py --oracle-worker``), each running the oracle on
+    its own sub-batch with one thread.  They never touch the GPU: the sub-batches are
+    handed over as .npy files, and a line on stdin starts a timed round."""
+
+    def __init__(self, job: dict, parts: list):
+        import subprocess
+        import tempfile
+        shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+        self.dir = tempfile.mkdtemp(prefix="pkv_oracle_", dir=shm)
+        for r, arrays in enumerate(parts):
+            for name, arr in arrays.items():
+                np.save(os.path.join(self.dir, f"{name}_{r}.npy"), np.ascontiguousarray(arr))
+        with open(os.path.join(self.dir, "job.json"), "w") as f:
+            json.dump(job, f)
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
+                   MKL_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="")
+        self.k = len(parts)
+        self.procs = [subprocess.Popen([sys.executable, "-u", os.path.abspath(__file__),
+                                        "--oracle-worker", self.dir, str(r), str(self.k)],
+                                       stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                                       text=True, env=env)
+                      for r in range(self.k)]
+        for p in self.procs:
+            self._expect(p, "ready")
+
+    @staticmethod
+    def _expect(p, word):
+        line = p.stdout.readline().strip()
+        if line != word:
+            raise RuntimeError(f"oracle worker said {line!r}, expected {word!r}")
+
+    def run(self, reps: int) -> float:
+        """Wall seconds for every worker to run its sub-batch ``reps`` times."""
+        t0 = time.perf_counter()
+        for p in self.procs:
+            p.stdin.write(f"run {reps}\n")
+            p.stdin.flush()
+        for p in self.procs:
+            self._expect(p, "done")
+        return time.perf_counter() - t0
+
+    def finish(self) -> list:
+        import shutil
+        try:
+            for p in self.procs:
+                p.stdin.write("quit\n")
+                p.stdin.flush()
+            for p in self.procs:
+                if p.wait(timeout=120) != 0:
+                    raise RuntimeError("an oracle worker failed")
+            return [np.load(os.path.join(self.dir, f"out_{r}.npy")) for r in range(self.k)]
+        finally:
+            for p in self.procs:
+                if p.poll() is None:
+                    p.kill()
+            shutil.rmtree(self.dir, ignore_errors=True)
+
+
+def oracle_worker(d: str, rank: str, k: str) -> int:
+    """Worker side of OracleWorkers: load the sub-batch, run the oracle on request."""
+    with open(os.path.join(d, "job.json")) as f:
+        job = json.load(f)
+    r = int(rank)
+    names = {"decode": ("q", "k", "v", "kc", "vc", "bt", "ctx"),
+             "decode_fp8": ("q", "k", "v", "kc", "vc", "bt", "ctx"),
+             "multi": ("q", "k", "v", "kc", "vc", "bt", "ctx", "qsl")}[job["kind"]]
+    a = {n: np.load(os.path.join(d, f"{n}_{r}.npy")) for n in names}
+    import oracle
+
+    def once():
+        if job["kind"] == "decode":
+            return oracle.decode_step(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"],
+                                      a["ctx"], job["scale"], job["kv_dtype"])[3]
+        if job["kind"] == "decode_fp8":
+            from oracle import fp8 as of8
+            BS = a["kc"].shape[1]
+            slots = oracle.slot_mapping(a["bt"], a["ctx"], BS)
+            kc, vc = of8.cache_write_fp8(a["kc"], a["vc"], oracle.bf16_bits_to_f64(a["k"]),
+                                         oracle.bf16_bits_to_f64(a["v"]), slots, BS,
+                                         job["k_scale"], job["v_scale"])
+            return of8.paged_attention_decode_fp8(oracle.bf16_bits_to_f64(a["q"]), kc, vc,
+                                                  a["bt"], a["ctx"], job["scale"],
+                                                  job["k_scale"], job["v_scale"])
+        from oracle import multi_query as omq
+        return omq.multi_query_step(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"],
+                                    a["ctx"], a["qsl"], job["scale"], job["kv_dtype"])[3]
+
+    out = None
+    print("ready", flush=True)
+    for line in sys.stdin:
+        cmd = line.split()
+        if not cmd or cmd[0] == "quit":
+            break
+        if cmd[0] == "run":
+            for _ in range(int(cmd[1])):
+                out = once()
+            print("done", flush=True)
+    if out is None:
+        out = once()
+    np.save(os.path.join(d, f"out_{r}.npy"), out)
+    return 0
+
+
+def _timed_rounds(workers, cpu_seconds: float):
+    """One calibration round, then enough rounds for about ``cpu_seconds`` of CPU work
+    over all workers (at least one second of wall time); returns (seconds per round,
+    rounds, wall seconds of the timed rounds)."""
+    w1 = workers.run(1)
+    reps = int(max(1, min(100, np.ceil(max(1.0, cpu_seconds / workers.k) / w1))))
+    wall = workers.run(reps)
+    return wall / reps, reps, wall
+
+
+def cpu_workers() -> int:
+    return max(1, min(CPU_WORKER_CAP, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(b, gpu_out, n_sample, cpu_seconds=15.0):
+    """The oracle, untuned, over the first ``n_sample`` sequences of the batch (all by
+    default): slot mapping, cache write and fp64 attention, the sequences split over
+    k one-thread worker processes (longest first onto the least loaded); timed as the
+    wall time of all workers per round, rounds repeated for about ``cpu_seconds`` of
+    CPU work."""
+    B = b.num_seqs
+    n = min(B, n_sample) if n_sample else B
+    k = min(cpu_workers(), n)
     fp8 = b.kv_dtype == "fp8"
-
-    def run():
-        if not fp8:
-            return oracle.decode_step(q, k, v, kc, vc, tables, ctx, b.scale, b.kv_dtype)[3]
-        from oracle import fp8 as of8
-        ks, vs = b.extra["k_scale"], b.extra["v_scale"]
-        slots = oracle.slot_mapping(tables, ctx, b.spec.block_size)
-        kc2, vc2 = of8.cache_write_fp8(kc, vc, oracle.bf16_bits_to_f64(k),
-                                       oracle.bf16_bits_to_f64(v), slots, b.spec.block_size,
-                                       ks, vs)
-        return of8.paged_attention_decode_fp8(oracle.bf16_bits_to_f64(q), kc2, vc2, tables, ctx,
-                                              b.scale, ks, vs)
-
-    times = []
-    with threadpool_limits(limits=1):
-        while len(times) < max_reps and sum(times) < min_seconds:
-            t0 = time.perf_counter()
-            ref = run()
-            times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+    groups = _assign([int(c) for c in b.context_lens[:n]], k)
+    st = b.numpy_storage
+    q_all, k_all, v_all = st(b.query), st(b.key), st(b.value)
+    parts = []
+    for seqs in groups:
+        s = np.asarray(seqs)
+        kc, vc, tables = _compact(b, s)
+        parts.append({"q": q_all[s], "k": k_all[s], "v": v_all[s], "kc": kc, "vc": vc,
+                      "bt": tables, "ctx": b.context_lens[s]})
+    job = {"kind": "decode_fp8" if fp8 else "decode", "scale": b.scale,
+           "kv_dtype": b.kv_dtype}
+    if fp8:
+        job.update(k_scale=b.extra["k_scale"], v_scale=b.extra["v_scale"])
+    workers = OracleWorkers(job, parts)
+    try:
+        per_round, reps, wall = _timed_rounds(workers, cpu_seconds)
+    finally:
+        outs = workers.finish()
+    ref = np.empty((n,) + tuple(gpu_out.shape[1:]), dtype=np.float64)
+    for seqs, o in zip(groups, outs):
+        ref[np.asarray(seqs)] = o
+    ctx = b.context_lens[:n]
     sample_kv = int(ctx.astype(np.int64).sum()) * b.spec.num_kv_heads * b.spec.head_dim * 2 * \
         {"bf16": 2, "f32": 4, "fp8": 1}[b.kv_dtype]
     g = gpu_out[:n].float().cpu().numpy().astype(np.float64)
     err = float(np.abs(g - ref).max())
     what = "the whole batch" if n == B else f"the first {n} of {B} sequences"
     base = {
-        "value": round(sample_kv / dt / 1e9, 4),
+        "value": round(sample_kv / per_round / 1e9, 4),
         "unit": "GB/s",
-        "tokens_per_s": round(n / dt, 2),
-        "seconds_per_rep": round(dt, 3),
-        "reps": len(times),
-        "cpu_seconds_total": round(sum(times), 2),
-        "cores": 1,
+        "tokens_per_s": round(n / per_round, 2),
+        "seconds_per_round": round(per_round, 4),
+        "rounds": reps,
+        "cpu_seconds_total": round(wall * len(groups), 2),
+        "cores": len(groups),
         "kind": "oracle",
         "cpu_model": cpu_model(),
         "host_cpus_visible": len(os.sched_getaffinity(0)),
         "sample": f"{what} ({n} sequences, {int(ctx.sum())} context tokens): slot mapping, "
-                  f"cache write and fp64 attention for all {b.spec.num_heads} heads, "
-                  f"{len(times)} repetitions on one host thread; median repetition",
+                  f"cache write and fp64 attention for all {b.spec.num_heads} heads, split by "
+                  f"sequence over {len(groups)} one-thread worker processes; {reps} timed "
+                  f"rounds after one untimed",
     }
     parity = {"sequences": n, "max_abs_err_vs_oracle": err, "tolerance": 2e-3,
+              "ok": bool(err <= 2e-3)}
+    return base, parity
+
+
+def cpu_baseline_multi(b, gpu_out, cpu_seconds=15.0):
+    """The oracle, untuned, on the whole multi-token batch: the sequences split over k
+    one-thread worker processes (at most one per sequence), timed per round as in
+    cpu_baseline; rate in new tokens per second."""
+    qsl = b.extra["query_start_loc"]
+    ql = np.diff(qsl)
+    B = b.num_seqs
+    k = min(cpu_workers(), B)
+    costs = [int(q) * int(c) for q, c in zip(ql, b.context_lens)]
+    groups = _assign(costs, k)
+    st = b.numpy_storage
+    q_all, k_all, v_all = st(b.query), st(b.key), st(b.value)
+    parts = []
+    for seqs in groups:
+        s = np.asarray(seqs)
+        rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs]).astype(np.int64)
+        sub_qsl = np.concatenate([[0], np.cumsum(ql[s])]).astype(np.int64)
+        kc, vc, tables = _compact(b, s)
+        parts.append({"q": q_all[rows], "k": k_all[rows], "v": v_all[rows], "kc": kc,
+                      "vc": vc, "bt": tables, "ctx": b.context_lens[s], "qsl": sub_qsl})
+    workers = OracleWorkers({"kind": "multi", "scale": b.scale, "kv_dtype": b.kv_dtype}, parts)
+    try:
+        per_round, reps, wall = _timed_rounds(workers, cpu_seconds)
+    finally:
+        outs = workers.finish()
+    T = int(qsl[-1])
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    err = 0.0
+    for seqs, o in zip(groups, outs):
+        rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs]).astype(np.int64)
+        err = max(err, float(np.abs(g[rows] - o).max()))
+    base = {"value": round(T / per_round, 2), "unit": "new tokens/s", "cores": len(groups),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cpus_visible": len(os.sched_getaffinity(0)),
+            "seconds_per_round": round(per_round, 4), "rounds": reps,
+            "cpu_seconds_total": round(wall * len(groups), 2),
+            "sample": f"the whole batch ({B} sequences, {T} new tokens): slot mapping, cache "
+                      f"write and fp64 causal attention for all heads, split by sequence over "
+                      f"{len(groups)} one-thread worker processes; {reps} timed rounds after "
+                      f"one untimed"}
+    parity = {"tokens": T, "max_abs_err_vs_oracle": err, "tolerance": 2e-3,
               "ok": bool(err <= 2e-3)}
     return base, parity
 

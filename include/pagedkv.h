@@ -15,14 +15,18 @@
  *  - partition_size P > 0 (fixed partitions): sequence i is cut into partitions of
  *    P tokens; one workgroup per (sequence, partition) and group of kv heads, which
  *    streams whole token rows of its heads through LDS; longest partitions first.
- *  - partition_size 0 (balanced split): the (sequence, 16-token tile) pairs of the
- *    whole batch, plus one position per sequence for its fixed cost, form one list
- *    that is cut into equal contiguous shares, one per workgroup of a grid the GPU
- *    holds at once; each workgroup streams whole token rows of its kv-head group
+ *    partition_size PKV_PARTITION_DEFAULT (0) means P = PKV_DEFAULT_PARTITION_TOKENS
+ *    (512).  A sequence's result depends only on its own data and P.
+ *  - partition_size PKV_PARTITION_BALANCED (-1): the (sequence, 16-token tile) pairs
+ *    of the whole batch, plus one position per sequence for its fixed cost, form one
+ *    list that is cut into equal contiguous shares, one per workgroup of a grid the
+ *    GPU holds at once; each workgroup streams whole token rows of its kv-head group
  *    through LDS.  Where the pieces of a sequence end therefore depends on the
  *    whole batch (and on the GPU's compute-unit count), so a sequence's result
  *    may differ between batches in the last bits of fp32; for one batch on one
- *    GPU it is deterministic.
+ *    GPU it is deterministic.  It is the faster split when context lengths vary
+ *    widely.
+ * Other negative values are PKV_ERR_INVALID_ARG.
  *
  * Cache layout (both key_cache and value_cache), row-major, no padding:
  *     [num_blocks][block_size][num_kv_heads][head_dim]
@@ -57,7 +61,12 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
+
+/* partition_size values with a name (see above) */
+#define PKV_PARTITION_DEFAULT 0            /* fixed partitions of 512 tokens */
+#define PKV_DEFAULT_PARTITION_TOKENS 512
+#define PKV_PARTITION_BALANCED (-1)        /* the balanced split */
 
 typedef enum {
   PKV_OK = 0,
@@ -264,15 +273,15 @@ pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pa
  * (in_dtype) rows; num_kv_heads*head_dim must be a multiple of 16.
  *
  * pkv_decode_prologue_fp8 -- pkv_decode_prologue storing codes as above; it builds
- * the balanced-split plan (partition_size 0).
+ * the balanced-split plan (partition_size PKV_PARTITION_BALANCED).
  *
  * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 caches:
  * scores scale * k_scale * <q, decode(k_t)>, output sum_t p_t v_scale decode(v_t) /
  * sum_t p_t.  Decoding is exact (every E4M3 value is a bfloat16); queries are bf16;
  * accumulation is fp32.  Always the balanced split: the workspace is
- * pkv_paged_attention_workspace_bytes(..., partition_size = 0), and the staged form
- * is pkv_paged_attention_plan and pkv_paged_attention_reduce with partition_size 0
- * around pkv_paged_attention_partition_fp8.  Supported: head_dim 64 (with an even
+ * pkv_paged_attention_workspace_bytes(..., PKV_PARTITION_BALANCED), and the staged
+ * form is pkv_paged_attention_plan and pkv_paged_attention_reduce with partition_size
+ * PKV_PARTITION_BALANCED around pkv_paged_attention_partition_fp8.  Supported: head_dim 64 (with an even
  * num_kv_heads) or 128, block_size 16 or 32, num_heads / num_kv_heads in {1, 2, 4,
  * 8}, out_dtype PKV_F32 or PKV_BF16.  The device-side contract (NaN rows for a bad
  * context length or block id) is that of pkv_paged_attention_decode.  The unscaled
@@ -413,7 +422,7 @@ pkv_status pkv_decode_prologue(const int32_t* block_tables, const int32_t* conte
  *     rounded up to 256 bytes:  256 + roundup256(num_seqs * NP * 16);
  *   - one (max, sum, partial output) fp32 record per (sequence, query head,
  *     partition):  num_seqs * num_heads * NP * (head_dim + 2) * 4.
- * With the balanced split (partition_size 0) it holds
+ * With the balanced split (PKV_PARTITION_BALANCED) it holds
  *   - the tile plan: 256 bytes of header, then num_seqs + 1 int32 prefix sums,
  *     rounded up to 256 bytes:  256 + roundup256((num_seqs + 1) * 4);
  *   - one record per (segment label, query head), labels below 1024 + num_seqs:
@@ -441,7 +450,8 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  * are not printed on the pages; they leave the result unchanged.)
  *
  * Contexts are split into pieces (fixed partitions of P = partition_size tokens,
- * or the segments of the balanced split when partition_size is 0), each giving
+ * 512 for PKV_PARTITION_DEFAULT, or the segments of the balanced split for
+ * PKV_PARTITION_BALANCED), each giving
  * (m_k, l_k, o_k); the pieces are merged in order as
  *     M = max m_k,  w_k = l_k exp(m_k - M),  out = sum w_k o_k / sum w_k.
  * A sequence in a single piece is written directly.
@@ -453,8 +463,9 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *                 ceil(ctx/block_size) are never read
  *   context_lens  device int32 [num_seqs], 1 <= ctx <= max_blocks_per_seq*block_size
  *   scale         multiplies q.k (1/sqrt(head_dim) for standard attention)
- *   partition_size  P in tokens, a multiple of block_size and of 16; or 0 for the
- *                 balanced split
+ *   partition_size  P in tokens, a multiple of block_size and of 16;
+ *                 PKV_PARTITION_DEFAULT (0) for 512; PKV_PARTITION_BALANCED (-1) for
+ *                 the balanced split
  *   workspace     device buffer of at least pkv_paged_attention_workspace_bytes()
  *
  * Supported: kv_dtype in {PKV_F32, PKV_BF16}; out_dtype in {PKV_F32, PKV_BF16}
@@ -526,6 +537,43 @@ pkv_status pkv_paged_attention_reduce(void* out, const int32_t* context_lens, in
                                       int32_t max_blocks_per_seq, int32_t partition_size,
                                       pkv_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * The per-head layout of fixed partitions, for batches whose sequences share prefix
+ * blocks.  (Page "读一个真实 serving 系统 · vLLM 架构巡礼", section 2: requests with a
+ * common prefix point at the same physical blocks; page "vllm源码剖析", the BlockPool
+ * paragraphs: a cached block is handed to every request that matches it.)  The
+ * library cannot tell from its arguments that tables share blocks; the caller, who
+ * holds the reference counts, can.
+ *
+ * pkv_paged_attention_partition_per_head is pkv_paged_attention_partition with one
+ * 4-wave workgroup per (kv head, partition, sequence) instead of one per (partition,
+ * sequence) and group of kv heads, reading keys and values through the caches (the
+ * streaming kernel's copies bypass them).  The workgroups of sequences that share a
+ * block then run side by side and the block is fetched from HBM about once.  Same
+ * arguments, same workspace and plan (pkv_paged_attention_plan, then
+ * pkv_paged_attention_reduce), same results to fp32 rounding; fixed partitions only:
+ * partition_size PKV_PARTITION_BALANCED is PKV_ERR_INVALID_ARG.  Caches of PKV_F32 or
+ * PKV_BF16.
+ *
+ * pkv_paged_attention_decode_per_head is pkv_paged_attention_decode (plan, this
+ * partition stage, reduce) in that layout.
+ */
+pkv_status pkv_paged_attention_partition_per_head(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+pkv_status pkv_paged_attention_decode_per_head(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,8 @@ include/pagedkv.h; this package only marshals torch tensors into that ABI.
 
 from ._lib import LIB_PATH, PkvError, load_library, status_string  # noqa: F401
 from .ops import (  # noqa: F401
+    PARTITION_BALANCED,
+    PARTITION_DEFAULT,
     BlockPool,
     DecodeStep,
     alloc_workspace,
@@ -19,9 +21,11 @@ from .ops import (  # noqa: F401
     multi_query_workspace_bytes,
     paged_attention_decode,
     paged_attention_decode_fp8,
+    paged_attention_decode_per_head,
     paged_attention_partition,
     paged_attention_multi_query,
     paged_attention_partition_fp8,
+    paged_attention_partition_per_head,
     paged_attention_plan,
     prefix_block_hashes,
     paged_attention_reduce,

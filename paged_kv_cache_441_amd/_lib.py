@@ -25,6 +25,11 @@ PKV_F32 = 0
 PKV_BF16 = 1
 PKV_FP8_E4M3 = 2
 
+# partition_size values with a name
+PKV_PARTITION_DEFAULT = 0          # fixed partitions of PKV_DEFAULT_PARTITION_TOKENS
+PKV_DEFAULT_PARTITION_TOKENS = 512
+PKV_PARTITION_BALANCED = -1        # the balanced split
+
 _i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
 # name -> (restype, argtypes), in the order of include/pagedkv.h
@@ -74,9 +79,15 @@ SIGNATURES = {
                                              _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                                           _sz, _vp]),
+    "pkv_paged_attention_partition_per_head": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _i64, _f32, _i32,
+                                                      _i32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_per_head": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _i64, _f32, _i32, _i32, _i32,
+                                                   _vp, _sz, _vp]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lock = threading.Lock()
 _lib = None

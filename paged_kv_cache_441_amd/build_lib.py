@@ -3,7 +3,9 @@
     python -m paged_kv_cache_441_amd.build_lib [--jobs N]
 
 Objects go to paged_kv_cache_441_amd/_build/, the library to
-paged_kv_cache_441_amd/libpagedkv.so.  Every call recompiles.
+paged_kv_cache_441_amd/libpagedkv.so.  Every call recompiles.  The benchmark's
+read-ceiling kernels (csrc/read_ceiling.hip) go to a library of their own,
+libpkv_ceiling.so, which only bench.py loads.
 """
 
 from __future__ import annotations
@@ -22,6 +24,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["pkv_api.cpp", "block_pool.cpp", "cache_write.hip", "paged_attention.hip", "paged_attention_stream.hip",
            "paged_attention_multi.hip"]
+CEILING_SOURCE = "read_ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libpkv_ceiling.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -52,18 +56,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CEILING_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

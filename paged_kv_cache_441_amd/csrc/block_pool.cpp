@@ -62,6 +62,7 @@ uint64_t block_hash(uint64_t parent, const int32_t* tokens, int32_t n) {
 struct pkv_block_pool {
   std::vector<int32_t> prev, next;   // free list links; -1 ends it
   std::vector<int32_t> ref;          // reference count per block
+  std::vector<int32_t> pending;      // release(): references asked per block; 0 between calls
   std::vector<uint8_t> is_free;
   int32_t head = -1, tail = -1;      // front and back of the free list
   int64_t count = 0;                 // free blocks
@@ -73,7 +74,8 @@ struct pkv_block_pool {
   std::unordered_map<uint64_t, int32_t> cached;
 
   explicit pkv_block_pool(int32_t n)
-      : prev(n), next(n), ref(n, 0), is_free(n, 1), cached_flag(n, 0), hash(n, 0), parent(n, 0) {
+      : prev(n), next(n), ref(n, 0), pending(n, 0), is_free(n, 1), cached_flag(n, 0), hash(n, 0),
+        parent(n, 0) {
     for (int32_t i = 0; i < n; ++i) {
       prev[i] = i - 1;
       next[i] = i + 1 < n ? i + 1 : -1;
@@ -161,9 +163,20 @@ pkv_status pkv_block_pool_release(pkv_block_pool* pool, const int32_t* blocks, i
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->valid(blocks[i])) return PKV_ERR_INVALID_ARG;
   }
-  std::vector<int32_t> need(pool->size(), 0);
-  for (int32_t i = 0; i < n; ++i)
-    if (++need[blocks[i]] > pool->ref[blocks[i]]) return PKV_ERR_INVALID_ARG;
+  // count the references asked per block in the pool's reusable array, then clear
+  // only the entries this list touched: O(n), whatever the pool's size
+  int32_t counted = 0;
+  bool ok = true;
+  for (; counted < n; ++counted) {
+    const int32_t b = blocks[counted];
+    if (++pool->pending[b] > pool->ref[b]) {
+      ok = false;
+      ++counted;
+      break;
+    }
+  }
+  for (int32_t i = 0; i < counted; ++i) pool->pending[blocks[i]] = 0;
+  if (!ok) return PKV_ERR_INVALID_ARG;
   for (int32_t i = 0; i < n; ++i) pool->drop(blocks[i]);
   return PKV_OK;
 }

@@ -488,19 +488,15 @@ static hipError_t launch_partition_g(const AttentionArgs& a, hipStream_t stream)
 }
 
 // Fixed partitions run in the streaming kernel (whole token rows of a kv-head group
-// through LDS) unless built with PKV_FIXED_STREAM=0, which keeps the per-head
-// partition kernel above.
-#ifndef PKV_FIXED_STREAM
-#define PKV_FIXED_STREAM 1
-#endif
-
+// through LDS, copies past the caches) unless the caller asks for the per-head
+// layout above, which reads through the caches and suits batches sharing prefix blocks.
 hipError_t launch_attention_partition(const AttentionArgs& a, hipStream_t stream) {
   if (a.balanced) return launch_attention_stream(a, stream);
-  if (PKV_FIXED_STREAM) return launch_attention_stream_fixed(a, stream);
+  if (!a.per_head) return launch_attention_stream_fixed(a, stream);
   if (a.kv_bf16) {
     if (a.head_dim == 64) return launch_partition_g<BF16, 64>(a, stream);
     if (a.head_dim == 128) return launch_partition_g<BF16, 128>(a, stream);
-  } else {
+  } else if (!a.kv_fp8) {
     if (a.head_dim == 64) return launch_partition_g<F32, 64>(a, stream);
     if (a.head_dim == 128) return launch_partition_g<F32, 128>(a, stream);
   }

@@ -3,6 +3,7 @@
 // allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -26,6 +27,10 @@ bool valid_dtype(int32_t t) { return t == PKV_F32 || t == PKV_BF16; }
 // Types a cache may hold (bit copies).
 bool valid_storage(int32_t t) { return valid_dtype(t) || t == PKV_FP8_E4M3; }
 
+// A launch holds at most 2^32 - 1 threads per grid dimension; the per-token and
+// per-pair launches put up to 256 threads per item in x.
+constexpr int64_t kMaxItems256 = int64_t{UINT32_MAX} / 256;
+
 // A cache scale: positive and finite.
 bool valid_scale(float x) { return std::isfinite(x) && x > 0.f; }
 
@@ -38,7 +43,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
 }
 
 struct AttnShape {
-  bool balanced = false;    // partition_size 0: equal shares of the tile list per workgroup
+  bool balanced = false;    // PKV_PARTITION_BALANCED: equal shares of the tile list per workgroup
   int64_t max_parts = 0;
   int partition = 0;
   int64_t recs = 0;         // partial-result records (one per row of head_dim + 2 floats)
@@ -51,13 +56,16 @@ pkv_status check_attention_shape(int32_t num_seqs, int32_t num_heads, int32_t he
                                  int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t partition_size, AttnShape* s) {
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || partition_size < 0)
+      max_blocks_per_seq <= 0 || partition_size < PKV_PARTITION_BALANCED)
     return PKV_ERR_INVALID_ARG;
   if (!is_pow2(block_size) || block_size > 1024) return PKV_ERR_INVALID_ARG;
   int64_t max_ctx = 0;
   if (!mul_ok(max_blocks_per_seq, block_size, INT32_MAX, &max_ctx)) return PKV_ERR_INVALID_ARG;
+  // launches put at most 256 threads per (sequence, query head) row in x
+  int64_t rows = 0;
+  if (!mul_ok(num_seqs, num_heads, int64_t{UINT32_MAX} / 256, &rows)) return PKV_ERR_UNSUPPORTED;
   int64_t recs = 0, t = 0;
-  if (partition_size == 0) {
+  if (partition_size == PKV_PARTITION_BALANCED) {
     // Balanced: one record row per (segment label, head); labels < max workgroups + seqs.
     s->balanced = true;
     s->partition = 0;
@@ -70,7 +78,8 @@ pkv_status check_attention_shape(int32_t num_seqs, int32_t num_heads, int32_t he
       return PKV_ERR_INVALID_ARG;
     s->plan_bytes = pkv::tile_plan_bytes(num_seqs);
   } else {
-    const int P = partition_size;
+    const int P = partition_size == PKV_PARTITION_DEFAULT ? PKV_DEFAULT_PARTITION_TOKENS
+                                                          : partition_size;
     if (P % block_size != 0 || P % 16 != 0) return PKV_ERR_INVALID_ARG;
     s->partition = P;
     s->max_parts = (max_ctx + P - 1) / P;
@@ -144,8 +153,15 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs > 0 && (!workspace || workspace_bytes < s.ws_bytes)) return PKV_ERR_WORKSPACE;
-  if (s.max_parts * num_seqs * int64_t{num_kv_heads > 0 ? num_kv_heads : 1} > INT32_MAX)
-    return PKV_ERR_UNSUPPORTED;   // grid larger than one launch can hold
+  if (!s.balanced) {
+    // A launch holds at most 2^32 - 1 threads per grid dimension.  Fixed partitions put
+    // one workgroup per (sequence, partition) in x: up to 512 threads (eight kv heads
+    // of a group) in the streaming kernel, 256 per kv head in the per-head kernel.
+    const int64_t per_item = std::max<int64_t>(512, 256 * int64_t{num_kv_heads > 0 ? num_kv_heads : 1});
+    int64_t threads = 0;
+    if (!mul_ok(s.max_parts * num_seqs, per_item, int64_t{UINT32_MAX}, &threads))
+      return PKV_ERR_UNSUPPORTED;
+  }
 
   a->out = out;
   a->query = query;
@@ -170,6 +186,7 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
   a->v_scale = fp8 ? v_scale : 1.f;
   a->out_bf16 = out_dtype == PKV_BF16;
   a->balanced = s.balanced;
+  a->per_head = false;
   set_workspace(a, workspace, s.plan_bytes, s.recs);
   return PKV_OK;
 }
@@ -234,7 +251,7 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
   if (!mul_ok(num_blocks, block_size, INT64_MAX / 4096, &slots)) return PKV_ERR_INVALID_ARG;
   int64_t cache_bytes = 0;
   if (!mul_ok(slots, row, INT64_MAX / 2, &cache_bytes)) return PKV_ERR_INVALID_ARG;
-  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (row % 16 != 0 || num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
@@ -256,7 +273,7 @@ pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, void* key_
       !mul_ok(num_blocks, block_size, INT64_MAX / 4096, &slots) ||
       !mul_ok(slots, row, INT64_MAX / 2, &cache_bytes))
     return PKV_ERR_INVALID_ARG;
-  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (row % 16 != 0 || num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping,
@@ -277,7 +294,7 @@ pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pa
       !mul_ok(row, block_size, INT32_MAX / 2, &block) ||
       !mul_ok(block, num_blocks, INT64_MAX / 2, &cache_bytes))
     return PKV_ERR_INVALID_ARG;
-  if (block % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (block % 16 != 0 || num_pairs > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PKV_OK;
   if (!key_cache || !value_cache || !pairs) return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block,
@@ -322,7 +339,7 @@ pkv_status prologue(const int32_t* block_tables, const int32_t* context_lens, co
   if (!mul_ok(int64_t{num_kv_heads} * head_dim, elem_bytes(kv_dtype), INT32_MAX / 2, &row) ||
       !mul_ok(t, row, INT64_MAX / 2, &cache_bytes))
     return PKV_ERR_INVALID_ARG;
-  if (row % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (row % 16 != 0 || num_seqs >= kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!block_tables || !context_lens || !key || !value || !key_cache || !value_cache ||
       !slot_mapping)
@@ -364,8 +381,8 @@ pkv_status pkv_decode_prologue_fp8(const int32_t* block_tables, const int32_t* c
                                    void* workspace, size_t workspace_bytes, void* stream) {
   return prologue(block_tables, context_lens, key, value, key_cache, value_cache, slot_mapping,
                   num_seqs, max_blocks_per_seq, num_kv_heads, head_dim, block_size, num_blocks,
-                  PKV_FP8_E4M3, true, in_dtype, k_scale, v_scale, 0, workspace,
-                  workspace_bytes, stream);
+                  PKV_FP8_E4M3, true, in_dtype, k_scale, v_scale, PKV_PARTITION_BALANCED,
+                  workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
@@ -401,7 +418,7 @@ pkv_status pkv_paged_attention_partition(void* out, const void* query, const voi
                                          pkv_dtype kv_dtype, pkv_dtype out_dtype,
                                          void* workspace, size_t workspace_bytes, void* stream) {
   if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;   // the _fp8 entry carries scales
-  pkv::AttentionArgs a;
+  pkv::AttentionArgs a{};
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                       block_size, max_blocks_per_seq, num_blocks, scale,
@@ -416,7 +433,7 @@ pkv_status pkv_paged_attention_reduce(void* out, const int32_t* context_lens, in
                                       int32_t max_blocks_per_seq, int32_t partition_size,
                                       pkv_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  pkv::AttentionArgs a;
+  pkv::AttentionArgs a{};
   pkv_status st = fill_attention_args(out, nullptr, nullptr, nullptr, nullptr, context_lens,
                                       num_seqs, num_heads, 0, head_dim, block_size,
                                       max_blocks_per_seq, 0, 1.0f, partition_size, PKV_F32,
@@ -434,13 +451,53 @@ pkv_status pkv_paged_attention_decode(void* out, const void* query, const void* 
                                       pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;   // the _fp8 entry carries scales
-  pkv::AttentionArgs a;
+  pkv::AttentionArgs a{};
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                       block_size, max_blocks_per_seq, num_blocks, scale,
                                       partition_size, kv_dtype, out_dtype, workspace,
                                       workspace_bytes, true, &a);
   if (st != PKV_OK || num_seqs == 0) return st;
+  return run_decode(a, stream);
+}
+
+pkv_status pkv_paged_attention_partition_per_head(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (kv_dtype == PKV_FP8_E4M3 || partition_size == PKV_PARTITION_BALANCED)
+    return PKV_ERR_INVALID_ARG;
+  pkv::AttentionArgs a{};
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      partition_size, kv_dtype, out_dtype, workspace,
+                                      workspace_bytes, true, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.per_head = true;
+  return hip_status(pkv::launch_attention_partition(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_paged_attention_decode_per_head(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (kv_dtype == PKV_FP8_E4M3 || partition_size == PKV_PARTITION_BALANCED)
+    return PKV_ERR_INVALID_ARG;
+  pkv::AttentionArgs a{};
+  pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      partition_size, kv_dtype, out_dtype, workspace,
+                                      workspace_bytes, true, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.per_head = true;
   return run_decode(a, stream);
 }
 
@@ -454,12 +511,12 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
                                              float scale, float k_scale, float v_scale,
                                              pkv_dtype out_dtype, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  pkv::AttentionArgs a;
+  pkv::AttentionArgs a{};
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
-                                      block_size, max_blocks_per_seq, num_blocks, scale, 0,
-                                      PKV_FP8_E4M3, out_dtype, workspace, workspace_bytes, true,
-                                      &a, k_scale, v_scale);
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      PKV_PARTITION_BALANCED, PKV_FP8_E4M3, out_dtype, workspace,
+                                      workspace_bytes, true, &a, k_scale, v_scale);
   if (st != PKV_OK || num_seqs == 0) return st;
   return hip_status(pkv::launch_attention_partition(a, static_cast<hipStream_t>(stream)));
 }
@@ -473,12 +530,12 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, const void* query, const vo
                                           float scale, float k_scale, float v_scale,
                                           pkv_dtype out_dtype, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  pkv::AttentionArgs a;
+  pkv::AttentionArgs a{};
   pkv_status st = fill_attention_args(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
-                                      block_size, max_blocks_per_seq, num_blocks, scale, 0,
-                                      PKV_FP8_E4M3, out_dtype, workspace, workspace_bytes, true,
-                                      &a, k_scale, v_scale);
+                                      block_size, max_blocks_per_seq, num_blocks, scale,
+                                      PKV_PARTITION_BALANCED, PKV_FP8_E4M3, out_dtype, workspace,
+                                      workspace_bytes, true, &a, k_scale, v_scale);
   if (st != PKV_OK || num_seqs == 0) return st;
   return run_decode(a, stream);
 }
@@ -614,6 +671,7 @@ pkv_status pkv_paged_attention_multi_query(void* out, const void* query, const v
     return PKV_ERR_UNSUPPORTED;
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;   // the merge: a workgroup per token
   if (num_tokens == 0) return PKV_OK;
   if (num_seqs == 0) return PKV_ERR_INVALID_ARG;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||

@@ -62,9 +62,12 @@ struct AttentionArgs {
   float* ws_m;              // [num_seqs][num_heads][max_parts]
   float* ws_l;              // [num_seqs][num_heads][max_parts]
   float* ws_o;              // [num_seqs][num_heads][max_parts][head_dim]
-  // Balanced mode (partition_size 0): the tile plan, and the partial results of the
+  // Balanced mode (PKV_PARTITION_BALANCED): the tile plan, and the partial results of the
   // segments, one record row per (segment label, query head).
   bool balanced;
+  // Fixed partitions in the per-head layout (one workgroup per kv head, partition and
+  // sequence, loads through the caches) instead of the streaming kernel.
+  bool per_head;
   int* tile_hdr;            // [0] total tiles, [1] workgroups per kv-head group
   int* tile_cum;            // [num_seqs + 1] tiles before each sequence
   // Multi-token steps: the flat token batch and the units of the work list (a unit is

@@ -17,6 +17,10 @@ import torch
 from . import _lib
 
 _KV_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+# partition_size: 0 = fixed partitions of 512 tokens; PARTITION_BALANCED = the balanced
+# split (equal shares of the batch's tile list per workgroup)
+PARTITION_DEFAULT = _lib.PKV_PARTITION_DEFAULT
+PARTITION_BALANCED = _lib.PKV_PARTITION_BALANCED
 # E4M3 caches hold raw codes: uint8, or torch's float8_e4m3fn (the same format)
 _FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
@@ -216,6 +220,26 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
     return out
 
 
+def paged_attention_decode_per_head(query: torch.Tensor, key_cache: torch.Tensor,
+                                    value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                    context_lens: torch.Tensor, scale: float,
+                                    partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                                    out_dtype: torch.dtype = torch.float32,
+                                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode with fixed partitions in the per-head layout (for batches
+    whose sequences share prefix blocks)."""
+    dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
+        partition_size)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_decode_per_head(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb, _stream(query))
+    _lib.check(st, "pkv_paged_attention_decode_per_head")
+    return out
+
+
 def paged_attention_plan(context_lens: torch.Tensor, workspace: torch.Tensor, block_size: int,
                          max_blocks_per_seq: int, partition_size: int = 0) -> torch.Tensor:
     """Stage 1 of paged_attention_decode: the work list, written into ``workspace``."""
@@ -232,7 +256,7 @@ def paged_attention_plan(context_lens: torch.Tensor, workspace: torch.Tensor, bl
 
 
 def _partition_args(query, key_cache, value_cache, block_tables, context_lens, scale,
-                    partition_size, out, out_dtype, workspace, stream):
+                    partition_size, out, out_dtype, workspace, stream, per_head=False):
     dt, out, ws, wsb, B, H, Hkv, D, BS, NB = _attention_args(
         query, key_cache, value_cache, block_tables, context_lens, out, out_dtype, workspace,
         partition_size)
@@ -240,7 +264,8 @@ def _partition_args(query, key_cache, value_cache, block_tables, context_lens, s
             _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
             int(partition_size), dt, _KV_DTYPES[out.dtype], _ptr(ws), wsb,
             stream if stream is not None else _stream(query))
-    return "pkv_paged_attention_partition", args, out, ws
+    name = "pkv_paged_attention_partition" + ("_per_head" if per_head else "")
+    return name, args, out, ws
 
 
 def paged_attention_partition(query, key_cache, value_cache, block_tables, context_lens, scale,
@@ -249,6 +274,17 @@ def paged_attention_partition(query, key_cache, value_cache, block_tables, conte
     name, args, out, ws = _partition_args(query, key_cache, value_cache, block_tables,
                                           context_lens, scale, partition_size, out, out_dtype,
                                           workspace, None)
+    _call(name, args)
+    return out, ws
+
+
+def paged_attention_partition_per_head(query, key_cache, value_cache, block_tables, context_lens,
+                                       scale, partition_size=0, out=None, out_dtype=torch.float32,
+                                       workspace=None):
+    """Stage 2 in the per-head layout of fixed partitions; returns (out, workspace)."""
+    name, args, out, ws = _partition_args(query, key_cache, value_cache, block_tables,
+                                          context_lens, scale, partition_size, out, out_dtype,
+                                          workspace, None, per_head=True)
     _call(name, args)
     return out, ws
 
@@ -280,14 +316,14 @@ def paged_attention_reduce(out: torch.Tensor, context_lens: torch.Tensor, worksp
 
 def decode_step(query, key, value, key_cache, value_cache, block_tables, context_lens, scale,
                 partition_size=0, out=None, out_dtype=torch.float32, workspace=None,
-                slots=None):
+                slots=None, per_head=False):
     """One decode step on the GPU: slot mapping, cache write, paged attention."""
     NB, BS = key_cache.shape[0], key_cache.shape[1]
     slots = slot_mapping(block_tables, context_lens, BS, NB, out=slots)
     kv_cache_write(key, value, key_cache, value_cache, slots)
-    return paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
-                                  partition_size, out=out, out_dtype=out_dtype,
-                                  workspace=workspace)
+    attend = paged_attention_decode_per_head if per_head else paged_attention_decode
+    return attend(query, key_cache, value_cache, block_tables, context_lens, scale,
+                  partition_size, out=out, out_dtype=out_dtype, workspace=workspace)
 
 
 # ---- steps with several new tokens per sequence ---------------------------------------
@@ -457,7 +493,7 @@ def _fp8_attention_args(query, key_cache, value_cache, block_tables, context_len
         raise ValueError("out must be float32/bfloat16 [B, H, D]")
     _dev(out, "out")
     if workspace is None:
-        workspace = alloc_workspace(query, block_tables, BS, 0)
+        workspace = alloc_workspace(query, block_tables, BS, PARTITION_BALANCED)
     _dev(workspace, "workspace")
     _same_device(query, key_cache, value_cache, block_tables, context_lens, out, workspace)
     return out, workspace, workspace.numel() * workspace.element_size(), B, H, Hkv, D, BS, NB
@@ -512,18 +548,24 @@ class DecodeStep:
     the stored pointers and sizes, on the stream given (default: the current stream of
     the query's device at construction).  The tensors' contents may change between
     calls (new tokens, longer contexts, new block tables); their storage, shapes and
-    dtypes must not.  E4M3 caches (uint8 or float8_e4m3fn) take ``k_scale`` and
-    ``v_scale`` and always use the balanced split."""
+    dtypes must not.  ``partition_size`` None is the library default (512-token
+    partitions); ``per_head`` selects the per-head layout of fixed partitions.  E4M3
+    caches (uint8 or float8_e4m3fn) take ``k_scale`` and ``v_scale`` and always use the
+    balanced split."""
 
     def __init__(self, query, key, value, key_cache, value_cache, block_tables, context_lens,
-                 scale, partition_size=0, out=None, out_dtype=torch.float32, workspace=None,
-                 slot_mapping=None, k_scale=None, v_scale=None, stream=None):
+                 scale, partition_size=None, out=None, out_dtype=torch.float32, workspace=None,
+                 slot_mapping=None, k_scale=None, v_scale=None, stream=None, per_head=False):
         _dev(query, "query")
         fp8 = isinstance(key_cache, torch.Tensor) and key_cache.dtype in _FP8_DTYPES
         if fp8 and (k_scale is None or v_scale is None):
             raise ValueError("E4M3 caches need k_scale and v_scale")
-        if fp8 and partition_size != 0:
-            raise ValueError("E4M3 caches use the balanced split (partition_size 0)")
+        if partition_size is None:
+            partition_size = PARTITION_BALANCED if fp8 else PARTITION_DEFAULT
+        if fp8 and (partition_size != PARTITION_BALANCED or per_head):
+            raise ValueError("E4M3 caches use the balanced split (PARTITION_BALANCED)")
+        if per_head and partition_size == PARTITION_BALANCED:
+            raise ValueError("the per-head layout runs fixed partitions only")
         if stream is None:
             stream = torch.cuda.current_stream(query.device)
         st = ctypes.c_void_p(stream.cuda_stream)
@@ -543,7 +585,7 @@ class DecodeStep:
                                             slot_mapping, st)
             self._partition = _partition_args(query, key_cache, value_cache, block_tables,
                                               context_lens, scale, partition_size, out,
-                                              out_dtype, workspace, st)
+                                              out_dtype, workspace, st, per_head=per_head)
         self.slot_mapping = self._prologue[2]
         self.out, self.workspace = self._partition[2], self._partition[3]
         self._reduce = _reduce_args(self.out, context_lens, workspace, BS, block_tables.shape[1],

@@ -24,15 +24,20 @@ def device_meta(b):
     return bt, cl
 
 
-def run_step(b, partition_size=0, out_dtype=torch.float32, caches=None):
-    """Slot mapping, cache write (into copies unless ``caches`` is given), attention."""
+BAL = pkv.PARTITION_BALANCED
+
+
+def run_step(b, partition_size=0, out_dtype=torch.float32, caches=None, per_head=False):
+    """Slot mapping, cache write (into copies unless ``caches`` is given), attention
+    (partition_size 0: 512-token partitions; BAL: the balanced split; per_head: fixed
+    partitions in the per-head layout)."""
     kc, vc = caches if caches is not None else (b.key_cache.clone(), b.value_cache.clone())
     bt, cl = device_meta(b)
     NB, BS = kc.shape[0], kc.shape[1]
     slots = pkv.slot_mapping(bt, cl, BS, NB)
     pkv.kv_cache_write(b.key, b.value, kc, vc, slots)
-    out = pkv.paged_attention_decode(b.query, kc, vc, bt, cl, b.scale, partition_size,
-                                     out_dtype=out_dtype)
+    attend = pkv.paged_attention_decode_per_head if per_head else pkv.paged_attention_decode
+    out = attend(b.query, kc, vc, bt, cl, b.scale, partition_size, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return slots, kc, vc, out
 

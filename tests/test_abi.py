@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
 OK, INV, UNS, WS = (_lib.PKV_OK, _lib.PKV_ERR_INVALID_ARG, _lib.PKV_ERR_UNSUPPORTED,
                     _lib.PKV_ERR_WORKSPACE)
-F32, BF16 = _lib.PKV_F32, _lib.PKV_BF16
+F32, BF16, FP8 = _lib.PKV_F32, _lib.PKV_BF16, _lib.PKV_FP8_E4M3
 FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every case fails validation first
 NULL = ctypes.c_void_p(0)
 
@@ -66,20 +66,40 @@ def _ws_balanced(B, H, D, max_wgs=1024):
     return plan + (max_wgs + B) * H * (D + 2) * 4
 
 
+BAL = _lib.PKV_PARTITION_BALANCED
+
+
+def test_partition_size_constants():
+    # 0 names the default of 512-token partitions; -1 the balanced split
+    assert _lib.PKV_PARTITION_DEFAULT == 0 and _lib.PKV_DEFAULT_PARTITION_TOKENS == 512
+    assert BAL == -1
+    text = open(HEADER).read()
+    assert "#define PKV_PARTITION_DEFAULT 0" in text
+    assert "#define PKV_DEFAULT_PARTITION_TOKENS 512" in text
+    assert "#define PKV_PARTITION_BALANCED (-1)" in text
+    assert f"#define PKV_ABI_VERSION {_lib.ABI_VERSION}" in text
+
+
 def test_workspace_bytes_formula(lib):
     # plan (256 + roundup256(B*NP*16)) + B * H * NP * (D + 2) * 4, NP = ceil(MB*BS/P)
     assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 512) == _ws(256, 32, 128, 16)
     assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 512) == _ws(8, 32, 128, 256)
-    # partition_size 0 (balanced split): tile plan 256 + roundup256((B + 1) * 4), then one
-    # record row per (segment label < 1024 + B, head)
-    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == _ws_balanced(8, 32, 128)
+    # partition_size 0 is the default of 512-token partitions, exactly P = 512
+    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, 0) == _ws(8, 32, 128, 256)
+    assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 0) == _ws(256, 32, 128, 16)
+    assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 0) == _ws(4, 4, 64, 1)
+    # the balanced split: tile plan 256 + roundup256((B + 1) * 4), then one record row
+    # per (segment label < 1024 + B, head)
+    assert lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 16, 8192, BAL) == _ws_balanced(8, 32, 128)
     assert _ws_balanced(8, 32, 128) == 512 + 1032 * 32 * 130 * 4
-    assert lib.pkv_paged_attention_workspace_bytes(300, 4, 64, 16, 7, 0) == _ws_balanced(300, 4, 64)
+    assert lib.pkv_paged_attention_workspace_bytes(300, 4, 64, 16, 7, BAL) == _ws_balanced(300, 4, 64)
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 512) == _ws(4, 4, 64, 1)
     assert _ws(4, 4, 64, 1) == 512 + 4 * 4 * 66 * 4
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, 24) == 0     # P % 16
     assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 32, 7, 16) == 0     # P % BS
     assert lib.pkv_paged_attention_workspace_bytes(-1, 4, 64, 16, 7, 0) == 0
+    assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, -2) == 0     # no such mode
+    assert lib.pkv_paged_attention_workspace_bytes(4, 4, 64, 16, 7, -512) == 0
 
 
 def _decode(lib, **kw):
@@ -114,9 +134,48 @@ def _decode(lib, **kw):
     (dict(H=128, Hkv=8), UNS),         # group of 16
     (dict(ws=NULL), WS),
     (dict(wsb=16), WS),
+    (dict(P=-2), INV),                 # negative values other than the balanced split
+    (dict(P=-512), INV),
+    # more threads in x than a launch holds: 2^16 sequences x 8192 partitions of 16
+    # tokens x 512 threads
+    (dict(B=1 << 16, MB=8192, P=16, wsb=1 << 62), UNS),
 ])
 def test_decode_rejects(lib, cpu_only, kw, status):
     assert _decode(lib, **kw) == status
+
+
+def test_default_partition_needs_the_default_workspace(lib, cpu_only):
+    # P = 0 takes the fixed-partition workspace of P = 512, not the balanced one
+    need = _ws(4, 32, 128, 2)                          # MB 64 x 16 tokens = 2 partitions
+    assert _decode(lib, P=0, wsb=need - 1) == WS
+    need_bal = _ws_balanced(4, 32, 128)
+    assert need_bal > need
+    assert _decode(lib, P=BAL, wsb=need_bal - 1) == WS
+
+
+def _per_head(lib, fn="pkv_paged_attention_decode_per_head", **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, B=4, H=32, Hkv=8, D=128,
+             BS=16, MB=64, NB=1024, scale=0.088, P=0, kvd=BF16, outd=F32, ws=FAKE,
+             wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return getattr(lib, fn)(a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["B"],
+                            a["H"], a["Hkv"], a["D"], a["BS"], a["MB"], a["NB"], a["scale"],
+                            a["P"], a["kvd"], a["outd"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["pkv_paged_attention_decode_per_head",
+                                "pkv_paged_attention_partition_per_head"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=BAL), INV),                # fixed partitions only
+    (dict(kvd=FP8), INV),
+    (dict(query=NULL), INV),
+    (dict(D=96), UNS),
+    (dict(H=24), UNS),
+    (dict(wsb=16), WS),
+    (dict(B=0, out=NULL, query=NULL, kc=NULL, vc=NULL, bt=NULL, cl=NULL, ws=NULL, wsb=0), OK),
+])
+def test_per_head_rejects(lib, cpu_only, fn, kw, status):
+    assert _per_head(lib, fn=fn, **kw) == status
 
 
 def test_decode_empty_batch_is_noop(lib, cpu_only):
@@ -128,7 +187,9 @@ def test_plan_rejects(lib, cpu_only):
     p = lib.pkv_paged_attention_plan
     assert p(NULL, 4, 16, 64, 0, FAKE, 1 << 20, NULL) == INV
     assert p(FAKE, 4, 16, 64, 24, FAKE, 1 << 20, NULL) == INV          # P % 16
-    assert p(FAKE, 4, 16, 64, 0, FAKE, 300, NULL) == WS                # needs 256 + 256
+    assert p(FAKE, 4, 16, 64, -3, FAKE, 1 << 20, NULL) == INV
+    assert p(FAKE, 4, 16, 64, BAL, FAKE, 300, NULL) == WS              # needs 256 + 256
+    assert p(FAKE, 4, 16, 64, 0, FAKE, 300, NULL) == WS                # 256 + 256 (4 items)
     assert p(FAKE, 4, 16, 64, 0, NULL, 1 << 20, NULL) == WS
     assert p(NULL, 0, 16, 64, 0, NULL, 0, NULL) == OK
 
@@ -195,9 +256,6 @@ def test_binding_fails_loudly_without_gpu_tensors():
     kc = torch.zeros((64, 16, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         pkv.DecodeStep(q, kv, kv, kc, kc, bt, cl, 0.1)
-
-
-FP8 = _lib.PKV_FP8_E4M3
 
 
 def _decode_fp8(lib, B=4, H=32, Hkv=8, D=128, BS=16, MB=64, NB=1024, scale=0.1, ks=0.5, vs=0.5,

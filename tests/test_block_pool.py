@@ -296,6 +296,14 @@ def test_library_pool_rejects_bad_calls_without_changing_state(pkv):
     with pytest.raises(pkv.PkvError):
         lib.append_slots(tables, lens, [5], 16)   # 5 tokens but an empty table
     assert lib.num_free == 3
+    # a refused release leaves no count behind: after a fork the same list is valid
+    lib.fork([a])
+    b = lib.allocate()
+    with pytest.raises(pkv.PkvError):
+        lib.release([b, a, a, a])                 # a holds 2 references, not 3
+    assert lib.ref_count(a) == 2 and lib.ref_count(b) == 1
+    lib.release([a, b, a])
+    assert lib.ref_count(a) == 0 and lib.ref_count(b) == 0 and lib.num_free == 4
 
 
 # ----------------------------------------------------------------------------------
@@ -329,7 +337,7 @@ def test_copy_blocks_bit_exact(pkv, dtype, Hkv, D, BS):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("P", [0, 512])
+@pytest.mark.parametrize("P", [-1, 512])          # the balanced split; 512-token partitions
 def test_copy_on_write_decode_step_matches_oracle(pkv, P):
     """Beams forked from one prompt whose last block is partly filled: the pool sends
     every beam but one to a fresh copy of that block, the copies run on the GPU, the

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import paged_kv_cache_441_amd as pkv
-from gpu_helpers import (ATOL, bits, check_cache_write, device_meta, max_err, oracle_outputs,
-                         require_gpu, run_step)
+from gpu_helpers import (ATOL, BAL, bits, check_cache_write, device_meta, max_err,
+                         oracle_outputs, require_gpu, run_step)
 from workloads import (CONFIGS, build_batch, make_config, permute_physical_blocks,
                        unshare_prefix_blocks)
 from workloads.decode_batches import ConfigSpec
@@ -37,6 +37,17 @@ def config_batch(name):
         torch.cuda.empty_cache()
         _cache[name] = make_config(name, device="cuda")
     return _cache[name]
+
+
+_ref = {}
+
+
+def config_reference(name):
+    """The oracle's output for every sequence of the named workload (computed once)."""
+    if name not in _ref:
+        _ref.clear()
+        _ref[name] = oracle_outputs(config_batch(name))
+    return _ref[name]
 
 
 def spec_of(D=128, G=4, Hkv=2, BS=16, dtype="bf16", NB=4096, seed=5):
@@ -85,31 +96,33 @@ def test_slot_mapping_invalid_inputs_give_minus_one():
 # attention vs the oracle on the named workloads
 # ----------------------------------------------------------------------------
 
-SAMPLES = {
-    "tiny": None,
-    "llama2_7b": None,
-    "llama3_8b": "sample",
-    "long_ctx": [0, 3, 7],
-    "prefix_shared": None,
-}
-
-
-@pytest.mark.parametrize("mode", ["fixed", "balanced"])
+@pytest.mark.parametrize("mode", ["fixed", "balanced", "per_head", "default"])
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_attention_matches_oracle(name, mode):
+    # every sequence of the workload, in each layout: fixed partitions of the
+    # workload's own size (512 where it names none), the balanced split, fixed
+    # partitions in the per-head layout, and partition_size 0 (the 512 default)
     b = config_batch(name)
-    seqs = SAMPLES[name]
-    if seqs == "sample":
-        order = np.argsort(b.context_lens)
-        seqs = sorted(set(order[:4].tolist() + order[-4:].tolist() + list(range(0, b.num_seqs, 37))))
-    # fixed: the workload's own partition size (512 where it fixes none)
-    P = 0 if mode == "balanced" else (b.spec.partition_size or 512)
-    _, _, _, out = run_step(b, partition_size=P)
-    ref = oracle_outputs(b, seqs)
-    err = max_err(out, ref, seqs)
-    print(f"{name} P={P}: max |gpu - oracle| = {err:.3e} over {len(ref)} sequences")
+    own = b.spec.partition_size if b.spec.partition_size > 0 else 512
+    P = {"fixed": own, "balanced": BAL, "per_head": own, "default": 0}[mode]
+    _, _, _, out = run_step(b, partition_size=P, per_head=mode == "per_head")
+    ref = config_reference(name)
+    err = max_err(out, ref)
+    print(f"{name} {mode} P={P}: max |gpu - oracle| = {err:.3e} over {len(ref)} sequences")
+    assert len(ref) == b.num_seqs
     assert np.isfinite(out.cpu().numpy()).all()
     assert err <= ATOL
+
+
+def test_default_partition_is_512_tokens_bitwise():
+    # partition_size 0 means 512-token partitions: the same bits as P = 512
+    b = build_batch(spec_of(NB=4096), [1, 511, 512, 513, 3000, 9000], device="cuda")
+    o0 = run_step(b, partition_size=0)[3]
+    o512 = run_step(b, partition_size=512)[3]
+    assert torch.equal(bits(o0), bits(o512))
+    h0 = run_step(b, partition_size=0, per_head=True)[3]
+    h512 = run_step(b, partition_size=512, per_head=True)[3]
+    assert torch.equal(bits(h0), bits(h512))
 
 
 BOUNDARY = [1, 15, 16, 17, 511, 512, 513, 1024, 8192]
@@ -121,11 +134,12 @@ BOUNDARY = [1, 15, 16, 17, 511, 512, 513, 1024, 8192]
 ])
 def test_boundary_contexts(D, G, BS, dtype):
     b = build_batch(spec_of(D=D, G=G, BS=BS, dtype=dtype, NB=2048), BOUNDARY, device="cuda")
-    for P in (512, 64, 0):
-        _, _, _, out = run_step(b, partition_size=P)
-        ref = oracle_outputs(b)
+    ref = oracle_outputs(b)
+    for P, per_head in ((512, False), (64, False), (0, False), (BAL, False), (512, True),
+                        (64, True)):
+        _, _, _, out = run_step(b, partition_size=P, per_head=per_head)
         err = max_err(out, ref)
-        print(f"D={D} G={G} BS={BS} {dtype} P={P}: max err {err:.3e}")
+        print(f"D={D} G={G} BS={BS} {dtype} P={P} per_head={per_head}: max err {err:.3e}")
         assert err <= ATOL
 
 
@@ -135,11 +149,13 @@ def test_partitioned_equals_single_partition():
     _, _, _, single = run_step(b, partition_size=MB * 16)
     _, _, _, split = run_step(b, partition_size=512)
     _, _, _, fine = run_step(b, partition_size=16)
-    _, _, _, balanced = run_step(b, partition_size=0)
+    _, _, _, balanced = run_step(b, partition_size=BAL)
+    _, _, _, head_single = run_step(b, partition_size=MB * 16, per_head=True)
+    _, _, _, head_fine = run_step(b, partition_size=16, per_head=True)
     ref = oracle_outputs(b)
-    for o in (single, split, fine, balanced):
+    for o in (single, split, fine, balanced, head_single, head_fine):
         assert max_err(o, ref) <= ATOL
-    for o in (split, fine, balanced):
+    for o in (split, fine, balanced, head_single, head_fine):
         assert (single - o).abs().max().item() <= 2e-5
 
 
@@ -147,26 +163,32 @@ def test_partitioned_equals_single_partition():
 # bitwise invariances
 # ----------------------------------------------------------------------------
 
-def test_block_permutation_invariance_bitwise():
+LAYOUTS = [(0, False), (BAL, False), (0, True)]
+
+
+@pytest.mark.parametrize("P,per_head", LAYOUTS)
+def test_block_permutation_invariance_bitwise(P, per_head):
     b = build_batch(spec_of(NB=1024), [1, 33, 700, 1200, 3000], device="cuda")
     perm = np.random.default_rng(0).permutation(1024)
     pb = permute_physical_blocks(b, perm)
-    o1 = run_step(b)[3]
-    o2 = run_step(pb)[3]
+    o1 = run_step(b, partition_size=P, per_head=per_head)[3]
+    o2 = run_step(pb, partition_size=P, per_head=per_head)[3]
     assert torch.equal(bits(o1), bits(o2))
 
 
-def test_prefix_sharing_equals_private_copies_bitwise():
+@pytest.mark.parametrize("P,per_head", LAYOUTS)
+def test_prefix_sharing_equals_private_copies_bitwise(P, per_head):
     b = config_batch("prefix_shared")
     u = unshare_prefix_blocks(b)
-    o1 = run_step(b)[3]
-    o2 = run_step(u)[3]
+    o1 = run_step(b, partition_size=P, per_head=per_head)[3]
+    o2 = run_step(u, partition_size=P, per_head=per_head)[3]
     assert torch.equal(bits(o1), bits(o2))
 
 
-def test_run_to_run_determinism():
+@pytest.mark.parametrize("P,per_head", LAYOUTS)
+def test_run_to_run_determinism(P, per_head):
     b = build_batch(spec_of(NB=4096), [17, 900, 4000, 8192, 2], device="cuda")
-    outs = [run_step(b)[3] for _ in range(3)]
+    outs = [run_step(b, partition_size=P, per_head=per_head)[3] for _ in range(3)]
     assert torch.equal(bits(outs[0]), bits(outs[1])) and torch.equal(bits(outs[0]), bits(outs[2]))
 
 
@@ -182,33 +204,35 @@ def test_bf16_output_is_rounded_fp32_result():
     assert torch.equal(bits(o16), bits(o32.to(torch.bfloat16)))
 
 
-@pytest.mark.parametrize("P", [512, 0])
-def test_partition_then_reduce_equals_decode(P):
+@pytest.mark.parametrize("P,per_head", [(512, False), (BAL, False), (0, True)])
+def test_partition_then_reduce_equals_decode(P, per_head):
     b = build_batch(spec_of(NB=2048), [3, 513, 2000, 5000], device="cuda")
-    slots, kc, vc, out = run_step(b, partition_size=P)
+    slots, kc, vc, out = run_step(b, partition_size=P, per_head=per_head)
     bt, cl = device_meta(b)
     ws = pkv.alloc_workspace(b.query, bt, 16, P)
     pkv.paged_attention_plan(cl, ws, 16, bt.shape[1], P)
-    out2, ws = pkv.paged_attention_partition(b.query, kc, vc, bt, cl, b.scale, P, workspace=ws)
+    stage = pkv.paged_attention_partition_per_head if per_head else pkv.paged_attention_partition
+    out2, ws = stage(b.query, kc, vc, bt, cl, b.scale, P, workspace=ws)
     pkv.paged_attention_reduce(out2, cl, ws, 16, bt.shape[1], P)
     torch.cuda.synchronize()
     assert torch.equal(bits(out), bits(out2))
 
 
-@pytest.mark.parametrize("P", [128, 0])
-def test_invalid_device_data_gives_nan_rows_only(P):
+@pytest.mark.parametrize("P,per_head", [(128, False), (BAL, False), (128, True)])
+def test_invalid_device_data_gives_nan_rows_only(P, per_head):
     b = build_batch(spec_of(NB=1024), [20, 300, 40, 700], device="cuda")
-    slots, kc, vc, good = run_step(b, partition_size=P)
+    slots, kc, vc, good = run_step(b, partition_size=P, per_head=per_head)
     bt, cl = device_meta(b)
     bt_bad = bt.clone()
     bt_bad[1, 3] = 5000            # out of the pool, inside sequence 1's context
     cl_bad = cl.clone()
     cl_bad[2] = 0                  # empty context
-    out = pkv.paged_attention_decode(b.query, kc, vc, bt_bad, cl_bad, b.scale, P)
+    attend = pkv.paged_attention_decode_per_head if per_head else pkv.paged_attention_decode
+    out = attend(b.query, kc, vc, bt_bad, cl_bad, b.scale, P)
     torch.cuda.synchronize()
     o = out.cpu()
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
-    if P:
+    if P != BAL:
         assert torch.equal(bits(o[[0, 3]]), bits(good.cpu()[[0, 3]]))
     else:
         # the balanced split places its segment boundaries by the whole batch's
@@ -253,14 +277,14 @@ def test_plan_lists_every_partition_longest_first(P):
 
 
 def test_balanced_tile_plan_exact():
-    # partition_size 0: cum[i] = sum over earlier valid sequences of ceil(ctx/16) + 1
+    # the balanced split: cum[i] = sum over earlier valid sequences of ceil(ctx/16) + 1
     # (the per-sequence cost position); header word 0 holds the total
     ctx = np.array([1, 15, 16, 17, 511, 512, 513, 1024, 3000, 8192, 0, 9000, 7], np.int32)
     MB = 8192 // 16
     cl = torch.as_tensor(ctx, device="cuda")
-    ws = torch.full((pkv.workspace_bytes(len(ctx), 4, 64, 16, MB, 0),), 0xAB, dtype=torch.uint8,
-                    device="cuda")
-    pkv.paged_attention_plan(cl, ws, 16, MB, 0)
+    ws = torch.full((pkv.workspace_bytes(len(ctx), 4, 64, 16, MB, BAL),), 0xAB,
+                    dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_plan(cl, ws, 16, MB, BAL)
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     cum = raw[256:256 + 4 * (len(ctx) + 1)].view(np.int32)
@@ -278,14 +302,13 @@ def test_balanced_tile_plan_exact():
 ])
 def test_balanced_split_edge_batches(ctx):
     b = build_batch(spec_of(NB=4096), ctx, device="cuda")
-    _, _, _, out = run_step(b, partition_size=0)
-    seqs = sorted(set(range(0, len(ctx), max(1, len(ctx) // 12))) | {len(ctx) - 1})
-    ref = oracle_outputs(b, seqs)
-    assert max_err(out, ref, seqs) <= ATOL
+    _, _, _, out = run_step(b, partition_size=BAL)
+    ref = oracle_outputs(b)
+    assert max_err(out, ref) <= ATOL
     assert np.isfinite(out.cpu().numpy()).all()
 
 
-@pytest.mark.parametrize("P", [512, 0])
+@pytest.mark.parametrize("P", [512, BAL])
 def test_one_plan_serves_every_layer(P):
     # one plan, then the partition and reduce stages once per layer, with new cache
     # contents each time
@@ -317,9 +340,9 @@ def test_one_plan_serves_every_layer(P):
 def test_balanced_small_batches_and_empty_shares(ctx):
     b = build_batch(spec_of(NB=2048), [max(c, 1) for c in ctx], device="cuda")
     bt, cl = device_meta(b)
-    _, kc, vc, _ = run_step(b, partition_size=0)
+    _, kc, vc, _ = run_step(b, partition_size=BAL)
     cl_in = torch.as_tensor(np.array(ctx, np.int32), device="cuda")
-    out = pkv.paged_attention_decode(b.query, kc, vc, bt, cl_in, b.scale, 0)
+    out = pkv.paged_attention_decode(b.query, kc, vc, bt, cl_in, b.scale, BAL)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     good = [i for i, c in enumerate(ctx) if c >= 1]
@@ -391,8 +414,8 @@ def test_prologue_equals_separate_calls(nseq):
     assert torch.equal(bits(o1), bits(o2))
 
 
-@pytest.mark.parametrize("P", [512, 0])
-def test_prepared_step_equals_per_call_wrappers(P):
+@pytest.mark.parametrize("P,per_head", [(512, False), (BAL, False), (512, True)])
+def test_prepared_step_equals_per_call_wrappers(P, per_head):
     """DecodeStep (arguments checked once, one C call per stage) gives the bits of the
     per-call wrappers, also on a second call after the contexts changed in place."""
     rng = np.random.default_rng(23 + P)
@@ -404,11 +427,11 @@ def test_prepared_step_equals_per_call_wrappers(P):
     kc1, vc1 = b.key_cache.clone(), b.value_cache.clone()
     kc2, vc2 = b.key_cache.clone(), b.value_cache.clone()
     ws1 = pkv.alloc_workspace(b.query, bt, BS, P)
-    ds = pkv.DecodeStep(b.query, b.key, b.value, kc2, vc2, bt, cl, b.scale, P)
+    ds = pkv.DecodeStep(b.query, b.key, b.value, kc2, vc2, bt, cl, b.scale, P, per_head=per_head)
+    stage = pkv.paged_attention_partition_per_head if per_head else pkv.paged_attention_partition
     for _ in range(2):
         s1 = pkv.decode_prologue(bt, cl, b.key, b.value, kc1, vc1, ws1, P)
-        o1, _ = pkv.paged_attention_partition(b.query, kc1, vc1, bt, cl, b.scale, P,
-                                              workspace=ws1)
+        o1, _ = stage(b.query, kc1, vc1, bt, cl, b.scale, P, workspace=ws1)
         pkv.paged_attention_reduce(o1, cl, ws1, BS, bt.shape[1], P)
         o2 = ds()
         torch.cuda.synchronize()
@@ -418,3 +441,5 @@ def test_prepared_step_equals_per_call_wrappers(P):
         cl.sub_(1)   # the bound tensors' contents change between calls
     with pytest.raises(ValueError):
         pkv.DecodeStep(b.query, b.key[:4], b.value, kc2, vc2, bt, cl, b.scale, P)
+    with pytest.raises(ValueError):
+        pkv.DecodeStep(b.query, b.key, b.value, kc2, vc2, bt, cl, b.scale, BAL, per_head=True)

@@ -320,14 +320,18 @@ def test_gpu_decode_over_cached_prefix_blocks_equals_private_copies():
     kcd, vcd, qd, cld = kc.to(dev), vc.to(dev), q.to(dev), ctx.to(dev)
     outs = []
     for tables in (shared_tables, private_tables):
-        for P in (0, 32):
+        for P in (pkv.PARTITION_BALANCED, 32):
             outs.append(pkv.paged_attention_decode(qd, kcd, vcd, pad(tables).to(dev), cld,
                                                    D ** -0.5, P))
+        outs.append(pkv.paged_attention_decode_per_head(qd, kcd, vcd, pad(tables).to(dev), cld,
+                                                        D ** -0.5, 32))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0].view(torch.int32), outs[2].view(torch.int32))
-    assert torch.equal(outs[1].view(torch.int32), outs[3].view(torch.int32))
+    assert torch.equal(outs[0].view(torch.int32), outs[3].view(torch.int32))
+    assert torch.equal(outs[1].view(torch.int32), outs[4].view(torch.int32))
+    assert torch.equal(outs[2].view(torch.int32), outs[5].view(torch.int32))
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
     ref = oracle.paged_attention_decode(bits(q), bits(kc), bits(vc),
                                         pad(shared_tables).numpy(), ctx.numpy(), D ** -0.5,
                                         "bf16")
-    assert np.abs(outs[0].cpu().numpy() - ref).max() <= 2e-3
+    for o in outs[:3]:
+        assert np.abs(o.cpu().numpy() - ref).max() <= 2e-3

@@ -9,6 +9,7 @@ from .decode_batches import (  # noqa: F401
     CONFIGS,
     FP8_CONFIGS,
     MULTI_CONFIGS,
+    PARTITION_BALANCED,
     DecodeBatch,
     build_batch,
     build_fp8_batch,

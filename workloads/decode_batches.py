@@ -38,6 +38,11 @@ _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _INT_VIEW = {"f32": torch.int32, "bf16": torch.int16}
 
 
+# partition_size of the balanced split (the library's PKV_PARTITION_BALANCED); 0 is
+# the library's default of 512-token partitions
+PARTITION_BALANCED = -1
+
+
 def poison_bits(kv_dtype: str) -> int:
     return {"f32": F32_POISON, "bf16": BF16_POISON}[kv_dtype]
 
@@ -56,9 +61,10 @@ class ConfigSpec:
     ctx: tuple                  # ("fixed", lens) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
                                 # | ("prefix", shared_tokens, suffix_lo, suffix_hi)
     seed: int
-    partition_size: int = 512
+    partition_size: int = 512   # tokens per fixed partition, or PARTITION_BALANCED
     share_group: int = 0        # sequences per group sharing a prefix (0: no sharing)
     shared_blocks: int = 0      # physical blocks each group shares
+    per_head: bool = False      # fixed partitions in the per-head layout (shared prefixes)
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -78,20 +84,24 @@ CONFIGS = {
     # workload fixes no partition size either; the balanced split measured faster than
     # 512-token partitions on MI355X (5.97 vs 5.38 TB/s).
     "llama2_7b": ConfigSpec("llama2_7b", 64, 32, 32, 128, 16, 16384, "bf16", 2048,
-                            ("uniform", 128, 2048), 1, partition_size=0),
+                            ("uniform", 128, 2048), 1, partition_size=PARTITION_BALANCED),
     # One Llama-3-8B layer: GQA 32/8, D=128, bf16, lognormal contexts (median 1024,
     # sigma 1.0 in log space), clipped to [16, 8192], 200k-block pool.  The workload
-    # fixes no partition size; it runs in the balanced split (partition_size 0),
-    # which measured fastest on MI355X.
+    # fixes no partition size; it runs in the balanced split, which measured fastest
+    # on MI355X.
     "llama3_8b": ConfigSpec("llama3_8b", 256, 32, 8, 128, 16, 200_000, "bf16", 8192,
-                            ("lognormal", 1024, 1.0, 16, 8192), 2, partition_size=0),
+                            ("lognormal", 1024, 1.0, 16, 8192), 2,
+                            partition_size=PARTITION_BALANCED),
     # Long-context split decode: 8 sequences of 32k..128k tokens, partition 512.
     "long_ctx": ConfigSpec("long_ctx", 8, 32, 8, 128, 16, 65536, "bf16", 131072,
                            ("uniform", 32768, 131072), 3),
     # Prefix sharing: 32 groups of 4 sequences; each group shares its first 64
     # physical blocks (2048 tokens at block size 32); unique suffixes of 16..512 tokens.
+    # 512-token partitions in the per-head layout, whose workgroups of sharing
+    # sequences meet on the shared blocks in the caches.
     "prefix_shared": ConfigSpec("prefix_shared", 128, 32, 8, 128, 32, 16384, "bf16", 2048 + 512,
-                                ("prefix", 2048, 16, 512), 4, share_group=4, shared_blocks=64),
+                                ("prefix", 2048, 16, 512), 4, share_group=4, shared_blocks=64,
+                                per_head=True),
 }
 
 
@@ -353,7 +363,7 @@ MULTI_CONFIGS = {
                     ("fixed_all", 5)),
     "chunked_prefill": (ConfigSpec("chunked_prefill", 4, 32, 8, 128, 16, 16384, "bf16",
                                    8192 + 512, ("uniform", 512, 8192 + 512), 7,
-                                   partition_size=0), ("fixed_all", 512)),
+                                   partition_size=PARTITION_BALANCED), ("fixed_all", 512)),
 }
 
 
@@ -434,10 +444,11 @@ def build_fp8_batch(spec: ConfigSpec, context_lens: Sequence[int], device="cpu",
 
 # E4M3-cache forms of the named workloads: same shapes, context draws and tables.
 FP8_CONFIGS = {
-    "tiny_fp8": replace(CONFIGS["tiny"], name="tiny_fp8", kv_dtype="fp8"),
+    "tiny_fp8": replace(CONFIGS["tiny"], name="tiny_fp8", kv_dtype="fp8",
+                        partition_size=PARTITION_BALANCED),
     "llama3_8b_fp8": replace(CONFIGS["llama3_8b"], name="llama3_8b_fp8", kv_dtype="fp8"),
     "long_ctx_fp8": replace(CONFIGS["long_ctx"], name="long_ctx_fp8", kv_dtype="fp8",
-                            partition_size=0),
+                            partition_size=PARTITION_BALANCED),
 }
 
 
