@@ -74,7 +74,8 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2,  /* a valid combination the library has no kernel for */
   PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   PKV_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
-  PKV_ERR_NO_BLOCKS = 5     /* the block pool has no free block left */
+  PKV_ERR_NO_BLOCKS = 5,    /* the block pool has no free block left */
+  PKV_ERR_SCRATCH_LIMIT = 6 /* more scratch than the no-alloc entry point's fixed buffer */
 } pkv_status;
 
 typedef enum {
@@ -537,6 +538,33 @@ pkv_status pkv_paged_attention_reduce(void* out, const int32_t* context_lens, in
                                       int32_t max_blocks_per_seq, int32_t partition_size,
                                       pkv_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments minus the workspace, same kernels,
+ * same results (bit for bit, for the same partition_size).
+ *
+ * The workspace lives instead in a fixed device array inside the library, one per GPU,
+ * of PKV_NOALLOC_SCRATCH_BYTES (64 MiB); it is set up on the first call on a GPU (the
+ * GPU of `stream`, or the current one for the null stream) and held until the process
+ * ends.  A call whose workspace (pkv_paged_attention_workspace_bytes of the same
+ * arguments) would exceed it returns PKV_ERR_SCRATCH_LIMIT before any GPU work; the
+ * balanced split needs (1024 + num_seqs) * num_heads * (head_dim + 2) * 4 bytes plus
+ * its plan, e.g. 256 sequences of 32 heads of 128 fit.  The call allocates and frees
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from different host threads without ordering) race
+ * and may produce wrong results; calls ordered on one stream are safe.  The array's
+ * contents need no clearing between calls.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+pkv_status pkv_paged_attention_decode_noalloc(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream);
 
 /*
  * The per-head layout of fixed partitions, for batches whose sequences share prefix

@@ -21,6 +21,7 @@ from .ops import (  # noqa: F401
     multi_query_workspace_bytes,
     paged_attention_decode,
     paged_attention_decode_fp8,
+    paged_attention_decode_noalloc,
     paged_attention_decode_per_head,
     paged_attention_partition,
     paged_attention_multi_query,

@@ -20,6 +20,7 @@ PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE = 3
 PKV_ERR_HIP = 4
 PKV_ERR_NO_BLOCKS = 5
+PKV_ERR_SCRATCH_LIMIT = 6
 
 PKV_F32 = 0
 PKV_BF16 = 1
@@ -29,6 +30,7 @@ PKV_FP8_E4M3 = 2
 PKV_PARTITION_DEFAULT = 0          # fixed partitions of PKV_DEFAULT_PARTITION_TOKENS
 PKV_DEFAULT_PARTITION_TOKENS = 512
 PKV_PARTITION_BALANCED = -1        # the balanced split
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -79,6 +81,9 @@ SIGNATURES = {
                                              _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                                           _sz, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _i64, _f32, _i32, _i32, _i32,
+                                                  _vp]),
     "pkv_paged_attention_partition_per_head": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                       _i32, _i32, _i32, _i32, _i64, _f32, _i32,
                                                       _i32, _i32, _vp, _sz, _vp]),

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/pagedkv.h"
 #include "pkv_launch.hpp"
@@ -218,6 +219,8 @@ const char* pkv_status_string(int32_t status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error at launch";
     case PKV_ERR_NO_BLOCKS: return "no free block left in the pool";
+    case PKV_ERR_SCRATCH_LIMIT:
+      return "the call needs more device scratch than the library's fixed buffer holds";
     default: return "unknown status";
   }
 }
@@ -498,6 +501,76 @@ pkv_status pkv_paged_attention_decode_per_head(
                                       workspace_bytes, true, &a);
   if (st != PKV_OK || num_seqs == 0) return st;
   a.per_head = true;
+  return run_decode(a, stream);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing ------------------------------------------
+
+// The device scratch of pkv_paged_attention_decode_noalloc: one copy per GPU, held from
+// the first use on that GPU until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it is only a stand-in for the symbol); it uses the
+// address hipGetSymbolAddress returned for the device, kept in scratch_ptr below.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device of `stream` (the current device for the null
+// stream), looked up once per device with that device current.
+pkv_status device_scratch(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                        : hipGetDevice(&dev);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return PKV_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return PKV_ERR_HIP;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return PKV_ERR_HIP;
+    if (e != hipSuccess || !p) return PKV_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode_noalloc(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t partition_size,
+    pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
+  if (kv_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;   // the _fp8 entry carries scales
+  AttnShape s;
+  pkv_status st = check_attention_shape(num_seqs, num_heads, head_dim, block_size,
+                                        max_blocks_per_seq, partition_size, &s);
+  if (st != PKV_OK) return st;
+  if (s.ws_bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_LIMIT;
+  // every other argument check, with a stand-in workspace that is never dereferenced
+  pkv::AttentionArgs a{};
+  static char stand_in;
+  st = fill_attention_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                           num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, num_blocks, scale, partition_size, kv_dtype,
+                           out_dtype, &stand_in, s.ws_bytes, true, &a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  void* ws = nullptr;
+  st = device_scratch(stream, &ws);
+  if (st != PKV_OK) return st;
+  set_workspace(&a, ws, s.plan_bytes, s.recs);
   return run_decode(a, stream);
 }
 

@@ -220,6 +220,43 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
     return out
 
 
+def paged_attention_decode_noalloc(query: torch.Tensor, key_cache: torch.Tensor,
+                                   value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float,
+                                   partition_size: int = 0,
+                                   out: Optional[torch.Tensor] = None,
+                                   out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """paged_attention_decode with its workspace in the library's fixed device buffer
+    (pkv_paged_attention_decode_noalloc): the library allocates nothing.  Calls that
+    overlap on one GPU race for that buffer."""
+    dt = _kv(query, "query")
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        if _kv(t, n) != dt:
+            raise TypeError(f"{n} dtype differs from query")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    if query.dim() != 3 or key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("query [B, H, D]; caches [NB, BS, Hkv, D]")
+    B, H, D = query.shape
+    NB, BS, Hkv, Dk = key_cache.shape
+    if Dk != D or context_lens.shape != (B,) or block_tables.dim() != 2 or \
+            block_tables.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype, device=query.device)
+    if out.dtype not in _KV_DTYPES or out.shape != (B, H, D):
+        raise ValueError("out must be float32/bfloat16 [B, H, D]")
+    _dev(out, "out")
+    _same_device(query, key_cache, value_cache, block_tables, context_lens, out)
+    lib = _lib.load_library()
+    st = lib.pkv_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), B, H, Hkv, D, BS, block_tables.shape[1], NB, float(scale),
+        int(partition_size), dt, _KV_DTYPES[out.dtype], _stream(query))
+    _lib.check(st, "pkv_paged_attention_decode_noalloc")
+    return out
+
+
 def paged_attention_decode_per_head(query: torch.Tensor, key_cache: torch.Tensor,
                                     value_cache: torch.Tensor, block_tables: torch.Tensor,
                                     context_lens: torch.Tensor, scale: float,
