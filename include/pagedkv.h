@@ -81,7 +81,12 @@ typedef enum {
 typedef enum {
   PKV_F32 = 0,      /* IEEE binary32 */
   PKV_BF16 = 1,     /* bfloat16 (top 16 bits of a binary32) */
-  PKV_FP8_E4M3 = 2  /* OCP 8-bit float E4M3 (cache storage only; see the FP8 section) */
+  PKV_FP8_E4M3 = 2, /* OCP 8-bit float E4M3 (cache storage only; see the FP8 section) */
+  /* Not types: these two make every int32 value a value of pkv_dtype, so that an
+   * unknown code passed by a caller is rejected (PKV_ERR_INVALID_ARG) rather than
+   * being an out-of-range enumeration value. */
+  PKV_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PKV_DTYPE_RANGE_MAX_ = 2147483647
 } pkv_dtype;
 
 /* PKV_ABI_VERSION of the loaded library. */

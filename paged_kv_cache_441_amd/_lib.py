@@ -12,7 +12,9 @@ import threading
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+# PKV_LIBRARY names another build of the same ABI (the host-sanitizer build in
+# tests/host_sanitizers.sh); by default the in-tree libpagedkv.so
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG, "libpagedkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1

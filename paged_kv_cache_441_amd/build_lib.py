@@ -1,11 +1,16 @@
 """Build libpagedkv.so for gfx950 with hipcc (ahead of time, in-tree).
 
-    python -m paged_kv_cache_441_amd.build_lib [--jobs N]
+    python -m paged_kv_cache_441_amd.build_lib [--jobs N] [--host-sanitize]
 
 Objects go to paged_kv_cache_441_amd/_build/, the library to
 paged_kv_cache_441_amd/libpagedkv.so.  Every call recompiles.  The benchmark's
 read-ceiling kernels (csrc/read_ceiling.hip) go to a library of their own,
 libpkv_ceiling.so, which only bench.py loads.
+
+--host-sanitize builds libpagedkv_hostsan.so instead: the same sources with the host
+side (block pool, prefix cache, argument checks, launch set-up) instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer, for CPU-only tests
+(tests/host_sanitizers.sh); the device code is built as usual and never runs there.
 """
 
 from __future__ import annotations
@@ -26,6 +31,11 @@ SOURCES = ["pkv_api.cpp", "block_pool.cpp", "cache_write.hip", "paged_attention.
            "paged_attention_multi.hip"]
 CEILING_SOURCE = "read_ceiling.hip"
 CEILING_LIB = os.path.join(PKG, "libpkv_ceiling.so")
+HOSTSAN_LIB = os.path.join(PKG, "libpagedkv_hostsan.so")
+# each sanitizer flag applies to the host compilation only
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -46,10 +56,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (needs a ROCm install)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), subdir: str = "") -> str:
+    obj = os.path.join(BUILD, subdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -76,11 +86,28 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(jobs: int = 4, verbose: bool = False) -> str:
+    """libpagedkv_hostsan.so: host code under ASan + UBSan.  A shared library does not
+    carry the sanitizer runtime; the process that loads it preloads the ASan runtime
+    (which holds the UBSan handlers too)."""
+    os.makedirs(os.path.join(BUILD, "hostsan"), exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, HOST_SANITIZE, "hostsan"), SOURCES))
+    _link(objs, HOSTSAN_LIB)
+    if verbose:
+        print(f"built {HOSTSAN_LIB}")
+    return HOSTSAN_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--host-sanitize", action="store_true")
     args = ap.parse_args(argv)
-    build(args.jobs, verbose=True)
+    if args.host_sanitize:
+        build_host_sanitized(args.jobs, verbose=True)
+    else:
+        build(args.jobs, verbose=True)
     return 0
 
 
