@@ -44,6 +44,7 @@
 #include "pkv_stream.hpp"
 #include "pkv_tile.hpp"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace pkv {
@@ -630,6 +631,446 @@ void paged_attention_multi_kernel(AttentionArgs a) {
   wait_copies<0>();
 }
 
+// ---- long prompts with bf16 caches: one workgroup per 256-row unit -------------------
+// Chunked prefill hands a few sequences many new tokens each.  There the work is the
+// matrix products, and what costs is re-reading a sequence's context for every unit
+// of its rows.  This mode:
+//  - makes units of 256 rows (kPfWaves waves of two 16-row MFMA blocks sharing one kv
+//    head's staged tiles), one workgroup each, over the unit's whole causal context:
+//    no split, no records, no merge;
+//  - gives the units of one (sequence, kv head) consecutive work-item indices, and
+//    item indices are dealt to the XCDs in equal contiguous ranges, so
+//    the units of a sequence and kv head run side by side on one XCD, reading the
+//    same tiles at about the same time: L2 serves the repeats;
+//  - stages 32-token tiles, so that P.V runs on the full-rate v_mfma_f32_16x16x32_bf16
+//    with k = the lane's four tokens of each 16-token half: the lane's own eight
+//    probabilities form its A operand (as hi and lo bf16 parts, two instructions),
+//    and its B operand packs the matching eight value rows.
+// Rows of a sequence whose context lists a block id outside the pool are all NaN
+// (the workgroup checks the whole table row first).
+constexpr int kPfWaves = kMqPrefillUnit / 32;   // 8 waves, 32 rows each
+constexpr int kPfTok = 32;                       // tokens per tile
+#ifndef PKV_PREFILL_NBUF
+#define PKV_PREFILL_NBUF 4
+#endif
+constexpr int kPfNbuf = PKV_PREFILL_NBUF;        // tiles in the ring
+
+template <int G>
+__global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_attention_prefill_kernel(AttentionArgs a) {
+  constexpr int D = 128;
+  constexpr int RB = 2;                     // 16-row MFMA blocks per wave
+  constexpr int ROWB = D * 2;               // bytes of one head's bf16 row
+  constexpr int SLOTS = ROWB / 16;          // 16-byte slots per row
+  constexpr int TSLOTS = kPfTok * SLOTS;    // slots per tile and cache
+  constexpr int TPB = kMqPrefillUnit / G;   // new tokens per unit
+  constexpr int CPL = D / 16;               // value columns per lane = output blocks
+  static_assert(kPfTok * ROWB == kPfWaves * 1024, "one 1 KiB copy per wave, cache and tile");
+  __shared__ uint4 kring[kPfNbuf][TSLOTS], vring[kPfNbuf][TSLOTS];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int quarter = lane >> 4;
+  const int col = lane & 15;
+  const int Hkv = a.num_kv_heads;
+  const int H = Hkv * G;
+  // the merge that follows only writes the NaN rows of invalid sequences: one share
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.tile_hdr[1] = 1;
+  // the U * Hkv items are dealt to the XCDs in equal contiguous ranges (workgroup b
+  // runs on XCD b % 8): XCD x takes items [x c, (x + 1) c), c = ceil(items / 8), so
+  // no XCD holds more than its share; workgroups past them exit
+  const int U = ((cint32*)a.tile_hdr)[2];
+  const int n_items = U * Hkv;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int slot_in_xcd = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + slot_in_xcd;
+  if (slot_in_xcd >= per_xcd || item >= n_items) return;
+
+  // item -> (sequence, kv head, unit): items of sequence i are seq_unit[i] * Hkv ..,
+  // kv-head-major, so one sequence and kv head's units have consecutive indices
+  cint32* seq_unit = (cint32*)a.seq_unit;
+  int lo = 0, hi = a.num_seqs;              // seq_unit[lo] * Hkv <= item < seq_unit[hi] * Hkv
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (seq_unit[mid] * Hkv <= item) lo = mid; else hi = mid;
+  }
+  const int seq = lo;
+  const int u0 = seq_unit[seq];
+  const int nun = seq_unit[seq + 1] - u0;   // > 0 for the sequence holding the item
+  const int o = item - u0 * Hkv;
+  const int g = o / nun;
+  const int j0 = (o % nun) * TPB;           // first new token of the unit
+  cint32* qsl = (cint32*)a.query_start_loc;
+  const int q0 = qsl[seq];
+  const int qlen = qsl[seq + 1] - q0;
+  const int ctx = ((cint32*)a.context_lens)[seq];
+  const int j1 = min(qlen, j0 + TPB);
+  const int base_pos = ctx - qlen;          // position of new token 0
+  const int ntiles = (base_pos + j1 + kPfTok - 1) / kPfTok;
+
+  const int shift = a.block_shift;
+  const int bs_mask = (1 << shift) - 1;
+  const int MB = a.max_blocks_per_seq;
+  const int num_blocks = (int)a.num_blocks;
+  const int32_t* table = a.block_tables + (int64_t)seq * MB;
+
+  // every block of the context must be in the pool
+  bool bad_lane = false;
+  for (int b = lane; b < ((ctx + bs_mask) >> shift); b += kWave) {
+    const int32_t id = table[b];
+    bad_lane |= id < 0 || id >= num_blocks;
+  }
+  const bool seq_bad = __ballot(bad_lane) != 0;
+
+  // this wave's rows: r = 32 wave + 16 rb + col is new token j0 + r / G with query head
+  // g G + r % G (a row past the last new token repeats token j0 and is not stored)
+  const int wrow0 = wave * 16 * RB;
+  const int wj_lo = j0 + wrow0 / G;
+  const int wj_hi = min(j0 + (wrow0 + 16 * RB - 1) / G, qlen - 1);
+  const bool wave_live = wj_lo < qlen;
+  const int wpos_lo = base_pos + min(wj_lo, qlen - 1);   // positions the wave's rows see
+  const int wpos_hi = base_pos + wj_hi;
+  const int wtiles = wave_live ? wpos_hi / kPfTok + 1 : 0;
+
+  // queries; for a negative scale the query's sign bits are flipped (exact) so that
+  // the scale is positive and a row's largest raw score is its largest scaled one
+  // (a zero scale becomes the smallest normal float: every 2^(s * scale) is then 1 as
+  // for zero, and a masked -inf score stays -inf instead of turning NaN)
+  const float scale = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  uint4 qa[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wrow0 + rb * 16 + col;
+    const int jq = j0 + r / G < qlen ? j0 + r / G : j0;
+    const char* row = static_cast<const char*>(a.query) +
+                      ((int64_t)(q0 + jq) * H + g * G + r % G) * ROWB;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 v = *reinterpret_cast<const uint4*>(row + (4 * c + quarter) * 16);
+      v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+      qa[rb][c] = v;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // copies: wave w brings rows 4w .. 4w + 3 of each tile, lane l row 4w + l / 16, its
+  // 16-byte piece l % 16 stored at slot (l % 16) ^ row (rows are 16 slots)
+  const int64_t row_stride = (int64_t)Hkv * ROWB;
+  const int crow = 4 * wave + quarter;
+  const uint32_t copy_off = (uint32_t)(quarter * row_stride) + (uint32_t)(((col ^ crow) & 15) * 16);
+  const char* kcache = static_cast<const char*>(a.key_cache) + g * ROWB;
+  const char* vcache = static_cast<const char*>(a.value_cache) + g * ROWB;
+  auto issue = [&](int tt, int slot) {
+    int64_t off = 0;                        // rows past the context: the pool's first rows
+    const int t0 = tt * kPfTok + 4 * wave;
+    if (tt < ntiles && t0 < ctx) {
+      const int32_t blk = uniform(((cint32*)table)[t0 >> shift]);
+      if (blk >= 0 && blk < num_blocks) off = (((int64_t)blk << shift) + (t0 & bs_mask)) * row_stride;
+    }
+    dma16<Cpol::kDefault>(kcache + off, copy_off, lds_addr(kring[slot]) + wave * 1024);
+    dma16<Cpol::kDefault>(vcache + off, copy_off, lds_addr(vring[slot]) + wave * 1024);
+  };
+
+  const float kNegInf = -__builtin_inff();
+  float m_run[RB], l_lane[RB];
+  floatx4 acc[RB][CPL];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_lane[rb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[rb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // S^T = K . Q^T of a tile's two 16-token halves (raw, unscaled): lane (quarter q,
+  // column n) gets row n's scores of tokens 16 h + 4 q + i in s[rb][4 h + i]
+  auto scores = [&](const uint4* kb, float (&sv)[RB][8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 kk[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kk[c] = kb[(16 * h + col) * SLOTS + ((4 * c + quarter) ^ col)];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const floatx4 s4 = tile_scores<BF16, 4>(kk, qa[rb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[rb][4 * h + i] = s4[i];
+      }
+    }
+  };
+  // the causal edge: tokens past a row's position get -inf (a branch taken on the last
+  // tiles of the wave's rows only)
+  auto mask_edge = [&](int tt, float (&sv)[RB][8]) {
+    const int tok0 = tt * kPfTok;
+    if (tok0 + kPfTok - 1 > wpos_lo) {
+      keep_branch();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) sv[rb][k] = kNegInf;
+      }
+    }
+  };
+  // the running maxima after a tile (base-2 domain; raw scores, positive scale): a row
+  // takes a new maximum only when it exceeds the old one by more than 2^8, and then
+  // its earlier terms are scaled by alpha; returns whether any row of the wave rose
+  auto maxima = [&](const float (&sv)[RB][8], float (&mnew)[RB], float (&alpha)[RB]) {
+    constexpr float kRebase = 8.f;
+    bool rise = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float a3 = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), sv[rb][2]);
+      const float b3 = fmaxf(fmaxf(sv[rb][3], sv[rb][4]), sv[rb][5]);
+      const float c3 = fmaxf(fmaxf(sv[rb][6], sv[rb][7]), a3);
+      const float mx = max_xor32(max_xor16(fmaxf(b3, c3))) * scale;
+      const bool up = mx > m_run[rb] + kRebase;
+      mnew[rb] = up ? mx : m_run[rb];
+      alpha[rb] = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
+      rise |= up;
+    }
+    return __ballot(rise) != 0;
+  };
+  // probabilities of a tile relative to mnew, as bf16 hi + lo parts (together exact
+  // to about 2^-17 of p), and their sums per lane
+  auto probs = [&](const float (&sv)[RB][8], const float (&mnew)[RB], bf16x8 (&ph)[RB],
+                   bf16x8 (&pl)[RB], float (&lsum)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float nref = mnew[rb] == kNegInf ? 0.f : -mnew[rb];
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        p[k] = fast_exp2(fmaf(sv[rb][k], scale, nref));   // 0 for masked tokens
+        lsum[rb] += p[k];
+      }
+      // lo = p - hi as one bf16 dot product per value, (hi0, hi1) . (-1, 0) + p0: the
+      // products are exact and so is the difference, which fp32 holds.  The pair
+      // (-1, 0) is 0x0000bf80; it is moved into a scalar register here because the
+      // compiler would otherwise encode it as the inline constant -1.0, which the
+      // instruction reads as 0xbf800000, i.e. (0, -1).
+      uint32_t kneg0;
+      asm("s_mov_b32 %0, 0xbf80" : "=s"(kneg0));
+      const bf16x2 neg0 = __builtin_bit_cast(bf16x2, kneg0);
+      const bf16x2 neg1 = __builtin_bit_cast(bf16x2, 0xbf800000u);
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        const floatx2 pp = {p[k], p[k + 1]};
+        const bf16x2 h2 = __builtin_convertvector(pp, bf16x2);
+        const floatx2 rr = {__builtin_amdgcn_fdot2_f32_bf16(h2, neg0, p[k], false),
+                            __builtin_amdgcn_fdot2_f32_bf16(h2, neg1, p[k + 1], false)};
+        const bf16x2 l2 = __builtin_convertvector(rr, bf16x2);
+        ph[rb][k] = h2[0]; ph[rb][k + 1] = h2[1];
+        pl[rb][k] = l2[0]; pl[rb][k + 1] = l2[1];
+      }
+    }
+  };
+  // half hv of the value rows of the lane's eight tokens: columns 8 col + 4 hv ..
+  // 8 col + 4 hv + 3 (two words of each row); rows past the context (which may hold
+  // NaN) zeroed when zero_tail
+  auto read_v = [&](int tt, const uint4* vb, int hv, uint32_t (&w)[8][2], bool zero_tail) {
+#pragma unroll
+    for (int sr = 0; sr < 8; ++sr) {
+      const int vr = 16 * (sr >> 2) + 4 * quarter + (sr & 3);
+      const uint2 c = reinterpret_cast<const uint2*>(vb)[2 * (vr * SLOTS + (col ^ (vr & 15))) + hv];
+      w[sr][0] = c.x; w[sr][1] = c.y;
+    }
+    if (zero_tail && tt * kPfTok + kPfTok > ctx) {
+      keep_branch();
+#pragma unroll
+      for (int sr = 0; sr < 8; ++sr)
+        if (tt * kPfTok + 16 * (sr >> 2) + 4 * quarter + (sr & 3) >= ctx) w[sr][0] = w[sr][1] = 0u;
+    }
+  };
+  // acc += P . V for output blocks 4 hv .. 4 hv + 3 on v_mfma_f32_16x16x32_bf16: block e
+  // is column 8 col + e of the eight token rows (even e the low bf16 of a word, odd e
+  // the high one)
+  auto pv = [&](const uint32_t (&w)[8][2], int hv, const bf16x8 (&ph)[RB], const bf16x8 (&pl)[RB]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * hv + k;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int d = k >> 1;
+      uint4 bw;
+      bw.x = __builtin_amdgcn_perm(w[1][d], w[0][d], sel);
+      bw.y = __builtin_amdgcn_perm(w[3][d], w[2][d], sel);
+      bw.z = __builtin_amdgcn_perm(w[5][d], w[4][d], sel);
+      bw.w = __builtin_amdgcn_perm(w[7][d], w[6][d], sel);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rb], bv, acc[rb][e], 0, 0, 0);
+        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rb], bv, acc[rb][e], 0, 0, 0);
+      }
+    }
+  };
+  auto rescale = [&](const float (&alpha)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha[rb], 4 * quarter + i);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[rb][e][i] *= ai;
+      }
+  };
+
+  // The tile loop, pipelined one tile deep.  Step t (tile t sits in ring slot
+  // t % kPfNbuf) starts with the scores of tile t in registers, masked, and the running
+  // maxima already raised for them.  It waits for this wave's copies of tile t + 1,
+  // passes one barrier (every wave's copies of tile t + 1 have landed; every wave is
+  // done with step t - 1 and so with tile t - 1), issues tile t + kPfNbuf - 1 into
+  // tile t - 1's slot, and then runs one block of straight-line work: the scores of
+  // tile t + 1 on the matrix cores beside the probabilities of tile t on the vector
+  // unit, then P.V of tile t on the matrix cores beside the value permutes of tile t
+  // and the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
+  // matrix instructions but not another wave's, so the block interleaves them
+  // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
+  // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
+  // branch).  The wave's last steps take a general path with the conditions.
+  static_assert(kPfNbuf >= 4, "tiles t and t + 1 stay staged while t + 2 lands");
+  constexpr int kAhead = (kPfNbuf - 3) * 2;   // copies of later tiles left in flight
+#pragma unroll
+  for (int i = 0; i < kPfNbuf - 1; ++i) issue(i, i);
+  float sA[RB][8], sB[RB][8];
+  wait_copies<kAhead + 2>();                  // tile 0
+  bare_barrier();
+  if (wtiles > 0) {
+    scores(kring[0], sA);
+    mask_edge(0, sA);
+    float mnew[RB], alpha[RB];
+    maxima(sA, mnew, alpha);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) m_run[rb] = mnew[rb];
+  }
+
+  auto step = [&](int tt, float (&s_cur)[RB][8], float (&s_nxt)[RB][8]) {
+    wait_copies<kAhead>();                    // tile tt + 1
+    bare_barrier();
+    issue(tt + kPfNbuf - 1, (tt + kPfNbuf - 1) % kPfNbuf);
+    float mnew[RB], alpha[RB], lsum[RB] = {0.f, 0.f};
+    bf16x8 ph[RB], pl[RB];
+    bool rise = false;
+    if (tt + 1 < wtiles) {
+      // tile tt is not the unit's last, so its value rows are all inside the context
+      auto block = [&](bool edge) {
+        uint32_t w0[8][2], w1[8][2];
+        scores(kring[(tt + 1) % kPfNbuf], s_nxt);
+        read_v(tt, vring[tt % kPfNbuf], 0, w0, false);
+        probs(s_cur, m_run, ph, pl, lsum);
+        if (edge) {
+          const int tok0 = (tt + 1) * kPfTok;
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) s_nxt[rb][k] = kNegInf;
+          }
+        }
+        pv(w0, 0, ph, pl);
+        read_v(tt, vring[tt % kPfNbuf], 1, w1, false);
+        pv(w1, 1, ph, pl);
+        rise = maxima(s_nxt, mnew, alpha);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // keys and the first values
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {                        // scores beside probabilities
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {                        // P.V beside permutes, maxima
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+        }
+      };
+      block((tt + 1) * kPfTok + kPfTok - 1 > wpos_lo);
+    } else {
+      if (tt < wtiles) {
+        uint32_t w0[8][2], w1[8][2];
+        read_v(tt, vring[tt % kPfNbuf], 0, w0, true);
+        probs(s_cur, m_run, ph, pl, lsum);
+        pv(w0, 0, ph, pl);
+        read_v(tt, vring[tt % kPfNbuf], 1, w1, true);
+        pv(w1, 1, ph, pl);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_lane[rb] += lsum[rb];
+    if (rise) {
+      keep_branch();
+      rescale(alpha);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l_lane[rb] *= alpha[rb];
+    }
+    if (tt + 1 < wtiles) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) m_run[rb] = mnew[rb];
+    }
+  };
+  for (int tt = 0; tt < ntiles; tt += 2) {
+    step(tt, sA, sB);
+    if (tt + 1 >= ntiles) break;
+    step(tt + 1, sB, sA);
+  }
+  wait_copies<0>();
+  if (!wave_live) return;
+
+  // rows 16 rb + 4 quarter + i of the wave: sum across the four lanes of each row,
+  // normalise, store columns 8 col .. 8 col + 7
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_row = sum_xor32(sum_xor16(l_lane[rb]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wrow0 + rb * 16 + 4 * quarter + i;
+      const float lr = __shfl(l_row, 4 * quarter + i);
+      const int jq = j0 + r / G;
+      if (jq >= qlen) continue;
+      const float inv = seq_bad ? __builtin_nanf("") : 1.f / lr;
+      const int64_t orow = ((int64_t)(q0 + jq) * H + g * G + r % G) * D + col * CPL;
+      if (a.out_bf16) {
+        uint4 v;
+        v.x = f32_to_bf16_rne(acc[rb][0][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][1][i] * inv) << 16;
+        v.y = f32_to_bf16_rne(acc[rb][2][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][3][i] * inv) << 16;
+        v.z = f32_to_bf16_rne(acc[rb][4][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][5][i] * inv) << 16;
+        v.w = f32_to_bf16_rne(acc[rb][6][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][7][i] * inv) << 16;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = v;
+      } else {
+        float* dst = static_cast<float*>(a.out) + orow;
+        const floatx4 v0 = {acc[rb][0][i] * inv, acc[rb][1][i] * inv, acc[rb][2][i] * inv, acc[rb][3][i] * inv};
+        const floatx4 v1 = {acc[rb][4][i] * inv, acc[rb][5][i] * inv, acc[rb][6][i] * inv, acc[rb][7][i] * inv};
+        *reinterpret_cast<floatx4*>(dst) = v0;
+        *reinterpret_cast<floatx4*>(dst + 4) = v1;
+      }
+    }
+  }
+}
+
+template <int G>
+static hipError_t launch_prefill_g(const AttentionArgs& a, hipStream_t stream) {
+  // one workgroup per possible (unit, kv head) item, a multiple of the XCD count
+  const int64_t items = (int64_t)a.max_units * a.num_kv_heads;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(paged_attention_prefill_kernel<G>, dim3((unsigned)grid), dim3(kPfWaves * kWave), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_prefill(const AttentionArgs& a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_prefill_g<1>(a, stream);
+    case 2: return launch_prefill_g<2>(a, stream);
+    case 4: return launch_prefill_g<4>(a, stream);
+    case 8: return launch_prefill_g<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ---- merge of the segments ----------------------------------------------------------
 // One workgroup per new token.  The token's sequence, its unit and the shares that hold
 // the unit are found once per workgroup, with wave-uniform scalar loads; the threads
@@ -718,6 +1159,22 @@ __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(Atten
   }
 }
 
+void select_multi_mode(AttentionArgs* a) {
+  // bf16 caches with 128-element heads whose rows would take the row-split mode take
+  // the 256-row prefill units instead when those fill the GPU at least once (at least
+  // one (unit, kv head) item per compute unit; PKV_PREFILL_MIN_ITEMS sets another
+  // threshold, 0 to always take them)
+  if (a->unit_rows != kMqRowUnit || !a->kv_bf16 || a->head_dim != 128) return;
+  const int G = a->num_heads / a->num_kv_heads;
+  const int64_t tpb = kMqPrefillUnit / G;
+  const int64_t units = ((int64_t)a->num_tokens + tpb - 1) / tpb;
+  int64_t min_items = device_cus();
+  if (const char* env = getenv("PKV_PREFILL_MIN_ITEMS")) min_items = atoll(env);
+  if (units * a->num_kv_heads < min_items) return;
+  a->unit_rows = kMqPrefillUnit;
+  a->max_units = (int)(units + a->num_seqs);   // within the arrays sized for row-split units
+}
+
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_tokens);
   if (a.head_dim == 64)
@@ -794,6 +1251,7 @@ static hipError_t launch_multi_g(const AttentionArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attention_multi(const AttentionArgs& a, hipStream_t stream) {
+  if (a.unit_rows == kMqPrefillUnit) return launch_prefill(a, stream);
   if (a.kv_bf16) {
     if (a.head_dim == 64) return launch_multi_g<BF16, 64>(a, stream);
     if (a.head_dim == 128) return launch_multi_g<BF16, 128>(a, stream);

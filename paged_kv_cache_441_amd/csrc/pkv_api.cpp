@@ -772,6 +772,7 @@ pkv_status pkv_paged_attention_multi_query(void* out, const void* query, const v
   a.out_bf16 = out_dtype == PKV_BF16;
   a.v_scale = 1.f;
   set_multi_workspace(&a, workspace, m, num_seqs);
+  pkv::select_multi_mode(&a);
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(pkv::launch_multi_plan(a, s));
   if (st != PKV_OK) return st;

@@ -74,7 +74,7 @@ struct AttentionArgs {
   // one sequence's block of unit_rows (new token, query head) rows of one kv head).
   const int32_t* query_start_loc;   // [num_seqs + 1]
   int num_tokens;
-  int unit_rows;            // 16, 32 or kMqRowUnit rows per unit
+  int unit_rows;            // 16, 32, kMqRowUnit or kMqPrefillUnit rows per unit
   int max_units;            // capacity of the unit arrays
   int* unit_seq;            // [max_units] sequence of each unit
   int* seq_unit;            // [num_seqs + 1] first unit of each sequence
@@ -91,6 +91,10 @@ constexpr int kMqRowWaves = 4;
 #endif
 constexpr int kMqRowRB = PKV_MULTI_ROW_RB;   // row blocks per wave in that mode
 constexpr int kMqRowUnit = kMqRowWaves * 16 * kMqRowRB;
+// Long prompts with bf16 caches and 128-element heads: units of this many rows, one
+// workgroup each over the unit's whole causal context (no split), when such units
+// fill the GPU at least once.
+constexpr int kMqPrefillUnit = 256;
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels
 // (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.
@@ -133,6 +137,8 @@ hipError_t launch_slot_mapping_multi(const int32_t* block_tables, const int32_t*
 // Workspace of a multi-token step: plan header (256 B), then the unit plan arrays,
 // each rounded up to 256 bytes; the records follow.
 size_t multi_plan_bytes(int64_t num_seqs, int64_t max_units);
+// Picks the unit shape for the arguments (possibly the prefill units), before the plan.
+void select_multi_mode(AttentionArgs* a);
 hipError_t launch_multi_plan(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_multi(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream);

@@ -363,3 +363,59 @@ def test_gpu_bf16_output_determinism_and_relabelling():
     pb = permute_physical_blocks(b, np.random.default_rng(2).permutation(512))
     o3 = _gpu_step(pkv, pb)[3]
     assert torch.equal(o1.view(torch.int32), o3.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------
+# long prompts with bf16 caches: the prefill units (256 rows, one workgroup each, no
+# split).  The library takes them when they fill the GPU; PKV_PREFILL_MIN_ITEMS=0 makes
+# small batches take them too, so that every shape and edge can be checked here.
+# ----------------------------------------------------------------------------
+
+PREFILL_PAIRS = [(300, 300), (1000, 257), (2049, 200), (513, 129), (64, 64), (40, 33),
+                 (777, 70)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("G,Hkv,BS", [(4, 2, 16), (1, 2, 16), (2, 4, 32), (8, 1, 16)])
+def test_gpu_prefill_units_match_oracle(monkeypatch, G, Hkv, BS):
+    pkv = _gpu()
+    monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
+    ctx = [c for c, _ in PREFILL_PAIRS]
+    ql = [q for _, q in PREFILL_PAIRS]
+    b = build_multi_batch(_spec(D=128, G=G, Hkv=Hkv, BS=BS, NB=1024, dtype="bf16", seed=G + BS),
+                          ctx, ql, device="cuda")
+    _, _, _, out = _gpu_step(pkv, b)
+    ref = _oracle_subset(b, range(len(ctx)))
+    assert len(ref) == sum(ql)
+    err = _max_err(out, ref)
+    print(f"prefill units G={G} Hkv={Hkv} BS={BS}: max err {err:.3e} over {len(ref)} tokens")
+    assert np.isfinite(out.float().cpu().numpy()).all()
+    assert err <= ATOL
+    # bf16 output: the fp32 result rounded to nearest even
+    o16 = _gpu_step(pkv, b, out_dtype=torch.bfloat16)[3]
+    assert torch.equal(o16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
+    # the same batch through the row-split units agrees to fp32 accumulation order
+    monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", str(1 << 40))
+    rows = _gpu_step(pkv, b)[3]
+    assert (rows - out).abs().max().item() <= 2e-5
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_units_invalid_inputs_give_nan_rows_only(monkeypatch):
+    pkv = _gpu()
+    monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
+    b = build_multi_batch(_spec(D=128, G=4, Hkv=2, dtype="bf16", NB=1024), [400, 300, 900, 700],
+                          [100, 64, 200, 300], device="cuda")
+    _, _, _, good = _gpu_step(pkv, b)
+    bt, cl, qsl = _meta(b)
+    bt_bad = bt.clone()
+    bt_bad[1, 2] = 5000                 # outside the pool, before every new token of seq 1
+    bt_bad[2, 55] = -7                  # outside the pool, after seq 2's earliest new tokens
+    cl_bad = cl.clone()
+    cl_bad[3] = 250                     # fewer tokens than new tokens
+    _, _, _, out = _gpu_step(pkv, b, block_tables=bt_bad, context_lens=cl_bad)
+    o, gd = out.cpu(), good.cpu()
+    q = b.extra["query_start_loc"]
+    for i in (1, 2, 3):                 # every row of those sequences
+        assert torch.isnan(o[q[i]:q[i + 1]]).all()
+    assert torch.equal(o[q[0]:q[1]].view(torch.int32), gd[q[0]:q[1]].view(torch.int32))
