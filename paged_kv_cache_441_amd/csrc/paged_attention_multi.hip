@@ -32,11 +32,13 @@
 //  - P.V on the matrix cores.  Each lane reads D / 16 consecutive value columns of a
 //    token row in one LDS read, one column per output block, so the value tile needs
 //    no transpose either (output block e holds columns e, e + D/16, ...; undone at
-//    the store).  bf16 caches: v_mfma_f32_16x16x16_bf16 with lane quarter q supplying
-//    tokens 4q .. 4q + 3 (the B operand packed from four token rows) and P split into
-//    bf16 hi + lo parts, together exact to about 2^-17 of p (a single bf16 P could move
-//    outputs by up to ~5e-3); fp32 caches: v_mfma_f32_16x16x4_f32 with fp32 P, k-step
-//    s taking token 4q + s from lane quarter q.
+//    the store).  bf16 caches: P split into bf16 hi + lo parts, together exact to
+//    about 2^-17 of p (a single bf16 P could move outputs by up to ~5e-3), on the
+//    full-rate v_mfma_f32_16x16x32_bf16: lane quarter q supplies the hi and then the
+//    lo parts of tokens 4q .. 4q + 3 as its eight k values (A), and the same tokens'
+//    value rows twice (B, packed from four token rows); fp32 caches:
+//    v_mfma_f32_16x16x4_f32 with fp32 P, k-step s taking token 4q + s from lane
+//    quarter q.
 //  - A unit is one or two MFMA row blocks (16 or 32 rows: two when the sequences
 //    average more than 16 rows), so up to 32 rows share one pass over the tiles.
 #include "pkv_device.hpp"
@@ -237,7 +239,8 @@ void paged_attention_multi_kernel(AttentionArgs a) {
 
   // NBUF tiles rotate through one ring; the copies are assembly the compiler does not
   // track, so one array indexed at run time costs no extra waits
-  __shared__ uint4 kring[NBUF][NS], vring[NBUF][NS];
+  // (slot s: the key tile at ring[s], the value tile at ring[s] + NS)
+  __shared__ uint4 ring[NBUF][2 * NS];
   static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -456,10 +459,10 @@ void paged_attention_multi_kernel(AttentionArgs a) {
     }
     const bool full = tok0 + TOK <= uctx;
     if constexpr (std::is_same<T, BF16>::value) {
-      // P.V on bf16 matrix instructions (16x16x16): lane quarter q supplies tokens
-      // 4q .. 4q + 3 of its row (A) and of its value columns (B, packed from four token
-      // rows).  P is split into hi + lo bf16 terms, together exact to about 2^-17 of p,
-      // so the products keep fp32-level accuracy.
+      // P.V on bf16 matrix instructions (16x16x32): lane quarter q supplies the hi and
+      // the lo terms of tokens 4q .. 4q + 3 of its row (A) and those tokens' value
+      // columns twice (B, packed from four token rows).  Together hi + lo are exact to
+      // about 2^-17 of p, so the products keep fp32-level accuracy.
       uint32_t w[4][CPL / 2];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -500,13 +503,11 @@ void paged_attention_multi_kernel(AttentionArgs a) {
         const floatx2 r23 = p23 - __builtin_convertvector(h23, floatx2);
         const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
         const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
-        const bf16x4 ahi = {h01[0], h01[1], h23[0], h23[1]};
-        const bf16x4 alo = {l01[0], l01[1], l23[0], l23[1]};
+        const bf16x8 ahl = {h01[0], h01[1], h23[0], h23[1], l01[0], l01[1], l23[0], l23[1]};
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          const bf16x4 b = __builtin_bit_cast(bf16x4, bv[e]);
-          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc[rb][e], 0, 0, 0);
-          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc[rb][e], 0, 0, 0);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(bv[e].x, bv[e].y, bv[e].x, bv[e].y));
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahl, b, acc[rb][e], 0, 0, 0);
         }
       }
       return;
@@ -602,19 +603,22 @@ void paged_attention_multi_kernel(AttentionArgs a) {
   unit_info();
   load_query();
 
-  // Tile j sits in ring slot j % NBUF.  Per step: wait for this wave's copies of tile
-  // j, one barrier (every wave's copies of tile j have landed, and every wave is done
-  // with tile j - 1), issue tile j + NBUF - 1 into the slot of tile j - 1, compute
-  // tile j.  One barrier per tile.
+  // Tile j sits in ring slot j % NBUF.  Per step: issue tile j + NBUF - 1 into the
+  // slot of tile j - 1 (released by the previous step's last barrier), wait for this
+  // wave's copies of tile j (the NBUF - 1 later tiles stay in flight), barrier (every
+  // wave's copies of tile j have landed), compute tile j, barrier (every wave is done
+  // with its slot).  Issuing before the wait keeps NBUF - 1 tiles in flight during
+  // the wait, not NBUF - 2.
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) issue(kring[i], vring[i]);
+  for (int i = 0; i < NBUF - 1; ++i) issue(ring[i], ring[i] + NS);
   for (int j = 0;; ++j) {
     if (cc.t >= cc.stop) break;
-    wait_copies<(NBUF - 2) * L>();
-    bare_barrier();
     const int fill = (j + NBUF - 1) % NBUF;
-    issue(kring[fill], vring[fill]);
-    compute(kring[j % NBUF], vring[j % NBUF], (bad_pipe >> (NBUF - 1)) & 1u);
+    issue(ring[fill], ring[fill] + NS);
+    wait_copies<(NBUF - 1) * L>();
+    bare_barrier();
+    compute(ring[j % NBUF], ring[j % NBUF] + NS, (bad_pipe >> (NBUF - 1)) & 1u);
+    bare_barrier();
     if (cc.t == cc.stop - 1) {
       finish(seg_from_zero && cc.stop == cc.nt);
       reset();
@@ -1072,90 +1076,96 @@ static hipError_t launch_prefill(const AttentionArgs& a, hipStream_t stream) {
 }
 
 // ---- merge of the segments ----------------------------------------------------------
-// One workgroup per new token.  The token's sequence, its unit and the shares that hold
-// the unit are found once per workgroup, with wave-uniform scalar loads; the threads
-// then cover the token's query heads, 256 / (D / 4) heads per pass, each lane a float4
-// of one head's output row, and fold the head's records in share order.  Rows of
-// invalid sequences get NaN; rows whose unit lies in one share were written by the
-// attention kernel.
+// Two kinds of workgroups.  The first max_units * Hkv take one (unit, kv head) each:
+// a unit inside one share was written by the attention kernel and its workgroup
+// exits; otherwise the workgroup folds the unit's records of that kv head, share by
+// share in share order, and writes the rows.  The unit's records of one kv head and
+// label are contiguous rows, so the loads are whole rows, and the unit, its sequence
+// and its shares come from a few independent loads (no search).  The last
+// num_tokens workgroups take one new token each and give NaN rows to the tokens that
+// belong to no valid sequence (or to every token, when the plan has no units).
 template <int D>
 __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(AttentionArgs a) {
-  constexpr int LPR = D / 4;             // lanes per head row (float4 each)
-  constexpr int HPP = 256 / LPR;         // heads per pass
-  const int t = blockIdx.x;
+  constexpr int C4 = D / 4;              // float4 pieces of a row
+  constexpr int KS = 4;                  // shares whose records are loaded together
   const int H = a.num_heads;
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
-  const int hl = threadIdx.x / LPR;
-  const int lr = threadIdx.x % LPR;
-  cint32* qsl = (cint32*)a.query_start_loc;
+  const int rows = a.unit_rows;
   cint32* hdr = (cint32*)a.tile_hdr;
-  int lo = 0, hi = a.num_seqs;           // the sequence holding token t (qsl[0] <= t)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int i = lo;
-  const int q0 = qsl[i], q1 = qsl[i + 1];
-  const int max_ctx = a.max_blocks_per_seq << a.block_shift;
-  const bool valid = hdr[2] > 0 && t >= q0 && t < q1 &&
-                     seq_valid(q0, q1, ((cint32*)a.context_lens)[i], a.num_tokens, max_ctx);
-  const int64_t row0 = (int64_t)t * H;
-  if (!valid) {
+  cint32* qsl = (cint32*)a.query_start_loc;
+  const int64_t unit_wgs = (int64_t)a.max_units * Hkv;
+  if ((int64_t)blockIdx.x >= unit_wgs) {
+    const int t = (int)((int64_t)blockIdx.x - unit_wgs);
+    // the sequence holding token t: the last i with qsl[i] <= t (64-way search)
+    int lo = 0, len = a.num_seqs + 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    while (len > 1) {
+      const int step = (len + kWave - 1) / kWave;
+      const int i = lo + lane * step;
+      const bool ok = i < lo + len && qsl[i] <= t;
+      const int k = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
+      const int nlo = lo + (max(k, 1) - 1) * step;
+      len = min(step, lo + len - nlo);
+      lo = nlo;
+    }
+    const int i = lo;
+    const int q0 = qsl[i], q1 = qsl[i + 1];
+    const int max_ctx = a.max_blocks_per_seq << a.block_shift;
+    const bool valid = hdr[2] > 0 && t >= q0 && t < q1 &&
+                       seq_valid(q0, q1, ((cint32*)a.context_lens)[i], a.num_tokens, max_ctx);
+    if (valid) return;
     const float nan = __builtin_nanf("");
-    for (int h = hl; h < H; h += HPP)
-      store_row4(a, (row0 + h) * D + lr * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
+    for (int k = threadIdx.x; k < H * C4; k += 256)
+      store_row4(a, ((int64_t)t * H) * D + k * 4, Running{0.f, 1.f, make_float4(nan, nan, nan, nan)});
     return;
   }
-  const int rows = a.unit_rows;
-  const int tpb = rows / G;
-  const int jq = t - q0;
-  const int u = ((cint32*)a.seq_unit)[i] + jq / tpb;
+  const int u = blockIdx.x / Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int U = hdr[2];
+  if (u >= U) return;
   const int c0 = ((cint32*)a.tile_cum)[u], c1 = ((cint32*)a.tile_cum)[u + 1];
+  const int seq = ((cint32*)a.unit_seq)[u];
   const int total = hdr[0];
   const int nwg = hdr[1];
   const int w0 = share_of((int64_t)c0 + kSeqCost, nwg, total);
   const int w1 = share_of((int64_t)c1 - 1, nwg, total);
   if (w0 == w1) return;
-  const int rq = (jq % tpb) * G;
-  // KH heads per thread at a time, so that each share's records of all of them are
-  // loaded before any is merged (one round trip per share, not one per head).  Heads
-  // past H load head H - 1's records and store nothing.
-  constexpr int KH = 4;
-  for (int hb = hl; hb < H; hb += KH * HPP) {
-    int64_t in_label[KH];   // record of head h under label L: (L * Hkv + h / G) * rows + rq + h % G
-    Running acc[KH];
+  const int q0 = qsl[seq];
+  const int qlen = qsl[seq + 1] - q0;
+  const int uj0 = (u - ((cint32*)a.seq_unit)[seq]) * (rows / G);
+  const int nrows = min(rows, (qlen - uj0) * G);          // the unit's real rows
+  const int64_t lab_stride = (int64_t)Hkv * rows;           // between labels L and L + 1
+  const int64_t base = ((int64_t)u * Hkv + g) * rows;        // record row 0 under label 0
+  for (int k = threadIdx.x; k < nrows * C4; k += 256) {
+    const int r = k / C4, c = k % C4;
+    Running acc{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    for (int wb = w0; wb <= w1; wb += KS) {
+      float l[KS], m[KS];
+      floatx4 o[KS];
 #pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const int h = min(hb + k * HPP, H - 1);
-      in_label[k] = (int64_t)(h / G) * rows + rq + h % G;
-      acc[k] = Running{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    }
-    for (int ww = w0; ww <= w1; ++ww) {
-      if (!share_nonempty(ww, nwg, total)) continue;
-      const int64_t lab = ((int64_t)ww + u) * Hkv * rows;
-      float l[KH], m[KH];
-      floatx4 o[KH];
-#pragma unroll
-      for (int k = 0; k < KH; ++k) {
-        const int64_t rec = lab + in_label[k];
-        l[k] = a.ws_l[rec];
-        m[k] = a.ws_m[rec];
-        o[k] = reinterpret_cast<const floatx4*>(a.ws_o + rec * D)[lr];
+      for (int q = 0; q < KS; ++q) {
+        const int ww = min(wb + q, w1);
+        const int64_t rec = base + (int64_t)ww * lab_stride + r;
+        l[q] = a.ws_l[rec];
+        m[q] = a.ws_m[rec];
+        o[q] = reinterpret_cast<const floatx4*>(a.ws_o + rec * D)[c];
       }
       // Records of segments in which this row saw no token have l = 0 (and m = -inf);
-      // they weigh nothing.  A NaN l marks bad data and is kept.
+      // they weigh nothing.  A NaN l marks bad data and is kept.  Empty shares wrote
+      // no record.
 #pragma unroll
-      for (int k = 0; k < KH; ++k) {
-        if (!(l[k] > 0.f) && !(l[k] != l[k])) continue;
-        const Running sg{m[k], l[k], make_float4(o[k][0] * l[k], o[k][1] * l[k], o[k][2] * l[k],
-                                                 o[k][3] * l[k])};
-        merge_into(acc[k], sg);
+      for (int q = 0; q < KS; ++q) {
+        const int ww = wb + q;
+        if (ww > w1 || !share_nonempty(ww, nwg, total)) continue;
+        if (!(l[q] > 0.f) && !(l[q] != l[q])) continue;
+        const Running sg{m[q], l[q], make_float4(o[q][0] * l[q], o[q][1] * l[q], o[q][2] * l[q],
+                                                 o[q][3] * l[q])};
+        merge_into(acc, sg);
       }
     }
-#pragma unroll
-    for (int k = 0; k < KH; ++k)
-      if (hb + k * HPP < H) store_row4(a, (row0 + hb + k * HPP) * D + lr * 4, acc[k]);
+    const int jq = uj0 + r / G;
+    store_row4(a, ((int64_t)(q0 + jq) * H + g * G + r % G) * D + c * 4, acc);
   }
 }
 
@@ -1176,7 +1186,9 @@ void select_multi_mode(AttentionArgs* a) {
 }
 
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.num_tokens);
+  const int64_t wgs = (int64_t)a.max_units * a.num_kv_heads + a.num_tokens;
+  if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)wgs);
   if (a.head_dim == 64)
     hipLaunchKernelGGL(paged_attention_multi_reduce_kernel<64>, grid, dim3(256), 0, stream, a);
   else if (a.head_dim == 128)
@@ -1205,10 +1217,16 @@ static hipError_t launch_multi_rb(const AttentionArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Ring depth of the head mode (one wave per kv head of the workgroup).
+#ifndef PKV_MULTI_HEAD_NBUF
+#define PKV_MULTI_HEAD_NBUF 2
+#endif
+
 template <typename T, int D, int G, int HW>
 static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream) {
-  return a.unit_rows == 32 ? launch_multi_rb<T, D, G, HW, 2, HW>(a, stream)
-                           : launch_multi_rb<T, D, G, HW, 1, HW>(a, stream);
+  constexpr int NB = PKV_MULTI_HEAD_NBUF;
+  return a.unit_rows == 32 ? launch_multi_rb<T, D, G, HW, 2, HW, NB>(a, stream)
+                           : launch_multi_rb<T, D, G, HW, 1, HW, NB>(a, stream);
 }
 
 // Ring depth of the row-split mode: its tiles are one head's rows (a quarter or less
@@ -1218,11 +1236,14 @@ static hipError_t launch_multi_shape(const AttentionArgs& a, hipStream_t stream)
 #endif
 
 #ifndef PKV_MULTI_MAX_ROW
-#define PKV_MULTI_MAX_ROW 1024
+#define PKV_MULTI_MAX_ROW 2048
 #endif
 
 // Heads per workgroup: the largest of 8, 4, 2, 1 dividing the kv heads with a token
-// row of the group within PKV_MULTI_MAX_ROW bytes and at least 128 bytes.
+// row of the group within PKV_MULTI_MAX_ROW bytes and at least 128 bytes.  Whole 2 KiB
+// rows (8 bf16 heads of 128) with one workgroup per compute unit: 310 us per launch
+// for 5 speculated tokens per sequence on the Llama-3-8B-shaped batch, against 320 us
+// with 1 KiB rows and two workgroups per unit (MI355X).
 template <typename T, int D, int G>
 static hipError_t launch_multi_hw(const AttentionArgs& a, hipStream_t stream) {
   constexpr int kRow = D * T::kElemBytes;

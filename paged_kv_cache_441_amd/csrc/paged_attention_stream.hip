@@ -451,12 +451,11 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
     if constexpr (kMfmaPV) {
-      // P.V on 16x16x16 bf16 matrix instructions.  A: P with the wave's heads as rows
-      // (row col, real for col < G) and tokens 4 quarter .. 4 quarter + 3 as k; B: the
-      // same tokens' value columns col * 8 + e for output block e, packed from four
-      // token rows (a column permutation, undone at the store).  P is split into hi +
-      // lo bf16 terms, together exact to about 2^-17 of p; E4M3 values are exact in
-      // bf16.
+      // P.V on bf16 matrix instructions.  A: P with the wave's heads as rows (row col,
+      // real for col < G) and tokens 4 quarter .. 4 quarter + 3 as k; B: the same
+      // tokens' value columns col * 8 + e for output block e, packed from four token
+      // rows (a column permutation, undone at the store).  P is split into hi + lo
+      // bf16 terms, together exact to about 2^-17 of p; E4M3 values are exact in bf16.
       floatx4 pa = {0.f, 0.f, 0.f, 0.f};
       if (col < G) pa = *reinterpret_cast<const floatx4*>(&p_lds[wave][col % G][4 * quarter]);
       const floatx2 p01 = {pa[0], pa[1]}, p23 = {pa[2], pa[3]};
@@ -466,6 +465,11 @@ void paged_attention_stream_kernel(AttentionArgs a) {
       const bf16x2 l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, floatx2), bf16x2);
       const bf16x4 ahi = {h01[0], h01[1], h23[0], h23[1]};
       const bf16x4 alo = {l01[0], l01[1], l23[0], l23[1]};
+      // bf16 caches: one k = 32 operand, the lane's four hi terms then its four lo
+      // terms, against its four value rows twice (the order of k is free); E4M3
+      // caches, whose kernel runs four waves per SIMD, keep two k = 16 products,
+      // which need fewer registers
+      const bf16x8 ahl = {h01[0], h01[1], h23[0], h23[1], l01[0], l01[1], l23[0], l23[1]};
       uint32_t wv[4][4];   // token 4 quarter + s: value columns col * 8 .. col * 8 + 7
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -489,9 +493,14 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         uint2 bq;
         bq.x = __builtin_amdgcn_perm(wv[1][e >> 1], wv[0][e >> 1], sel);
         bq.y = __builtin_amdgcn_perm(wv[3][e >> 1], wv[2][e >> 1], sel);
-        const bf16x4 b = __builtin_bit_cast(bf16x4, bq);
-        acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc8[e], 0, 0, 0);
-        acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc8[e], 0, 0, 0);
+        if constexpr (kF8) {
+          const bf16x4 b = __builtin_bit_cast(bf16x4, bq);
+          acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc8[e], 0, 0, 0);
+          acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc8[e], 0, 0, 0);
+        } else {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(bq.x, bq.y, bq.x, bq.y));
+          acc8[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahl, b, acc8[e], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_wave_barrier();
       return;

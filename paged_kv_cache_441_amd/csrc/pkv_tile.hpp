@@ -123,11 +123,16 @@ __device__ __forceinline__ void accumulate(Running& r, const float (&m)[N], cons
   r.m = mb;
 }
 
+// Four consecutive outputs from idx (a multiple of 4) in one store.
 __device__ __forceinline__ void store_row4(const AttentionArgs& a, int64_t idx, const Running& r) {
-  store_out(a.out, idx + 0, r.o.x / r.l, a.out_bf16);
-  store_out(a.out, idx + 1, r.o.y / r.l, a.out_bf16);
-  store_out(a.out, idx + 2, r.o.z / r.l, a.out_bf16);
-  store_out(a.out, idx + 3, r.o.w / r.l, a.out_bf16);
+  const float x = r.o.x / r.l, y = r.o.y / r.l, z = r.o.z / r.l, w = r.o.w / r.l;
+  if (a.out_bf16) {
+    const uint2 v = make_uint2(f32_to_bf16_rne(x) | (uint32_t)f32_to_bf16_rne(y) << 16,
+                               f32_to_bf16_rne(z) | (uint32_t)f32_to_bf16_rne(w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + idx) = v;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + idx) = make_float4(x, y, z, w);
+  }
 }
 
 }  // namespace pkv
