@@ -65,8 +65,9 @@ def kernel_source_hash() -> str:
 
 
 def stored_traffic(kernel: str, workload: str, partition_size: int):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter runs,
-    or None when they were taken on other kernel sources or another workload."""
+    """The committed rocprofv3 counter summary of the partition kernel (HBM bytes per
+    launch and the copy-calibrated scale factors), or None when it was taken on other
+    kernel sources, another workload or another split."""
     try:
         with open(traffic_file(kernel, workload)) as f:
             t = json.load(f)
@@ -75,7 +76,104 @@ def stored_traffic(kernel: str, workload: str, partition_size: int):
     if (t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload
             or t.get("partition_size") != partition_size):
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t
+
+
+# The four counter runs a traffic summary reads, under gpurun_out/ (one counter per run:
+# FETCH_SIZE and WRITE_SIZE each take TCC counters of their own).
+def traffic_runs(workload: str):
+    return [("FETCH_SIZE", "pmc_fetch_copy", "--copy-calibration"),
+            ("WRITE_SIZE", "pmc_write_copy", "--copy-calibration"),
+            ("FETCH_SIZE", f"{workload}_pmc_fetch_bench",
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling"),
+            ("WRITE_SIZE", f"{workload}_pmc_write_bench",
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --no-ceiling")]
+
+
+def traffic_summary(workload: str) -> int:
+    """Writes profiles/traffic_paged_attention_stream_<workload>.json and its .md from
+    the four rocprofv3 --pmc runs of traffic_runs() (host only; the runs themselves
+    happen on the GPU).  FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is
+    scaled by what it reads for a plain 1 GiB copy."""
+    import collections
+    import csv
+    import glob
+    from workloads import CONFIGS, FP8_CONFIGS
+    from workloads.decode_batches import draw_context_lens
+
+    def per_dispatch(d: str, counter: str):
+        files = glob.glob(os.path.join(ROOT, "gpurun_out", d, "**", "*counter_collection.csv"),
+                          recursive=True)
+        if not files:
+            raise SystemExit(f"no counter file under gpurun_out/{d}")
+        acc, names = collections.defaultdict(float), {}
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        out = collections.defaultdict(list)
+        for k, v in acc.items():
+            out[names[k]].append(v)
+        return out
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    def short(n: str) -> str:
+        n = n.replace("void ", "").replace("(pkv::AttentionArgs)", "")
+        return n.split("(")[0]
+
+    runs = traffic_runs(workload)
+    cf = per_dispatch(runs[0][1], "FETCH_SIZE")
+    cw = per_dispatch(runs[1][1], "WRITE_SIZE")
+    copy_f = mean(next(v for k, v in cf.items() if "copyBuffer" in k))
+    copy_w = mean(next(v for k, v in cw.items() if "copyBuffer" in k))
+    fscale, wscale = 1048576.0 / copy_f, 1048576.0 / copy_w
+    spec = FP8_CONFIGS[workload] if workload in FP8_CONFIGS else CONFIGS[workload]
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[spec.kv_dtype]
+    algo = int(draw_context_lens(spec, None).astype(np.int64).sum()) * spec.num_kv_heads * \
+        spec.head_dim * 2 * elem
+    f = per_dispatch(runs[2][1], "FETCH_SIZE")
+    w = per_dispatch(runs[3][1], "WRITE_SIZE")
+    rows = []
+    for k in f:
+        if "pkv::" not in k:
+            continue
+        fk, wk = mean(f[k]), mean(w.get(k, [0.0]))
+        rows.append((short(k), len(f[k]), fk, wk, fk * 1024 * fscale, wk * 1024 * wscale))
+    stream = next(r for r in rows if "paged_attention_stream_kernel" in r[0])
+    traffic = int(round(stream[4] + stream[5]))
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/{d} -o run -- "
+            f"python3 bench.py {a}" for c, d, a in runs]
+    md = [f"# HBM traffic: one decode step of {workload} (partition size "
+          f"{spec.partition_size})", "",
+          "Commands, from the repository root on an MI355X, one counter per run, then "
+          f"`python3 bench.py --traffic-summary {workload}` on the host:", "", "```", *cmds,
+          "```", "",
+          "Scale factors from a plain 1 GiB device copy (`__amd_rocclr_copyBuffer`, "
+          "1,048,576 KiB read and written per call):", "",
+          f"- FETCH_SIZE reads {copy_f:,.1f} KiB per copy: factor {fscale:.3f}.",
+          f"- WRITE_SIZE reads {copy_w:,.1f} KiB per copy: factor {wscale:.3f}.", "",
+          "| Kernel | Dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Read (B, scaled) | "
+          "Written (B, scaled) |", "|---|---|---|---|---|---|"]
+    md += [f"| `{r[0]}` | {r[1]} | {r[2]:,.1f} | {r[3]:,.1f} | {r[4]:,.0f} | {r[5]:,.0f} |"
+           for r in rows]
+    md += ["", f"`paged_attention_stream_kernel`: {traffic:,} B per launch against {algo:,} "
+               f"algorithmic KV bytes = {traffic / algo:.4f}x (reads alone "
+               f"{stream[4] / algo:.4f}x)."]
+    name = f"paged_attention_stream_{workload}_hbm_traffic.md"
+    with open(os.path.join(PROFILES, name), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    js = {"workload": workload, "partition_size": spec.partition_size,
+          "source_sha256": kernel_source_hash(), "traffic_bytes_per_launch": traffic,
+          "read_bytes": int(round(stream[4])), "write_bytes": int(round(stream[5])),
+          "algorithmic_bytes": algo, "fetch_scale": round(fscale, 4),
+          "write_scale": round(wscale, 4), "summary": name}
+    with open(traffic_file("paged_attention_stream", workload), "w") as fh:
+        fh.write(json.dumps(js, indent=1) + "\n")
+    print(json.dumps(js))
+    return 0
 
 
 METRIC = "paged-attn decode KV HBM GB/s (% of peak) and tokens/s at batch×ctx, 1 GPU"
@@ -167,6 +265,10 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for HBM traffic counters)")
+    ap.add_argument("--traffic-summary", metavar="WORKLOAD",
+                    help="host only: summarise the rocprofv3 FETCH_SIZE / WRITE_SIZE runs "
+                         "under gpurun_out/ into profiles/ (the decode kernel's traffic "
+                         "per launch, read by later bench runs)")
     return ap.parse_args(argv)
 
 
@@ -201,6 +303,8 @@ def main(argv=None) -> int:
         return oracle_worker(*args.oracle_worker)
     if args.copy_calibration:
         return copy_calibration()
+    if args.traffic_summary:
+        return traffic_summary(args.traffic_summary)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
                                    "has no multi-GPU mode (use --gpus 1)"}))
@@ -308,6 +412,8 @@ def main(argv=None) -> int:
 
     kv_bytes = b.kv_bytes()
     unique_bytes = unique_kv_bytes(b)
+    traffic = stored_traffic("paged_attention_partition" if per_head else "paged_attention_stream",
+                             spec.name, P)
     # fixed partitions run in the same streaming kernel (one workgroup per partition)
     # unless the per-head layout is asked for
     kernel = "paged_attention_partition" if per_head else "paged_attention_stream"
@@ -367,9 +473,12 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(kernel, spec.name, P),
-            "traffic_unit": "bytes per launch (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, "
-                            "factors from a plain 1 GiB copy)",
+            "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+            "traffic_unit": ("bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f, factors "
+                             "from a plain 1 GiB copy; %s)" % (
+                                 traffic["fetch_scale"], traffic["write_scale"],
+                                 traffic["summary"]) if traffic else
+                             "bytes per launch; none stored for these kernel sources"),
             "achieved_unique": round(unique_bytes / (part_ms / 1e3) / 1e9, 1),
         },
         "device": torch.cuda.get_device_name(dev),
