@@ -39,12 +39,17 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers named as device buffers are device (HBM) addresses owned by the
- *    caller; the library never allocates, frees or retains them and keeps no
- *    global state.  All entry points are reentrant.
+ *    caller; the library never allocates, frees or retains them.  Its only global
+ *    state is per-device facts looked up once (the compute-unit count, the address of
+ *    pkv_paged_attention_decode_noalloc's scratch array); the entry points are
+ *    reentrant, with the overlap rule of that scratch array stated at its entry.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    only enqueued on it; no call synchronises the host.  Ordering (write before
  *    attention) is the caller's, by using one stream.
  *  - Integer tensors are int32, row-major.  Element types are pkv_dtype.
+ *  - Alignment: buffers of rows (caches, queries, keys, values, outputs, workspaces,
+ *    block-pair lists excepted) start on 16-byte boundaries, int32 arrays on 4-byte
+ *    ones; a misaligned pointer is PKV_ERR_INVALID_ARG.
  *  - Errors come back as a pkv_status, never as an abort or exception.  Every
  *    argument check happens before any GPU work is enqueued, so a call that
  *    returns an error other than PKV_ERR_HIP has touched nothing.
@@ -363,13 +368,25 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
  * new tokens' rows already written.  Accumulation fp32; scores and probabilities fp32
  * throughout (no reduced-precision P).  Supported: kv_dtype PKV_F32 or PKV_BF16,
  * head_dim 64 or 128, block_size 16 or 32, num_heads / num_kv_heads in {1, 2, 4, 8},
- * num_tokens * num_heads * head_dim * sizeof(kv_dtype) below 2^31.  Workspace:
- * pkv_paged_attention_multi_query_workspace_bytes() bytes, no initialisation needed.
- * With G = num_heads / num_kv_heads, R = 32 rows per unit when num_tokens * G >
- * 16 * num_seqs and 16 otherwise, and U = ceil(num_tokens / (R / G)) + num_seqs, it
- * holds a 256-byte header, the unit plan (U + 1, U and num_seqs + 1 int32, each
- * rounded up to 256 bytes) and (1024 + U) * num_kv_heads * R records of
- * (head_dim + 2) fp32.  Device-side contract: rows of a sequence that does not fit
+ * num_tokens * num_heads * head_dim * sizeof(kv_dtype) below 2^31.
+ * Work split.  Rows are (new token, query head) pairs; the rows of one sequence and kv
+ * head are cut into units of R rows (R / G consecutive new tokens with the
+ * G = num_heads / num_kv_heads query heads of the kv head).  With A = num_tokens * G /
+ * num_seqs the average rows per sequence: R = 16 when A <= 16; R = 128 when head_dim
+ * is 128 and A >= 128; R = 32 otherwise.  Units and their tiles are split over the
+ * GPU in equal shares and the pieces merged by log-sum-exp, except that with bf16
+ * caches, head_dim 128 and R = 128, units of 256 rows are used when they give at least
+ * one (unit, kv head) item per compute unit (the environment variable
+ * PKV_PREFILL_MIN_ITEMS, read at each call, sets another threshold): one workgroup then
+ * covers a unit's whole causal context and nothing is merged.  Where the pieces fall
+ * depends on the whole batch and the GPU, so results may differ between batches in
+ * the last bits of fp32; for one batch on one GPU they are deterministic.
+ * Workspace: pkv_paged_attention_multi_query_workspace_bytes() bytes, no
+ * initialisation needed.  With U = ceil(num_tokens / (R / G)) + num_seqs, it holds a
+ * 256-byte header, the unit plan (U + 1, U and num_seqs + 1 int32, each rounded up to
+ * 256 bytes) and (1024 + U) * num_kv_heads * R records of (head_dim + 2) fp32.
+ * PKV_ERR_UNSUPPORTED when U * num_kv_heads + num_tokens exceeds 2^32 / 256 - 1.
+ * Device-side contract: rows of a sequence that does not fit
  * (as for the slot mapping), or that lists a block id outside [0, num_blocks) within
  * its context, are NaN; a query_start_loc that is not a non-decreasing cut of the
  * flat batch may make every row NaN; nothing outside the listed blocks and the flat

@@ -23,6 +23,11 @@ int log2_exact(int64_t x) {
 
 size_t elem_bytes(int32_t t) { return t == PKV_FP8_E4M3 ? 1 : t == PKV_BF16 ? 2 : 4; }
 
+// Device buffers of rows (caches, queries, keys, values, outputs, workspaces) are
+// moved in 16-byte pieces, int32 arrays element by element.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 // Arithmetic types (queries, outputs, the inputs of a quantised write).
 bool valid_dtype(int32_t t) { return t == PKV_F32 || t == PKV_BF16; }
 // Types a cache may hold (bit copies).
@@ -146,6 +151,10 @@ pkv_status fill_attention_args(void* out, const void* query, const void* key_cac
     if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
     if (need_inputs && (!query || !key_cache || !value_cache || !block_tables))
       return PKV_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned4(context_lens) || !aligned16(workspace) ||
+        (need_inputs && (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+                         !aligned4(block_tables))))
+      return PKV_ERR_INVALID_ARG;
   }
   if (need_inputs) {
     const int G = num_heads / num_kv_heads;
@@ -236,6 +245,8 @@ pkv_status pkv_slot_mapping(const int32_t* block_tables, const int32_t* context_
     return PKV_ERR_INVALID_ARG;   // slots are int32
   if (num_seqs == 0) return PKV_OK;
   if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned4(block_tables) || !aligned4(context_lens) || !aligned4(slot_mapping))
+    return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_slot_mapping(block_tables, context_lens, slot_mapping, num_seqs,
                                              max_blocks_per_seq, log2_exact(block_size),
                                              num_blocks, static_cast<hipStream_t>(stream)));
@@ -257,6 +268,9 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, void* key_cach
   if (row % 16 != 0 || num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(slot_mapping))
+    return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
                                             num_tokens, static_cast<int>(row), slots,
                                             static_cast<hipStream_t>(stream)));
@@ -279,6 +293,9 @@ pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, void* key_
   if (row % 16 != 0 || num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(slot_mapping))
+    return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping,
                                                 num_tokens, static_cast<int>(row), slots,
                                                 in_dtype == PKV_BF16, k_scale, v_scale,
@@ -300,6 +317,8 @@ pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pa
   if (block % 16 != 0 || num_pairs > kMaxItems256) return PKV_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PKV_OK;
   if (!key_cache || !value_cache || !pairs) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(pairs))
+    return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block,
                                             num_blocks, static_cast<hipStream_t>(stream)));
 }
@@ -346,6 +365,10 @@ pkv_status prologue(const int32_t* block_tables, const int32_t* context_lens, co
   if (num_seqs == 0) return PKV_OK;
   if (!block_tables || !context_lens || !key || !value || !key_cache || !value_cache ||
       !slot_mapping)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned4(block_tables) || !aligned4(context_lens) || !aligned16(key) || !aligned16(value) ||
+      !aligned16(key_cache) || !aligned16(value_cache) || !aligned4(slot_mapping) ||
+      !aligned16(workspace))
     return PKV_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < s.plan_bytes) return PKV_ERR_WORKSPACE;
   pkv::AttentionArgs a{};
@@ -397,7 +420,7 @@ pkv_status pkv_paged_attention_plan(const int32_t* context_lens, int32_t num_seq
                                         partition_size, &s);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
-  if (!context_lens) return PKV_ERR_INVALID_ARG;
+  if (!context_lens || !aligned4(context_lens) || !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < s.plan_bytes) return PKV_ERR_WORKSPACE;
   pkv::AttentionArgs a{};
   a.context_lens = context_lens;
@@ -702,6 +725,9 @@ pkv_status pkv_slot_mapping_multi_query(const int32_t* block_tables, const int32
   if (num_seqs == 0) return PKV_ERR_INVALID_ARG;   // tokens need a sequence
   if (!block_tables || !context_lens || !query_start_loc || !slot_mapping)
     return PKV_ERR_INVALID_ARG;
+  if (!aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start_loc) ||
+      !aligned4(slot_mapping))
+    return PKV_ERR_INVALID_ARG;
   return hip_status(pkv::launch_slot_mapping_multi(
       block_tables, context_lens, query_start_loc, slot_mapping, num_seqs, num_tokens,
       max_blocks_per_seq, log2_exact(block_size), num_blocks, static_cast<hipStream_t>(stream)));
@@ -744,11 +770,19 @@ pkv_status pkv_paged_attention_multi_query(void* out, const void* query, const v
     return PKV_ERR_UNSUPPORTED;
   if (!(head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
   if (!(block_size == 16 || block_size == 32)) return PKV_ERR_UNSUPPORTED;
-  if (num_tokens > kMaxItems256) return PKV_ERR_UNSUPPORTED;   // the merge: a workgroup per token
+  // grids: the merge runs max_units * num_kv_heads + num_tokens workgroups of 256
+  // threads, the prefill units at most max_units * num_kv_heads (rounded up to 8) of 512
+  const int64_t unit_items = m.max_units * num_kv_heads;
+  if (unit_items + num_tokens > kMaxItems256 || (unit_items + 8) > int64_t{UINT32_MAX} / 512)
+    return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (num_seqs == 0) return PKV_ERR_INVALID_ARG;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
       !query_start_loc)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start_loc) ||
+      !aligned16(workspace))
     return PKV_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < m.ws_bytes) return PKV_ERR_WORKSPACE;
   pkv::AttentionArgs a{};

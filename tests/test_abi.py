@@ -144,6 +144,31 @@ def test_decode_rejects(lib, cpu_only, kw, status):
     assert _decode(lib, **kw) == status
 
 
+ODD16 = ctypes.c_void_p(0x1008)      # 8-byte aligned, not 16
+ODD4 = ctypes.c_void_p(0x1002)       # 2-byte aligned, not 4
+
+
+@pytest.mark.parametrize("kw", [dict(out=ODD16), dict(query=ODD16), dict(kc=ODD16),
+                                dict(vc=ODD16), dict(ws=ODD16), dict(bt=ODD4), dict(cl=ODD4),
+                                dict(P=-1, query=ODD16), dict(P=-1, cl=ODD4)])
+def test_decode_rejects_misaligned_buffers(lib, cpu_only, kw):
+    # rows move in 16-byte pieces, int32 arrays element by element
+    assert _decode(lib, **kw) == INV
+
+
+def test_writes_and_copies_reject_misaligned_buffers(lib, cpu_only):
+    w = lib.pkv_kv_cache_write
+    assert w(ODD16, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 1024, BF16, NULL) == INV
+    assert w(FAKE, FAKE, FAKE, ODD16, FAKE, 4, 8, 128, 16, 1024, BF16, NULL) == INV
+    assert w(FAKE, FAKE, FAKE, FAKE, ODD4, 4, 8, 128, 16, 1024, BF16, NULL) == INV
+    s = lib.pkv_slot_mapping
+    assert s(ODD4, FAKE, FAKE, 4, 64, 16, 1024, NULL) == INV
+    assert s(FAKE, FAKE, ODD4, 4, 64, 16, 1024, NULL) == INV
+    c = lib.pkv_copy_blocks
+    assert c(ODD16, FAKE, FAKE, 4, 8, 128, 16, 1024, BF16, NULL) == INV
+    assert c(FAKE, FAKE, ODD4, 4, 8, 128, 16, 1024, BF16, NULL) == INV
+
+
 def test_default_partition_needs_the_default_workspace(lib, cpu_only):
     # P = 0 takes the fixed-partition workspace of P = 512, not the balanced one
     need = _ws(4, 32, 128, 2)                          # MB 64 x 16 tokens = 2 partitions
@@ -335,3 +360,39 @@ def test_load_library_refuses_a_second_file(lib, tmp_path):
     other.write_bytes(b"")
     with pytest.raises(RuntimeError, match="already loaded"):
         _lib.load_library(str(other))
+
+
+def _mq(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qsl=FAKE, B=4, T=20, H=32,
+             Hkv=8, D=128, BS=16, MB=64, NB=1024, scale=0.088, kvd=BF16, outd=F32, ws=FAKE,
+             wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return lib.pkv_paged_attention_multi_query(
+        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["qsl"], a["B"], a["T"], a["H"],
+        a["Hkv"], a["D"], a["BS"], a["MB"], a["NB"], a["scale"], a["kvd"], a["outd"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(query=NULL), INV),
+    (dict(qsl=NULL), INV),
+    (dict(out=ODD16), INV),
+    (dict(query=ODD16), INV),
+    (dict(kc=ODD16), INV),
+    (dict(ws=ODD16), INV),
+    (dict(qsl=ODD4), INV),
+    (dict(bt=ODD4), INV),
+    (dict(B=0), INV),                  # tokens need a sequence
+    (dict(D=96), UNS),
+    (dict(H=24), UNS),                 # group of 3
+    (dict(ws=NULL), WS),
+    (dict(wsb=16), WS),
+    # the merge's grid: units x kv heads + tokens workgroups of 256 threads
+    (dict(B=1, T=(1 << 24) - (1 << 17), H=1, Hkv=1, D=64, wsb=1 << 62), UNS),
+])
+def test_multi_query_rejects(lib, cpu_only, kw, status):
+    assert _mq(lib, **kw) == status
+
+
+def test_multi_query_empty_step_is_noop(lib, cpu_only):
+    assert _mq(lib, T=0, out=NULL, query=NULL, ws=NULL, wsb=0) == OK
