@@ -649,7 +649,10 @@ void paged_attention_multi_kernel(AttentionArgs a) {
 //  - stages 32-token tiles, so that P.V runs on the full-rate v_mfma_f32_16x16x32_bf16
 //    with k = the lane's four tokens of each 16-token half: the lane's own eight
 //    probabilities form its A operand (as hi and lo bf16 parts, two instructions),
-//    and its B operand packs the matching eight value rows.
+//    and transposed LDS reads give its B operand, the matching eight value rows' entries
+//    of one dim (no byte permutes);
+//  - stages the output through the ring at the end, so that its stores write whole
+//    rows.
 // Rows of a sequence whose context lists a block id outside the pool are all NaN
 // (the workgroup checks the whole table row first).
 constexpr int kPfWaves = kMqPrefillUnit / 32;   // 8 waves, 32 rows each
@@ -658,6 +661,25 @@ constexpr int kPfTok = 32;                       // tokens per tile
 #define PKV_PREFILL_NBUF 4
 #endif
 constexpr int kPfNbuf = PKV_PREFILL_NBUF;        // tiles in the ring
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Maxima of raw scores as the hardware instructions alone.  fmaxf on values the
+// compiler cannot prove canonical (matrix results, lane swaps) gets a canonicalising
+// move per operand first: 12 of the tile's vector instructions per wave.  A NaN score
+// reaches its exponential, and so its row's output, either way.
+__device__ __forceinline__ float hw_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float hw_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 template <int G>
 __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
@@ -826,10 +848,14 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     bool rise = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float a3 = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), sv[rb][2]);
-      const float b3 = fmaxf(fmaxf(sv[rb][3], sv[rb][4]), sv[rb][5]);
-      const float c3 = fmaxf(fmaxf(sv[rb][6], sv[rb][7]), a3);
-      const float mx = max_xor32(max_xor16(fmaxf(b3, c3))) * scale;
+      const float a3 = hw_max3(sv[rb][0], sv[rb][1], sv[rb][2]);
+      const float b3 = hw_max3(sv[rb][3], sv[rb][4], sv[rb][5]);
+      const float c3 = hw_max3(sv[rb][6], sv[rb][7], a3);
+      float mx = hw_max(b3, c3);
+      auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = hw_max(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = hw_max(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * scale;
       const bool up = mx > m_run[rb] + kRebase;
       mnew[rb] = up ? mx : m_run[rb];
       alpha[rb] = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
@@ -871,42 +897,59 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
       }
     }
   };
-  // half hv of the value rows of the lane's eight tokens: columns 8 col + 4 hv ..
-  // 8 col + 4 hv + 3 (two words of each row); rows past the context (which may hold
-  // NaN) zeroed when zero_tail
-  auto read_v = [&](int tt, const uint4* vb, int hv, uint32_t (&w)[8][2], bool zero_tail) {
+  // Value operand of output block e, dims 16 e .. 16 e + 15 (lane column n: dim
+  // 16 e + n), over the lane's eight k slots: tokens 16 h + 4 quarter + i of the tile
+  // (h < 2, i < 4), the order of the probabilities in ph / pl.  Two transposed LDS
+  // reads per block (ds_read_b64_tr_b16): within each 16-lane quarter, lane 4 i + m
+  // addresses the 8 bytes of token 16 h + 4 quarter + i's row that hold dims
+  // 16 e + 4 m .. 16 e + 4 m + 3, and the read hands lane n the bf16 of dim 16 e + n
+  // from each of the four rows, in k order.  Slot j of row r is stored at j ^ (r & 15),
+  // so the lane's byte offset is tr_base + 32 (e ^ tr_x) for h = 0, 16 rows further
+  // for h = 1.
+  const int tr_row = 4 * quarter + (col >> 2);
+  const int tr_m = col & 3;
+  const uint32_t tr_base = (uint32_t)(tr_row * ROWB + ((((tr_m >> 1) ^ tr_row) & 1) << 4) +
+                                      ((tr_m & 1) << 3));
+  const uint32_t tr_x = (uint32_t)((tr_row & 15) >> 1);
+  auto read_v = [&](int tt, const uint4* vb, int hv, bf16x8 (&bv)[4], bool zero_tail) {
+    const uint32_t base = lds_addr(vb) + tr_base;
 #pragma unroll
-    for (int sr = 0; sr < 8; ++sr) {
-      const int vr = 16 * (sr >> 2) + 4 * quarter + (sr & 3);
-      const uint2 c = reinterpret_cast<const uint2*>(vb)[2 * (vr * SLOTS + (col ^ (vr & 15))) + hv];
-      w[sr][0] = c.x; w[sr][1] = c.y;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t o = base + (((uint32_t)(4 * hv + k) ^ tr_x) << 5);
+      const lds_s16x4* p0 = reinterpret_cast<const lds_s16x4*>((size_t)o);
+      const lds_s16x4* p1 = reinterpret_cast<const lds_s16x4*>((size_t)(o + 16 * ROWB));
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p1));
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      bv[k] = __builtin_bit_cast(bf16x8, both);
     }
     if (zero_tail && tt * kPfTok + kPfTok > ctx) {
+      // rows past the context may hold NaN: zero the lane's k slots of those tokens
       keep_branch();
+      uint32_t mk[4];
 #pragma unroll
-      for (int sr = 0; sr < 8; ++sr)
-        if (tt * kPfTok + 16 * (sr >> 2) + 4 * quarter + (sr & 3) >= ctx) w[sr][0] = w[sr][1] = 0u;
+      for (int d = 0; d < 4; ++d) {
+        const int t0 = tt * kPfTok + 16 * (d >> 1) + 4 * quarter + 2 * (d & 1);
+        mk[d] = (t0 < ctx ? 0xffffu : 0u) | (t0 + 1 < ctx ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint4 u = __builtin_bit_cast(uint4, bv[k]);
+        u.x &= mk[0]; u.y &= mk[1]; u.z &= mk[2]; u.w &= mk[3];
+        bv[k] = __builtin_bit_cast(bf16x8, u);
+      }
     }
   };
-  // acc += P . V for output blocks 4 hv .. 4 hv + 3 on v_mfma_f32_16x16x32_bf16: block e
-  // is column 8 col + e of the eight token rows (even e the low bf16 of a word, odd e
-  // the high one)
-  auto pv = [&](const uint32_t (&w)[8][2], int hv, const bf16x8 (&ph)[RB], const bf16x8 (&pl)[RB]) {
+  // acc += P . V for output blocks 4 hv .. 4 hv + 3 on v_mfma_f32_16x16x32_bf16 (hi and
+  // lo parts of P)
+  auto pv = [&](const bf16x8 (&bv)[4], int hv, const bf16x8 (&ph)[RB], const bf16x8 (&pl)[RB]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = 4 * hv + k;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const int d = k >> 1;
-      uint4 bw;
-      bw.x = __builtin_amdgcn_perm(w[1][d], w[0][d], sel);
-      bw.y = __builtin_amdgcn_perm(w[3][d], w[2][d], sel);
-      bw.z = __builtin_amdgcn_perm(w[5][d], w[4][d], sel);
-      bw.w = __builtin_amdgcn_perm(w[7][d], w[6][d], sel);
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rb], bv, acc[rb][e], 0, 0, 0);
-        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rb], bv, acc[rb][e], 0, 0, 0);
+        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rb], bv[k], acc[rb][e], 0, 0, 0);
+        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rb], bv[k], acc[rb][e], 0, 0, 0);
       }
     }
   };
@@ -928,8 +971,7 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
   // done with step t - 1 and so with tile t - 1), issues tile t + kPfNbuf - 1 into
   // tile t - 1's slot, and then runs one block of straight-line work: the scores of
   // tile t + 1 on the matrix cores beside the probabilities of tile t on the vector
-  // unit, then P.V of tile t on the matrix cores beside the value permutes of tile t
-  // and the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
+  // unit, then P.V of tile t on the matrix cores beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
   // matrix instructions but not another wave's, so the block interleaves them
   // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
   // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
@@ -960,7 +1002,7 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     if (tt + 1 < wtiles) {
       // tile tt is not the unit's last, so its value rows are all inside the context
       auto block = [&](bool edge) {
-        uint32_t w0[8][2], w1[8][2];
+        bf16x8 w0[4], w1[4];
         scores(kring[(tt + 1) % kPfNbuf], s_nxt);
         read_v(tt, vring[tt % kPfNbuf], 0, w0, false);
         probs(s_cur, m_run, ph, pl, lsum);
@@ -982,10 +1024,10 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {                        // scores beside probabilities
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {                        // P.V beside permutes, maxima
+        for (int i = 0; i < 32; ++i) {                        // P.V beside the maxima
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
         }
@@ -993,7 +1035,7 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
       block((tt + 1) * kPfTok + kPfTok - 1 > wpos_lo);
     } else {
       if (tt < wtiles) {
-        uint32_t w0[8][2], w1[8][2];
+        bf16x8 w0[4], w1[4];
         read_v(tt, vring[tt % kPfNbuf], 0, w0, true);
         probs(s_cur, m_run, ph, pl, lsum);
         pv(w0, 0, ph, pl);
@@ -1022,34 +1064,56 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     step(tt + 1, sB, sA);
   }
   wait_copies<0>();
+  bare_barrier();   // every wave is done with the ring, which now stages the output
   if (!wave_live) return;
 
-  // rows 16 rb + 4 quarter + i of the wave: sum across the four lanes of each row,
-  // normalise, store columns 8 col .. 8 col + 7
+  // Rows 16 rb + 4 quarter + i of the wave: sum across the four lanes of each row,
+  // normalise, and write them to the wave's 8 KiB of the ring as [row][dim] (lane n
+  // holds dims 16 e + n); read back 16 contiguous bytes per lane, so that every store
+  // covers whole rows.
+  float* stage = reinterpret_cast<float*>(wave < 4 ? &kring[0][0] : &vring[0][0]) + (wave & 3) * 16 * D;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_row = sum_xor32(sum_xor16(l_lane[rb]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wrow0 + rb * 16 + 4 * quarter + i;
       const float lr = __shfl(l_row, 4 * quarter + i);
-      const int jq = j0 + r / G;
-      if (jq >= qlen) continue;
       const float inv = seq_bad ? __builtin_nanf("") : 1.f / lr;
-      const int64_t orow = ((int64_t)(q0 + jq) * H + g * G + r % G) * D + col * CPL;
-      if (a.out_bf16) {
-        uint4 v;
-        v.x = f32_to_bf16_rne(acc[rb][0][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][1][i] * inv) << 16;
-        v.y = f32_to_bf16_rne(acc[rb][2][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][3][i] * inv) << 16;
-        v.z = f32_to_bf16_rne(acc[rb][4][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][5][i] * inv) << 16;
-        v.w = f32_to_bf16_rne(acc[rb][6][i] * inv) | (uint32_t)f32_to_bf16_rne(acc[rb][7][i] * inv) << 16;
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = v;
-      } else {
-        float* dst = static_cast<float*>(a.out) + orow;
-        const floatx4 v0 = {acc[rb][0][i] * inv, acc[rb][1][i] * inv, acc[rb][2][i] * inv, acc[rb][3][i] * inv};
-        const floatx4 v1 = {acc[rb][4][i] * inv, acc[rb][5][i] * inv, acc[rb][6][i] * inv, acc[rb][7][i] * inv};
-        *reinterpret_cast<floatx4*>(dst) = v0;
-        *reinterpret_cast<floatx4*>(dst + 4) = v1;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) stage[(4 * quarter + i) * D + 16 * e + col] = acc[rb][e][i] * inv;
+    }
+    // (a wave's LDS accesses complete in order: the reads see these writes, and the next
+    // block's writes come after these reads)
+    if (a.out_bf16) {
+#pragma unroll
+      for (int k = 0; k < 16 * (D / 8) / kWave; ++k) {
+        const int c = k * kWave + lane;
+        const int i = c / (D / 8), ch = c % (D / 8);
+        const floatx4 x = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8);
+        const floatx4 y = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8 + 4);
+        const int r = wrow0 + rb * 16 + i;
+        const int jq = j0 + r / G;
+        if (jq < qlen) {
+          uint4 v;
+          v.x = f32_to_bf16_rne(x[0]) | (uint32_t)f32_to_bf16_rne(x[1]) << 16;
+          v.y = f32_to_bf16_rne(x[2]) | (uint32_t)f32_to_bf16_rne(x[3]) << 16;
+          v.z = f32_to_bf16_rne(y[0]) | (uint32_t)f32_to_bf16_rne(y[1]) << 16;
+          v.w = f32_to_bf16_rne(y[2]) | (uint32_t)f32_to_bf16_rne(y[3]) << 16;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) +
+                                    ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 8) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
+        const int c = k * kWave + lane;
+        const int i = c / (D / 4), ch = c % (D / 4);
+        const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
+        const int r = wrow0 + rb * 16 + i;
+        const int jq = j0 + r / G;
+        if (jq < qlen)
+          *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) +
+                                      ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 4) = v;
       }
     }
   }
