@@ -12,10 +12,12 @@
 // Work decomposition.  One workgroup of four wave64s per (kv head, context
 // partition, sequence).  A partition of P tokens is cut into 16-token tiles; wave w
 // takes tiles w, w+4, w+8, ..., a few at a time.  For every tile:
-//   * Q.K^T on the matrix cores: one 16x16 MFMA output holds the scores of up to 16
-//     query heads (the kv head's GQA group, zero-padded) against 16 tokens.  Each
-//     lane feeds the MFMA a 16-byte piece of one key row straight from HBM, so a
-//     tile's keys are read once, in 64-byte runs per row and instruction.
+//   * Q.K^T on the matrix cores for GQA groups of four or eight heads: one 16x16
+//     MFMA output holds the scores of the group (zero-padded to 16 rows) against 16
+//     tokens.  Each lane feeds the MFMA a 16-byte piece of one key row straight from
+//     HBM, so a tile's keys are read once, in 64-byte runs per row and instruction.
+//     Groups of one or two heads take the same pieces into dot products on the VALU
+//     (each lane a quarter of the dims, the quarters added by lane-row swaps).
 //   * softmax on the VALU with a running (per wave) maximum in the base-2 exponent
 //     domain; row maxima and sums use DPP within 16-lane rows.
 //   * P.V on the VALU: 16-byte pieces of value rows, fp32 fused multiply-adds, the
@@ -29,6 +31,7 @@
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
 #include "pkv_plan.hpp"
+#include "pkv_stream.hpp"
 #include "pkv_tile.hpp"
 
 namespace pkv {
@@ -40,9 +43,6 @@ constexpr int kBufferFlags = 0x00020000;
 // Build-time tuning knobs (defaults: the measured best on MI355X).
 #ifndef PKV_WAVES_PER_EU
 #define PKV_WAVES_PER_EU 1         // occupancy floor handed to the register allocator
-#endif
-#ifndef PKV_Q_IN_LDS
-#define PKV_Q_IN_LDS 0             // 1: the query operand lives in LDS, not registers
 #endif
 
 size_t plan_bytes(int64_t num_seqs, int64_t max_parts) {
@@ -119,27 +119,25 @@ void paged_attention_partition_kernel(AttentionArgs a) {
   const int li = lane % NCH;       // 16-byte chunk within a value row
 
   // Query rows of this kv head's group, as the MFMA A operand (rows >= G are zero).
-#if PKV_Q_IN_LDS
-  // Kept in LDS and re-read for every tile, which frees the registers it would pin.
-  __shared__ uint4 q_lds[QKC][kWave];
-  if (wave == 0) {
-    const char* qrow = static_cast<const char*>(a.query) +
-                       ((int64_t)seq * H + g * G + (col < G ? col : 0)) * D * EB;
+  // Groups of one or two heads would fill one or two of its 16 rows: their scores are
+  // dot products on the VALU, with every head's chunks 4c + quarter of the query in qv.
+  constexpr bool kValuQK = G <= 2;
+  uint4 qa[kValuQK ? 1 : QKC];
+  uint4 qv[kValuQK ? G : 1][kValuQK ? QKC : 1];
+  if constexpr (kValuQK) {
 #pragma unroll
-    for (int c = 0; c < QKC; ++c)
-      q_lds[c][lane] = col < G ? load16(qrow, (4 * c + quarter) * 16) : make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-#else
-  uint4 qa[QKC];
-  {
+    for (int h = 0; h < G; ++h) {
+      const char* qrow = static_cast<const char*>(a.query) + ((int64_t)seq * H + g * G + h) * D * EB;
+#pragma unroll
+      for (int c = 0; c < QKC; ++c) qv[h][c] = load16(qrow, (4 * c + quarter) * 16);
+    }
+  } else {
     const char* qrow = static_cast<const char*>(a.query) +
                        ((int64_t)seq * H + g * G + (col < G ? col : 0)) * D * EB;
 #pragma unroll
     for (int c = 0; c < QKC; ++c)
       qa[c] = col < G ? load16(qrow, (4 * c + quarter) * 16) : make_uint4(0, 0, 0, 0);
   }
-#endif
 
   // Byte offsets: the block base is the same for the whole wave (a scalar), the
   // per-lane part fits in 32 bits.
@@ -214,14 +212,18 @@ void paged_attention_partition_kernel(AttentionArgs a) {
   // Scores, running maximum, probabilities and P.V for one loaded tile.
   auto compute = [&](const Loads& r) {
     if (r.ntok == 0) return;
-#if PKV_Q_IN_LDS
-    uint4 qa[QKC];
-    int ql = lane;
-    asm volatile("" : "+v"(ql));   // keep the reads in the loop
+    floatx4 s4;
+    if constexpr (kValuQK) {
+      // the lane's chunks of token col's key against each head's query, the four
+      // quarters' sums added; element j holds head j % G, as the MFMA rows would
+      float sh[G];
 #pragma unroll
-    for (int c = 0; c < QKC; ++c) qa[c] = q_lds[c][ql];
-#endif
-    const floatx4 s4 = tile_scores<T, QKC>(qa, r.k);
+      for (int h = 0; h < G; ++h) sh[h] = sum_xor32(sum_xor16(lane_dot<T, QKC>(qv[h], r.k)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4[j] = sh[j % G];
+    } else {
+      s4 = tile_scores<T, QKC>(qa, r.k);
+    }
     const bool live = col < r.ntok;
     float sc[4], gmax[4];
 #pragma unroll

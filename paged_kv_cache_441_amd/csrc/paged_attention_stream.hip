@@ -40,9 +40,11 @@
 // NBUF tiles rotate through distinct LDS buffers.  Per tile: issue the copies of
 // the tile NBUF - 1 ahead, wait for this wave's copies of the tile, barrier, compute
 // the tile from LDS: Q.K^T on the matrix cores (the GQA group of the wave's head as
-// the A operand), online softmax in the base-2 exponent domain, P.V on the VALU in
-// fp32; barrier.  While a wave waits for a tile, the tiles after it are already in
-// flight.  No atomics: results do not depend on timing.
+// the A operand; groups of one or two heads as dot products on the VALU), online
+// softmax in the base-2 exponent domain, P.V on the matrix cores (bf16 and E4M3 caches,
+// 128-element heads, groups of four or eight) or on the VALU in fp32; barrier.  While
+// a wave waits for a tile, the tiles after it are already in flight.  No atomics:
+// results do not depend on timing.
 #include "pkv_device.hpp"
 #include "pkv_launch.hpp"
 #include "pkv_plan.hpp"
@@ -112,9 +114,12 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   constexpr int RPS = kWave / NPC;          // value rows per wave read
   constexpr int STEPS = TOK / RPS;
   constexpr int kQuarters = (G + 3) / 4;    // MFMA output quarters holding real heads
-  // P.V on bf16 matrix instructions (bf16 and E4M3 caches, D = 128); fp32 caches and
-  // D = 64 use fp32 FMAs on the VALU
-  constexpr bool kMfmaPV = (kF8 || std::is_same<T, BF16>::value) && D == 128;
+  // GQA groups of four or eight heads: Q.K^T on the matrix cores, and P.V too with bf16
+  // and E4M3 caches and D = 128 (fp32 caches and D = 64 use fp32 FMAs on the VALU).
+  // Groups of one or two heads would fill one or two of a matrix instruction's 16
+  // rows: their dot products and P.V run on the VALU.
+  constexpr bool kValuQK = G <= 2;
+  constexpr bool kMfmaPV = (kF8 || std::is_same<T, BF16>::value) && D == 128 && !kValuQK;
   static_assert(NCH % 4 == 0 || kF8, "row shape");
   constexpr int L = 2 * St::kCopies;        // copy instructions per wave per tile
   constexpr int NS = St::kTileSlots;
@@ -319,7 +324,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   // in its steps of 4) in row chunks 4c + quarter.  With an E4M3 cache a lane instead
   // takes the contiguous query chunks QKC * quarter + c, matching the contiguous key
   // bytes it reads; a dot product may sum its terms in any order.
-  uint4 qa[QKC];
+  uint4 qa[kValuQK ? 1 : QKC];
   bool q_fresh = false;   // a query copy was issued after the last step's copies
   auto load_query = [&](int s) {
     q_fresh = true;
@@ -331,10 +336,14 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         dma16(src, (uint32_t)((i * kWave + lane) * 16), lds_addr(q_lds[wave]) + i * 1024);
     }
   };
+  // (VALU scores read the query from q_lds at every tile instead: it stays there until
+  // the sequence's last tile is done)
   auto read_query = [&]() {
-    const uint4* q = q_lds[wave] + (col % G) * (D * QEB / 16);
+    if constexpr (!kValuQK) {
+      const uint4* q = q_lds[wave] + (col % G) * (D * QEB / 16);
 #pragma unroll
-    for (int c = 0; c < QKC; ++c) qa[c] = q[kF8 ? QKC * quarter + c : 4 * c + quarter];
+      for (int c = 0; c < QKC; ++c) qa[c] = q[kF8 ? QKC * quarter + c : 4 * c + quarter];
+    }
   };
 
   float m_run[G];
@@ -391,7 +400,25 @@ void paged_attention_stream_kernel(AttentionArgs a) {
       for (int c = 0; c < QKC; ++c)
         kk[c] = kb[kr * St::kSlots + ((wave * NCH + 4 * c + quarter) ^ St::swz(kr))];
     }
-    const floatx4 s4 = tile_scores<QT, QKC>(qa, kk);
+    floatx4 s4;
+    if constexpr (kValuQK) {
+      // lane (quarter, col): its chunks of token col's key against each head's query,
+      // then the four quarters' sums added (every quarter ends with the same value);
+      // element j holds head j % G, as the matrix instruction's rows would
+      float sh[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        uint4 qc[QKC];   // head h's chunks of the lane's dims (the key chunks it holds)
+#pragma unroll
+        for (int c = 0; c < QKC; ++c)
+          qc[c] = q_lds[wave][h * (D * QEB / 16) + (kF8 ? QKC * quarter + c : 4 * c + quarter)];
+        sh[h] = sum_xor32(sum_xor16(lane_dot<QT, QKC>(qc, kk)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4[j] = sh[j % G];
+    } else {
+      s4 = tile_scores<QT, QKC>(qa, kk);
+    }
     const bool live = col < ntok;
     float sc[4];
     int gkey[4];

@@ -66,6 +66,35 @@ __device__ __forceinline__ floatx4 tile_scores<F32, 8>(const uint4 (&q)[8], cons
   return tile_scores_f32<8>(q, k);
 }
 
+// One lane's part of a query-key dot product on the VALU: its QKC 16-byte chunks of
+// one head's query against the same dims of a key row, bfloat16 pairs by v_dot2 (the
+// products are exact in fp32) or fp32 FMAs; two partial sums for a shorter chain.
+// For GQA groups of one or two heads, where a 16-row matrix instruction would hold
+// one or two real rows.
+template <typename T, int QKC>
+__device__ __forceinline__ float lane_dot(const uint4 (&q)[QKC], const uint4 (&k)[QKC]) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < QKC; ++c) {
+    if constexpr (T::kElemBytes == 4) {
+      s0 = fmaf(__uint_as_float(q[c].x), __uint_as_float(k[c].x), s0);
+      s1 = fmaf(__uint_as_float(q[c].y), __uint_as_float(k[c].y), s1);
+      s0 = fmaf(__uint_as_float(q[c].z), __uint_as_float(k[c].z), s0);
+      s1 = fmaf(__uint_as_float(q[c].w), __uint_as_float(k[c].w), s1);
+    } else {
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[c].x),
+                                          __builtin_bit_cast(bf16x2, k[c].x), s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[c].y),
+                                          __builtin_bit_cast(bf16x2, k[c].y), s1, false);
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[c].z),
+                                          __builtin_bit_cast(bf16x2, k[c].z), s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[c].w),
+                                          __builtin_bit_cast(bf16x2, k[c].w), s1, false);
+    }
+  }
+  return s0 + s1;
+}
+
 __device__ __forceinline__ uint4 load16(const void* base, int64_t byte_off) {
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + byte_off);
 }
