@@ -1151,7 +1151,8 @@ static hipError_t launch_prefill(const AttentionArgs& a, hipStream_t stream) {
 template <int D>
 __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(AttentionArgs a) {
   constexpr int C4 = D / 4;              // float4 pieces of a row
-  constexpr int KS = 4;                  // shares whose records are loaded together
+  constexpr int KS = 2;                  // shares whose records are loaded together
+  constexpr int NI = 4;                  // items per thread whose records are loaded together
   const int H = a.num_heads;
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
@@ -1201,35 +1202,55 @@ __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(Atten
   const int nrows = min(rows, (qlen - uj0) * G);          // the unit's real rows
   const int64_t lab_stride = (int64_t)Hkv * rows;           // between labels L and L + 1
   const int64_t base = ((int64_t)u * Hkv + g) * rows;        // record row 0 under label 0
-  for (int k = threadIdx.x; k < nrows * C4; k += 256) {
-    const int r = k / C4, c = k % C4;
-    Running acc{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    for (int wb = w0; wb <= w1; wb += KS) {
-      float l[KS], m[KS];
-      floatx4 o[KS];
+  // Each thread merges NI (row, float4) items of the unit; the records of all NI items
+  // and KS shares are loaded before any is merged, so one round of loads covers a unit
+  // split over at most KS shares.
+  const int items = nrows * C4;
+  for (int k0 = threadIdx.x; k0 < items; k0 += 256 * NI) {
+    Running acc[NI];
 #pragma unroll
-      for (int q = 0; q < KS; ++q) {
-        const int ww = min(wb + q, w1);
-        const int64_t rec = base + (int64_t)ww * lab_stride + r;
-        l[q] = a.ws_l[rec];
-        m[q] = a.ws_m[rec];
-        o[q] = reinterpret_cast<const floatx4*>(a.ws_o + rec * D)[c];
+    for (int i = 0; i < NI; ++i) acc[i] = Running{-__builtin_inff(), 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    for (int wb = w0; wb <= w1; wb += KS) {
+      float l[NI][KS], m[NI][KS];
+      floatx4 o[NI][KS];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int k = min(k0 + 256 * i, items - 1);   // past the unit's items: a repeat
+        const int r = k / C4, c = k % C4;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          const int ww = min(wb + q, w1);
+          const int64_t rec = base + (int64_t)ww * lab_stride + r;
+          l[i][q] = a.ws_l[rec];
+          m[i][q] = a.ws_m[rec];
+          o[i][q] = reinterpret_cast<const floatx4*>(a.ws_o + rec * D)[c];
+        }
       }
-      // Records of segments in which this row saw no token have l = 0 (and m = -inf);
+      // Records of segments in which a row saw no token have l = 0 (and m = -inf);
       // they weigh nothing.  A NaN l marks bad data and is kept.  Empty shares wrote
       // no record.
 #pragma unroll
       for (int q = 0; q < KS; ++q) {
         const int ww = wb + q;
         if (ww > w1 || !share_nonempty(ww, nwg, total)) continue;
-        if (!(l[q] > 0.f) && !(l[q] != l[q])) continue;
-        const Running sg{m[q], l[q], make_float4(o[q][0] * l[q], o[q][1] * l[q], o[q][2] * l[q],
-                                                 o[q][3] * l[q])};
-        merge_into(acc, sg);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (!(l[i][q] > 0.f) && !(l[i][q] != l[i][q])) continue;
+          const float lq = l[i][q];
+          const Running sg{m[i][q], lq, make_float4(o[i][q][0] * lq, o[i][q][1] * lq,
+                                                   o[i][q][2] * lq, o[i][q][3] * lq)};
+          merge_into(acc[i], sg);
+        }
       }
     }
-    const int jq = uj0 + r / G;
-    store_row4(a, ((int64_t)(q0 + jq) * H + g * G + r % G) * D + c * 4, acc);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = k0 + 256 * i;
+      if (k >= items) break;
+      const int r = k / C4, c = k % C4;
+      const int jq = uj0 + r / G;
+      store_row4(a, ((int64_t)(q0 + jq) * H + g * G + r % G) * D + c * 4, acc[i]);
+    }
   }
 }
 
