@@ -147,6 +147,89 @@ __device__ int block_scan(int n, F x_of, int* __restrict__ out) {
   return carry;
 }
 
+// ---- prefill schedule ------------------------------------------------------------------
+// Prefill units (kMqPrefillUnit rows over the unit's whole causal context) are split in
+// two pieces along the context, so that the longest units no longer set the kernel's
+// time; the piece that finishes second merges the pair.  The pieces are dealt to the
+// XCDs by (sequence, kv head) group, group k to XCD k % kXcds with the groups ranked by
+// context length (longest first): the units of one group share their tiles in one L2,
+// and every XCD gets a similar mix.  Within an XCD the groups' pieces form one list,
+// largest first (a group's units last to first); the XCD's workgroups take it in snake
+// order (round r: workgroup j takes position rW + j, or rW + W - 1 - j on odd rounds),
+// which pairs large pieces with small ones.
+//
+// Workspace (words; NI = max_units * num_kv_heads items, NG = num_seqs * num_kv_heads
+// groups, J = ceil(NG / kXcds)):
+//   m array: the records' m values [2 NI * kMqPrefillUnit], then the per-XCD prefix sums
+//            of pieces over its groups [kXcds][J + 1], then the ranked sequences [B],
+//            then the plan's scan [kXcds J + 1];
+//   l array: the records' l values [2 NI * kMqPrefillUnit], then one counter per item;
+//   o array: the records' rows [2 NI * kMqPrefillUnit][head_dim].
+// Record of piece h of item i, row r: (2 i + h) * kMqPrefillUnit + r.
+struct PrefillLayout {
+  int NI, NG, J;
+  int* xcum;    // [kXcds][J + 1]
+  int* order;   // [num_seqs]: sequence of each rank
+  int* scan;    // [kXcds J + 1]: the plan's scan, XCD-major
+  int* ctr;     // [NI]
+  __device__ explicit PrefillLayout(const AttentionArgs& a) {
+    NI = a.max_units * a.num_kv_heads;
+    NG = a.num_seqs * a.num_kv_heads;
+    J = (NG + kXcds - 1) / kXcds;
+    xcum = reinterpret_cast<int*>(a.ws_m + 2 * (int64_t)NI * kMqPrefillUnit);
+    order = xcum + kXcds * (J + 1);
+    scan = order + a.num_seqs;
+    ctr = reinterpret_cast<int*>(a.ws_l + 2 * (int64_t)NI * kMqPrefillUnit);
+  }
+};
+
+// Sequences are ranked only up to this many (beyond, they keep their index order).
+constexpr int kPfRankMax = 1024;
+
+__device__ void build_prefill_schedule(const AttentionArgs& a, int U) {
+  const int B = a.num_seqs, Hkv = a.num_kv_heads;
+  const PrefillLayout L(a);
+  for (int i = threadIdx.x; i < U * Hkv; i += kMqPlanThreads) L.ctr[i] = 0;
+  // rank: context length, longest first (ties by index); sequences without units last
+  __shared__ int key[kPfRankMax];
+  auto key_of = [&](int i) {
+    return a.seq_unit[i + 1] > a.seq_unit[i] ? a.context_lens[i] : -1;
+  };
+  if (B <= kPfRankMax) {
+    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) key[i] = key_of(i);
+    __syncthreads();
+    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) {
+      const int ki = key[i];
+      int r = 0;
+      for (int j = 0; j < B; ++j) {
+        const int kj = key[j];
+        r += kj > ki || (kj == ki && j < i);
+      }
+      L.order[r] = i;
+    }
+  } else {
+    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) L.order[i] = i;
+  }
+  __syncthreads();
+  // per XCD x: exclusive prefix sums over its groups k = kXcds j + x (rank k / Hkv, kv
+  // head k % Hkv) of their pieces, two per unit; entry J is the XCD's total.  One scan
+  // over t = x J + j (XCD-major), then each XCD's sums less its first.
+  const int J = L.J;
+  auto pieces_of = [&](int t) {
+    const int k = kXcds * (t % J) + t / J;
+    if (k >= L.NG) return 0;
+    const int i = L.order[k / Hkv];
+    return 2 * (a.seq_unit[i + 1] - a.seq_unit[i]);
+  };
+  const int tot = block_scan<kMqPlanThreads>(kXcds * J, pieces_of, L.scan);
+  if (threadIdx.x == 0) L.scan[kXcds * J] = tot;
+  __syncthreads();
+  for (int t = threadIdx.x; t < kXcds * (J + 1); t += kMqPlanThreads) {
+    const int x = t / (J + 1), j = t % (J + 1);
+    L.xcum[t] = L.scan[x * J + j] - L.scan[x * J];
+  }
+}
+
 __global__ __launch_bounds__(kMqPlanThreads) void multi_plan_kernel(AttentionArgs a) {
   const int B = a.num_seqs;
   const int G = a.num_heads / a.num_kv_heads;
@@ -172,6 +255,11 @@ __global__ __launch_bounds__(kMqPlanThreads) void multi_plan_kernel(AttentionArg
     }
   }
   __syncthreads();
+  if (a.unit_rows == kMqPrefillUnit) {
+    if (threadIdx.x == 0) a.tile_hdr[2] = U;
+    build_prefill_schedule(a, U);
+    return;
+  }
   // positions of unit u: the tiles up to its last token's position, plus kSeqCost
   auto positions_of = [&](int u) {
     const int i = a.unit_seq[u];
@@ -635,26 +723,26 @@ void paged_attention_multi_kernel(AttentionArgs a) {
   wait_copies<0>();
 }
 
-// ---- long prompts with bf16 caches: one workgroup per 256-row unit -------------------
+// ---- long prompts with bf16 caches: 256-row units in two context pieces ----------------
 // Chunked prefill hands a few sequences many new tokens each.  There the work is the
 // matrix products, and what costs is re-reading a sequence's context for every unit
 // of its rows.  This mode:
 //  - makes units of 256 rows (kPfWaves waves of two 16-row MFMA blocks sharing one kv
-//    head's staged tiles), one workgroup each, over the unit's whole causal context:
-//    no split, no records, no merge;
-//  - gives the units of one (sequence, kv head) consecutive work-item indices, and
-//    item indices are dealt to the XCDs in equal contiguous ranges, so
-//    the units of a sequence and kv head run side by side on one XCD, reading the
-//    same tiles at about the same time: L2 serves the repeats;
+//    head's staged tiles); each (unit, kv head) item's causal context is cut into two
+//    halves, the pieces, computed by one workgroup each and merged by the later one
+//    (the prefill schedule above), so that a few long histories no longer set the time;
+//  - deals the pieces of one (sequence, kv head) to one XCD, where its units run side
+//    by side reading the same tiles at about the same time: L2 serves the repeats;
+//  - runs one workgroup per compute unit, each taking its XCD's pieces in snake order;
 //  - stages 32-token tiles, so that P.V runs on the full-rate v_mfma_f32_16x16x32_bf16
 //    with k = the lane's four tokens of each 16-token half: the lane's own eight
 //    probabilities form its A operand (as hi and lo bf16 parts, two instructions),
 //    and transposed LDS reads give its B operand, the matching eight value rows' entries
 //    of one dim (no byte permutes);
-//  - stages the output through the ring at the end, so that its stores write whole
-//    rows.
+//  - stages each piece's record through the ring at the end, so that its stores write
+//    whole rows.
 // Rows of a sequence whose context lists a block id outside the pool are all NaN
-// (the workgroup checks the whole table row first).
+// (each piece checks the whole table row first).
 constexpr int kPfWaves = kMqPrefillUnit / 32;   // 8 waves, 32 rows each
 constexpr int kPfTok = 32;                       // tokens per tile
 #ifndef PKV_PREFILL_NBUF
@@ -700,430 +788,493 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
   const int col = lane & 15;
   const int Hkv = a.num_kv_heads;
   const int H = Hkv * G;
-  // the merge that follows only writes the NaN rows of invalid sequences: one share
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.tile_hdr[1] = 1;
-  // the U * Hkv items are dealt to the XCDs in equal contiguous ranges (workgroup b
-  // runs on XCD b % 8): XCD x takes items [x c, (x + 1) c), c = ceil(items / 8), so
-  // no XCD holds more than its share; workgroups past them exit
-  const int U = ((cint32*)a.tile_hdr)[2];
-  const int n_items = U * Hkv;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int slot_in_xcd = blockIdx.x / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + slot_in_xcd;
-  if (slot_in_xcd >= per_xcd || item >= n_items) return;
-
-  // item -> (sequence, kv head, unit): items of sequence i are seq_unit[i] * Hkv ..,
-  // kv-head-major, so one sequence and kv head's units have consecutive indices
+  __shared__ int merge_flag;
+  const PrefillLayout PL(a);
   cint32* seq_unit = (cint32*)a.seq_unit;
-  int lo = 0, hi = a.num_seqs;              // seq_unit[lo] * Hkv <= item < seq_unit[hi] * Hkv
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (seq_unit[mid] * Hkv <= item) lo = mid; else hi = mid;
-  }
-  const int seq = lo;
-  const int u0 = seq_unit[seq];
-  const int nun = seq_unit[seq + 1] - u0;   // > 0 for the sequence holding the item
-  const int o = item - u0 * Hkv;
-  const int g = o / nun;
-  const int j0 = (o % nun) * TPB;           // first new token of the unit
-  cint32* qsl = (cint32*)a.query_start_loc;
-  const int q0 = qsl[seq];
-  const int qlen = qsl[seq + 1] - q0;
-  const int ctx = ((cint32*)a.context_lens)[seq];
-  const int j1 = min(qlen, j0 + TPB);
-  const int base_pos = ctx - qlen;          // position of new token 0
-  const int ntiles = (base_pos + j1 + kPfTok - 1) / kPfTok;
-
-  const int shift = a.block_shift;
-  const int bs_mask = (1 << shift) - 1;
-  const int MB = a.max_blocks_per_seq;
-  const int num_blocks = (int)a.num_blocks;
-  const int32_t* table = a.block_tables + (int64_t)seq * MB;
-
-  // every block of the context must be in the pool
-  bool bad_lane = false;
-  for (int b = lane; b < ((ctx + bs_mask) >> shift); b += kWave) {
-    const int32_t id = table[b];
-    bad_lane |= id < 0 || id >= num_blocks;
-  }
-  const bool seq_bad = __ballot(bad_lane) != 0;
-
-  // this wave's rows: r = 32 wave + 16 rb + col is new token j0 + r / G with query head
-  // g G + r % G (a row past the last new token repeats token j0 and is not stored)
-  const int wrow0 = wave * 16 * RB;
-  const int wj_lo = j0 + wrow0 / G;
-  const int wj_hi = min(j0 + (wrow0 + 16 * RB - 1) / G, qlen - 1);
-  const bool wave_live = wj_lo < qlen;
-  const int wpos_lo = base_pos + min(wj_lo, qlen - 1);   // positions the wave's rows see
-  const int wpos_hi = base_pos + wj_hi;
-  const int wtiles = wave_live ? wpos_hi / kPfTok + 1 : 0;
-
-  // queries; for a negative scale the query's sign bits are flipped (exact) so that
-  // the scale is positive and a row's largest raw score is its largest scaled one
-  // (a zero scale becomes the smallest normal float: every 2^(s * scale) is then 1 as
-  // for zero, and a masked -inf score stays -inf instead of turning NaN)
-  const float scale = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
-  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  uint4 qa[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = wrow0 + rb * 16 + col;
-    const int jq = j0 + r / G < qlen ? j0 + r / G : j0;
-    const char* row = static_cast<const char*>(a.query) +
-                      ((int64_t)(q0 + jq) * H + g * G + r % G) * ROWB;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 v = *reinterpret_cast<const uint4*>(row + (4 * c + quarter) * 16);
-      v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
-      qa[rb][c] = v;
+  cint32* order = (cint32*)PL.order;
+  // this workgroup's XCD (workgroup b runs on XCD b % 8) and its place among the W there
+  const int W = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
+  cint32* xc = (cint32*)PL.xcum + xcd * (PL.J + 1);
+  const int nx = xc[PL.J];
+  for (int rnd = 0;; ++rnd) {
+    const int pos = rnd * W + ((rnd & 1) ? W - 1 - jw : jw);   // snake order
+    if (pos >= nx) break;
+    // the group holding list position pos: the last glo < J with xc[glo] <= pos
+    int glo = 0, ghi = PL.J;
+    while (ghi - glo > 1) {
+      const int mid = (glo + ghi) >> 1;
+      if (xc[mid] <= pos) glo = mid; else ghi = mid;
     }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const int grp = kXcds * glo + xcd;
+    const int seq = order[grp / Hkv];
+    const int g = grp % Hkv;
+    const int in_grp = pos - xc[glo];
+    const int u0 = seq_unit[seq];
+    const int nun = seq_unit[seq + 1] - u0;   // > 0 for a group with pieces
+    const int unit = nun - 1 - (in_grp >> 1);  // a group's units last to first (largest first)
+    const int half = in_grp & 1;               // first or second half of the unit's context
+    const int item = u0 * Hkv + g * nun + unit;
+    const int j0 = unit * TPB;                 // first new token of the unit
+    cint32* qsl = (cint32*)a.query_start_loc;
+    const int q0 = qsl[seq];
+    const int qlen = qsl[seq + 1] - q0;
+    const int ctx = ((cint32*)a.context_lens)[seq];
+    const int j1 = min(qlen, j0 + TPB);
+    const int base_pos = ctx - qlen;          // position of new token 0
+    const int ntiles = (base_pos + j1 + kPfTok - 1) / kPfTok;
+    // this piece's tiles
+    const int t_lo = half ? ntiles / 2 : 0;
+    const int t_hi = half ? ntiles : ntiles / 2;
+    __syncthreads();   // the previous piece is done with the ring and merge_flag
 
-  // copies: wave w brings rows 4w .. 4w + 3 of each tile, lane l row 4w + l / 16, its
-  // 16-byte piece l % 16 stored at slot (l % 16) ^ row (rows are 16 slots)
-  const int64_t row_stride = (int64_t)Hkv * ROWB;
-  const int crow = 4 * wave + quarter;
-  const uint32_t copy_off = (uint32_t)(quarter * row_stride) + (uint32_t)(((col ^ crow) & 15) * 16);
-  const char* kcache = static_cast<const char*>(a.key_cache) + g * ROWB;
-  const char* vcache = static_cast<const char*>(a.value_cache) + g * ROWB;
-  auto issue = [&](int tt, int slot) {
-    int64_t off = 0;                        // rows past the context: the pool's first rows
-    const int t0 = tt * kPfTok + 4 * wave;
-    if (tt < ntiles && t0 < ctx) {
-      const int32_t blk = uniform(((cint32*)table)[t0 >> shift]);
-      if (blk >= 0 && blk < num_blocks) off = (((int64_t)blk << shift) + (t0 & bs_mask)) * row_stride;
-    }
-    dma16<Cpol::kDefault>(kcache + off, copy_off, lds_addr(kring[slot]) + wave * 1024);
-    dma16<Cpol::kDefault>(vcache + off, copy_off, lds_addr(vring[slot]) + wave * 1024);
-  };
+    const int shift = a.block_shift;
+    const int bs_mask = (1 << shift) - 1;
+    const int MB = a.max_blocks_per_seq;
+    const int num_blocks = (int)a.num_blocks;
+    const int32_t* table = a.block_tables + (int64_t)seq * MB;
 
-  const float kNegInf = -__builtin_inff();
-  float m_run[RB], l_lane[RB];
-  floatx4 acc[RB][CPL];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_lane[rb] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[rb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+    // every block of the context must be in the pool
+    bool bad_lane = false;
+    for (int b = lane; b < ((ctx + bs_mask) >> shift); b += kWave) {
+      const int32_t id = table[b];
+      bad_lane |= id < 0 || id >= num_blocks;
+    }
+    const bool seq_bad = __ballot(bad_lane) != 0;
 
-  // S^T = K . Q^T of a tile's two 16-token halves (raw, unscaled): lane (quarter q,
-  // column n) gets row n's scores of tokens 16 h + 4 q + i in s[rb][4 h + i]
-  auto scores = [&](const uint4* kb, float (&sv)[RB][8]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 kk[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kk[c] = kb[(16 * h + col) * SLOTS + ((4 * c + quarter) ^ col)];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const floatx4 s4 = tile_scores<BF16, 4>(kk, qa[rb]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[rb][4 * h + i] = s4[i];
-      }
-    }
-  };
-  // the causal edge: tokens past a row's position get -inf (a branch taken on the last
-  // tiles of the wave's rows only)
-  auto mask_edge = [&](int tt, float (&sv)[RB][8]) {
-    const int tok0 = tt * kPfTok;
-    if (tok0 + kPfTok - 1 > wpos_lo) {
-      keep_branch();
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) sv[rb][k] = kNegInf;
-      }
-    }
-  };
-  // the running maxima after a tile (base-2 domain; raw scores, positive scale): a row
-  // takes a new maximum only when it exceeds the old one by more than 2^8, and then
-  // its earlier terms are scaled by alpha; returns whether any row of the wave rose
-  auto maxima = [&](const float (&sv)[RB][8], float (&mnew)[RB], float (&alpha)[RB]) {
-    constexpr float kRebase = 8.f;
-    bool rise = false;
+    // this wave's rows: r = 32 wave + 16 rb + col is new token j0 + r / G with query head
+    // g G + r % G (a row past the last new token repeats token j0 and is not stored)
+    const int wrow0 = wave * 16 * RB;
+    const int wj_lo = j0 + wrow0 / G;
+    const int wj_hi = min(j0 + (wrow0 + 16 * RB - 1) / G, qlen - 1);
+    const bool wave_live = wj_lo < qlen;
+    const int wpos_lo = base_pos + min(wj_lo, qlen - 1);   // positions the wave's rows see
+    const int wpos_hi = base_pos + wj_hi;
+    const int wtiles = wave_live ? wpos_hi / kPfTok + 1 : 0;
+    const int w_end = min(wtiles, t_hi);      // the wave's tiles in this piece: [t_lo, w_end)
+
+    // queries; for a negative scale the query's sign bits are flipped (exact) so that
+    // the scale is positive and a row's largest raw score is its largest scaled one
+    // (a zero scale becomes the smallest normal float: every 2^(s * scale) is then 1 as
+    // for zero, and a masked -inf score stays -inf instead of turning NaN)
+    const float scale = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+    uint4 qa[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float a3 = hw_max3(sv[rb][0], sv[rb][1], sv[rb][2]);
-      const float b3 = hw_max3(sv[rb][3], sv[rb][4], sv[rb][5]);
-      const float c3 = hw_max3(sv[rb][6], sv[rb][7], a3);
-      float mx = hw_max(b3, c3);
-      auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = hw_max(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = hw_max(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * scale;
-      const bool up = mx > m_run[rb] + kRebase;
-      mnew[rb] = up ? mx : m_run[rb];
-      alpha[rb] = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
-      rise |= up;
+      const int r = wrow0 + rb * 16 + col;
+      const int jq = j0 + r / G < qlen ? j0 + r / G : j0;
+      const char* row = static_cast<const char*>(a.query) +
+                        ((int64_t)(q0 + jq) * H + g * G + r % G) * ROWB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 v = *reinterpret_cast<const uint4*>(row + (4 * c + quarter) * 16);
+        v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+        qa[rb][c] = v;
+      }
     }
-    return __ballot(rise) != 0;
-  };
-  // probabilities of a tile relative to mnew, as bf16 hi + lo parts (together exact
-  // to about 2^-17 of p), and their sums per lane
-  auto probs = [&](const float (&sv)[RB][8], const float (&mnew)[RB], bf16x8 (&ph)[RB],
-                   bf16x8 (&pl)[RB], float (&lsum)[RB]) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // copies: wave w brings rows 4w .. 4w + 3 of each tile, lane l row 4w + l / 16, its
+    // 16-byte piece l % 16 stored at slot (l % 16) ^ row (rows are 16 slots)
+    const int64_t row_stride = (int64_t)Hkv * ROWB;
+    const int crow = 4 * wave + quarter;
+    const uint32_t copy_off = (uint32_t)(quarter * row_stride) + (uint32_t)(((col ^ crow) & 15) * 16);
+    const char* kcache = static_cast<const char*>(a.key_cache) + g * ROWB;
+    const char* vcache = static_cast<const char*>(a.value_cache) + g * ROWB;
+    auto issue = [&](int tt, int slot) {
+      int64_t off = 0;                        // rows past the context: the pool's first rows
+      const int t0 = tt * kPfTok + 4 * wave;
+      if (tt < t_hi && t0 < ctx) {
+        const int32_t blk = uniform(((cint32*)table)[t0 >> shift]);
+        if (blk >= 0 && blk < num_blocks) off = (((int64_t)blk << shift) + (t0 & bs_mask)) * row_stride;
+      }
+      dma16<Cpol::kDefault>(kcache + off, copy_off, lds_addr(kring[slot]) + wave * 1024);
+      dma16<Cpol::kDefault>(vcache + off, copy_off, lds_addr(vring[slot]) + wave * 1024);
+    };
+
+    const float kNegInf = -__builtin_inff();
+    float m_run[RB], l_lane[RB];
+    floatx4 acc[RB][CPL];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float nref = mnew[rb] == kNegInf ? 0.f : -mnew[rb];
-      float p[8];
+      m_run[rb] = kNegInf;
+      l_lane[rb] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        p[k] = fast_exp2(fmaf(sv[rb][k], scale, nref));   // 0 for masked tokens
-        lsum[rb] += p[k];
-      }
-      // lo = p - hi as one bf16 dot product per value, (hi0, hi1) . (-1, 0) + p0: the
-      // products are exact and so is the difference, which fp32 holds.  The pair
-      // (-1, 0) is 0x0000bf80; it is moved into a scalar register here because the
-      // compiler would otherwise encode it as the inline constant -1.0, which the
-      // instruction reads as 0xbf800000, i.e. (0, -1).
-      uint32_t kneg0;
-      asm("s_mov_b32 %0, 0xbf80" : "=s"(kneg0));
-      const bf16x2 neg0 = __builtin_bit_cast(bf16x2, kneg0);
-      const bf16x2 neg1 = __builtin_bit_cast(bf16x2, 0xbf800000u);
-#pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const floatx2 pp = {p[k], p[k + 1]};
-        const bf16x2 h2 = __builtin_convertvector(pp, bf16x2);
-        const floatx2 rr = {__builtin_amdgcn_fdot2_f32_bf16(h2, neg0, p[k], false),
-                            __builtin_amdgcn_fdot2_f32_bf16(h2, neg1, p[k + 1], false)};
-        const bf16x2 l2 = __builtin_convertvector(rr, bf16x2);
-        ph[rb][k] = h2[0]; ph[rb][k + 1] = h2[1];
-        pl[rb][k] = l2[0]; pl[rb][k + 1] = l2[1];
-      }
+      for (int e = 0; e < CPL; ++e) acc[rb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-  };
-  // Value operand of output block e, dims 16 e .. 16 e + 15 (lane column n: dim
-  // 16 e + n), over the lane's eight k slots: tokens 16 h + 4 quarter + i of the tile
-  // (h < 2, i < 4), the order of the probabilities in ph / pl.  Two transposed LDS
-  // reads per block (ds_read_b64_tr_b16): within each 16-lane quarter, lane 4 i + m
-  // addresses the 8 bytes of token 16 h + 4 quarter + i's row that hold dims
-  // 16 e + 4 m .. 16 e + 4 m + 3, and the read hands lane n the bf16 of dim 16 e + n
-  // from each of the four rows, in k order.  Slot j of row r is stored at j ^ (r & 15),
-  // so the lane's byte offset is tr_base + 32 (e ^ tr_x) for h = 0, 16 rows further
-  // for h = 1.
-  const int tr_row = 4 * quarter + (col >> 2);
-  const int tr_m = col & 3;
-  const uint32_t tr_base = (uint32_t)(tr_row * ROWB + ((((tr_m >> 1) ^ tr_row) & 1) << 4) +
-                                      ((tr_m & 1) << 3));
-  const uint32_t tr_x = (uint32_t)((tr_row & 15) >> 1);
-  auto read_v = [&](int tt, const uint4* vb, int hv, bf16x8 (&bv)[4], bool zero_tail) {
-    const uint32_t base = lds_addr(vb) + tr_base;
+
+    // S^T = K . Q^T of a tile's two 16-token halves (raw, unscaled): lane (quarter q,
+    // column n) gets row n's scores of tokens 16 h + 4 q + i in s[rb][4 h + i]
+    auto scores = [&](const uint4* kb, float (&sv)[RB][8]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t o = base + (((uint32_t)(4 * hv + k) ^ tr_x) << 5);
-      const lds_s16x4* p0 = reinterpret_cast<const lds_s16x4*>((size_t)o);
-      const lds_s16x4* p1 = reinterpret_cast<const lds_s16x4*>((size_t)(o + 16 * ROWB));
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p1));
-      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      bv[k] = __builtin_bit_cast(bf16x8, both);
-    }
-    if (zero_tail && tt * kPfTok + kPfTok > ctx) {
-      // rows past the context may hold NaN: zero the lane's k slots of those tokens
-      keep_branch();
-      uint32_t mk[4];
+      for (int h = 0; h < 2; ++h) {
+        uint4 kk[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int t0 = tt * kPfTok + 16 * (d >> 1) + 4 * quarter + 2 * (d & 1);
-        mk[d] = (t0 < ctx ? 0xffffu : 0u) | (t0 + 1 < ctx ? 0xffff0000u : 0u);
+        for (int c = 0; c < 4; ++c) kk[c] = kb[(16 * h + col) * SLOTS + ((4 * c + quarter) ^ col)];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const floatx4 s4 = tile_scores<BF16, 4>(kk, qa[rb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[rb][4 * h + i] = s4[i];
+        }
       }
+    };
+    // the causal edge: tokens past a row's position get -inf (a branch taken on the last
+    // tiles of the wave's rows only)
+    auto mask_edge = [&](int tt, float (&sv)[RB][8]) {
+      const int tok0 = tt * kPfTok;
+      if (tok0 + kPfTok - 1 > wpos_lo) {
+        keep_branch();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) sv[rb][k] = kNegInf;
+        }
+      }
+    };
+    // the running maxima after a tile (base-2 domain; raw scores, positive scale): a row
+    // takes a new maximum only when it exceeds the old one by more than 2^8, and then
+    // its earlier terms are scaled by alpha; returns whether any row of the wave rose
+    auto maxima = [&](const float (&sv)[RB][8], float (&mnew)[RB], float (&alpha)[RB]) {
+      constexpr float kRebase = 8.f;
+      bool rise = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float a3 = hw_max3(sv[rb][0], sv[rb][1], sv[rb][2]);
+        const float b3 = hw_max3(sv[rb][3], sv[rb][4], sv[rb][5]);
+        const float c3 = hw_max3(sv[rb][6], sv[rb][7], a3);
+        float mx = hw_max(b3, c3);
+        auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = hw_max(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+        auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = hw_max(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * scale;
+        const bool up = mx > m_run[rb] + kRebase;
+        mnew[rb] = up ? mx : m_run[rb];
+        alpha[rb] = up ? fast_exp2(m_run[rb] - mx) : 1.f;   // 0 when m_run is -inf
+        rise |= up;
+      }
+      return __ballot(rise) != 0;
+    };
+    // probabilities of a tile relative to mnew, as bf16 hi + lo parts (together exact
+    // to about 2^-17 of p), and their sums per lane
+    auto probs = [&](const float (&sv)[RB][8], const float (&mnew)[RB], bf16x8 (&ph)[RB],
+                     bf16x8 (&pl)[RB], float (&lsum)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float nref = mnew[rb] == kNegInf ? 0.f : -mnew[rb];
+        float p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          p[k] = fast_exp2(fmaf(sv[rb][k], scale, nref));   // 0 for masked tokens
+          lsum[rb] += p[k];
+        }
+        // lo = p - hi as one bf16 dot product per value, (hi0, hi1) . (-1, 0) + p0: the
+        // products are exact and so is the difference, which fp32 holds.  The pair
+        // (-1, 0) is 0x0000bf80; it is moved into a scalar register here because the
+        // compiler would otherwise encode it as the inline constant -1.0, which the
+        // instruction reads as 0xbf800000, i.e. (0, -1).
+        uint32_t kneg0;
+        asm("s_mov_b32 %0, 0xbf80" : "=s"(kneg0));
+        const bf16x2 neg0 = __builtin_bit_cast(bf16x2, kneg0);
+        const bf16x2 neg1 = __builtin_bit_cast(bf16x2, 0xbf800000u);
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          const floatx2 pp = {p[k], p[k + 1]};
+          const bf16x2 h2 = __builtin_convertvector(pp, bf16x2);
+          const floatx2 rr = {__builtin_amdgcn_fdot2_f32_bf16(h2, neg0, p[k], false),
+                              __builtin_amdgcn_fdot2_f32_bf16(h2, neg1, p[k + 1], false)};
+          const bf16x2 l2 = __builtin_convertvector(rr, bf16x2);
+          ph[rb][k] = h2[0]; ph[rb][k + 1] = h2[1];
+          pl[rb][k] = l2[0]; pl[rb][k + 1] = l2[1];
+        }
+      }
+    };
+    // Value operand of output block e, dims 16 e .. 16 e + 15 (lane column n: dim
+    // 16 e + n), over the lane's eight k slots: tokens 16 h + 4 quarter + i of the tile
+    // (h < 2, i < 4), the order of the probabilities in ph / pl.  Two transposed LDS
+    // reads per block (ds_read_b64_tr_b16): within each 16-lane quarter, lane 4 i + m
+    // addresses the 8 bytes of token 16 h + 4 quarter + i's row that hold dims
+    // 16 e + 4 m .. 16 e + 4 m + 3, and the read hands lane n the bf16 of dim 16 e + n
+    // from each of the four rows, in k order.  Slot j of row r is stored at j ^ (r & 15),
+    // so the lane's byte offset is tr_base + 32 (e ^ tr_x) for h = 0, 16 rows further
+    // for h = 1.
+    const int tr_row = 4 * quarter + (col >> 2);
+    const int tr_m = col & 3;
+    const uint32_t tr_base = (uint32_t)(tr_row * ROWB + ((((tr_m >> 1) ^ tr_row) & 1) << 4) +
+                                        ((tr_m & 1) << 3));
+    const uint32_t tr_x = (uint32_t)((tr_row & 15) >> 1);
+    auto read_v = [&](int tt, const uint4* vb, int hv, bf16x8 (&bv)[4], bool zero_tail) {
+      const uint32_t base = lds_addr(vb) + tr_base;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint4 u = __builtin_bit_cast(uint4, bv[k]);
-        u.x &= mk[0]; u.y &= mk[1]; u.z &= mk[2]; u.w &= mk[3];
-        bv[k] = __builtin_bit_cast(bf16x8, u);
+        const uint32_t o = base + (((uint32_t)(4 * hv + k) ^ tr_x) << 5);
+        const lds_s16x4* p0 = reinterpret_cast<const lds_s16x4*>((size_t)o);
+        const lds_s16x4* p1 = reinterpret_cast<const lds_s16x4*>((size_t)(o + 16 * ROWB));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p1));
+        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bv[k] = __builtin_bit_cast(bf16x8, both);
       }
-    }
-  };
-  // acc += P . V for output blocks 4 hv .. 4 hv + 3 on v_mfma_f32_16x16x32_bf16 (hi and
-  // lo parts of P)
-  auto pv = [&](const bf16x8 (&bv)[4], int hv, const bf16x8 (&ph)[RB], const bf16x8 (&pl)[RB]) {
+      if (zero_tail && tt * kPfTok + kPfTok > ctx) {
+        // rows past the context may hold NaN: zero the lane's k slots of those tokens
+        keep_branch();
+        uint32_t mk[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 4 * hv + k;
+        for (int d = 0; d < 4; ++d) {
+          const int t0 = tt * kPfTok + 16 * (d >> 1) + 4 * quarter + 2 * (d & 1);
+          mk[d] = (t0 < ctx ? 0xffffu : 0u) | (t0 + 1 < ctx ? 0xffff0000u : 0u);
+        }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rb], bv[k], acc[rb][e], 0, 0, 0);
-        acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rb], bv[k], acc[rb][e], 0, 0, 0);
+        for (int k = 0; k < 4; ++k) {
+          uint4 u = __builtin_bit_cast(uint4, bv[k]);
+          u.x &= mk[0]; u.y &= mk[1]; u.z &= mk[2]; u.w &= mk[3];
+          bv[k] = __builtin_bit_cast(bf16x8, u);
+        }
       }
-    }
-  };
-  auto rescale = [&](const float (&alpha)[RB]) {
+    };
+    // acc += P . V for output blocks 4 hv .. 4 hv + 3 on v_mfma_f32_16x16x32_bf16 (hi and
+    // lo parts of P)
+    auto pv = [&](const bf16x8 (&bv)[4], int hv, const bf16x8 (&ph)[RB], const bf16x8 (&pl)[RB]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * hv + k;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha[rb], 4 * quarter + i);
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) acc[rb][e][i] *= ai;
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[rb], bv[k], acc[rb][e], 0, 0, 0);
+          acc[rb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[rb], bv[k], acc[rb][e], 0, 0, 0);
+        }
       }
-  };
+    };
+    auto rescale = [&](const float (&alpha)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha[rb], 4 * quarter + i);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[rb][e][i] *= ai;
+        }
+    };
 
-  // The tile loop, pipelined one tile deep.  Step t (tile t sits in ring slot
-  // t % kPfNbuf) starts with the scores of tile t in registers, masked, and the running
-  // maxima already raised for them.  It waits for this wave's copies of tile t + 1,
-  // passes one barrier (every wave's copies of tile t + 1 have landed; every wave is
-  // done with step t - 1 and so with tile t - 1), issues tile t + kPfNbuf - 1 into
-  // tile t - 1's slot, and then runs one block of straight-line work: the scores of
-  // tile t + 1 on the matrix cores beside the probabilities of tile t on the vector
-  // unit, then P.V of tile t on the matrix cores beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
-  // matrix instructions but not another wave's, so the block interleaves them
-  // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
-  // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
-  // branch).  The wave's last steps take a general path with the conditions.
-  static_assert(kPfNbuf >= 4, "tiles t and t + 1 stay staged while t + 2 lands");
-  constexpr int kAhead = (kPfNbuf - 3) * 2;   // copies of later tiles left in flight
+    // The tile loop, pipelined one tile deep.  Step t (tile t sits in ring slot
+    // t % kPfNbuf) starts with the scores of tile t in registers, masked, and the running
+    // maxima already raised for them.  It waits for this wave's copies of tile t + 1,
+    // passes one barrier (every wave's copies of tile t + 1 have landed; every wave is
+    // done with step t - 1 and so with tile t - 1), issues tile t + kPfNbuf - 1 into
+    // tile t - 1's slot, and then runs one block of straight-line work: the scores of
+    // tile t + 1 on the matrix cores beside the probabilities of tile t on the vector
+    // unit, then P.V of tile t on the matrix cores beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
+    // matrix instructions but not another wave's, so the block interleaves them
+    // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
+    // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
+    // branch).  The wave's last steps take a general path with the conditions.
+    static_assert(kPfNbuf >= 4, "tiles t and t + 1 stay staged while t + 2 lands");
+    constexpr int kAhead = (kPfNbuf - 3) * 2;   // copies of later tiles left in flight
 #pragma unroll
-  for (int i = 0; i < kPfNbuf - 1; ++i) issue(i, i);
-  float sA[RB][8], sB[RB][8];
-  wait_copies<kAhead + 2>();                  // tile 0
-  bare_barrier();
-  if (wtiles > 0) {
-    scores(kring[0], sA);
-    mask_edge(0, sA);
-    float mnew[RB], alpha[RB];
-    maxima(sA, mnew, alpha);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) m_run[rb] = mnew[rb];
-  }
-
-  auto step = [&](int tt, float (&s_cur)[RB][8], float (&s_nxt)[RB][8]) {
-    wait_copies<kAhead>();                    // tile tt + 1
+    for (int i = 0; i < kPfNbuf - 1; ++i) issue(t_lo + i, i);
+    float sA[RB][8], sB[RB][8];
+    wait_copies<kAhead + 2>();                  // tile t_lo
     bare_barrier();
-    issue(tt + kPfNbuf - 1, (tt + kPfNbuf - 1) % kPfNbuf);
-    float mnew[RB], alpha[RB], lsum[RB] = {0.f, 0.f};
-    bf16x8 ph[RB], pl[RB];
-    bool rise = false;
-    if (tt + 1 < wtiles) {
-      // tile tt is not the unit's last, so its value rows are all inside the context
-      auto block = [&](bool edge) {
-        bf16x8 w0[4], w1[4];
-        scores(kring[(tt + 1) % kPfNbuf], s_nxt);
-        read_v(tt, vring[tt % kPfNbuf], 0, w0, false);
-        probs(s_cur, m_run, ph, pl, lsum);
-        if (edge) {
-          const int tok0 = (tt + 1) * kPfTok;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-              if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) s_nxt[rb][k] = kNegInf;
-          }
-        }
-        pv(w0, 0, ph, pl);
-        read_v(tt, vring[tt % kPfNbuf], 1, w1, false);
-        pv(w1, 1, ph, pl);
-        rise = maxima(s_nxt, mnew, alpha);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // keys and the first values
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {                        // scores beside probabilities
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {                        // P.V beside the maxima
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
-        }
-      };
-      block((tt + 1) * kPfTok + kPfTok - 1 > wpos_lo);
-    } else {
-      if (tt < wtiles) {
-        bf16x8 w0[4], w1[4];
-        read_v(tt, vring[tt % kPfNbuf], 0, w0, true);
-        probs(s_cur, m_run, ph, pl, lsum);
-        pv(w0, 0, ph, pl);
-        read_v(tt, vring[tt % kPfNbuf], 1, w1, true);
-        pv(w1, 1, ph, pl);
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_lane[rb] += lsum[rb];
-    if (rise) {
-      keep_branch();
-      rescale(alpha);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l_lane[rb] *= alpha[rb];
-    }
-    if (tt + 1 < wtiles) {
+    if (w_end > t_lo) {
+      scores(kring[0], sA);
+      mask_edge(t_lo, sA);
+      float mnew[RB], alpha[RB];
+      maxima(sA, mnew, alpha);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) m_run[rb] = mnew[rb];
     }
-  };
-  for (int tt = 0; tt < ntiles; tt += 2) {
-    step(tt, sA, sB);
-    if (tt + 1 >= ntiles) break;
-    step(tt + 1, sB, sA);
-  }
-  wait_copies<0>();
-  bare_barrier();   // every wave is done with the ring, which now stages the output
-  if (!wave_live) return;
 
-  // Rows 16 rb + 4 quarter + i of the wave: sum across the four lanes of each row,
-  // normalise, and write them to the wave's 8 KiB of the ring as [row][dim] (lane n
-  // holds dims 16 e + n); read back 16 contiguous bytes per lane, so that every store
-  // covers whole rows.
-  float* stage = reinterpret_cast<float*>(wave < 4 ? &kring[0][0] : &vring[0][0]) + (wave & 3) * 16 * D;
+    auto step = [&](int lt, float (&s_cur)[RB][8], float (&s_nxt)[RB][8]) {
+      const int tt = t_lo + lt;                 // tile tt sits in ring slot lt % kPfNbuf
+      wait_copies<kAhead>();                    // tile tt + 1
+      bare_barrier();
+      issue(tt + kPfNbuf - 1, (lt + kPfNbuf - 1) % kPfNbuf);
+      float mnew[RB], alpha[RB], lsum[RB] = {0.f, 0.f};
+      bf16x8 ph[RB], pl[RB];
+      bool rise = false;
+      if (tt + 1 < w_end) {
+        // tile tt is not the wave's last, so its value rows are all inside the context
+        auto block = [&](bool edge) {
+          bf16x8 w0[4], w1[4];
+          scores(kring[(lt + 1) % kPfNbuf], s_nxt);
+          read_v(tt, vring[lt % kPfNbuf], 0, w0, false);
+          probs(s_cur, m_run, ph, pl, lsum);
+          if (edge) {
+            const int tok0 = (tt + 1) * kPfTok;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_row = sum_xor32(sum_xor16(l_lane[rb]));
+            for (int rb = 0; rb < RB; ++rb) {
+              const int prow = base_pos + min(j0 + (wrow0 + rb * 16 + col) / G, qlen - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lr = __shfl(l_row, 4 * quarter + i);
-      const float inv = seq_bad ? __builtin_nanf("") : 1.f / lr;
+              for (int k = 0; k < 8; ++k)
+                if (tok0 + 16 * (k >> 2) + 4 * quarter + (k & 3) > prow) s_nxt[rb][k] = kNegInf;
+            }
+          }
+          pv(w0, 0, ph, pl);
+          read_v(tt, vring[lt % kPfNbuf], 1, w1, false);
+          pv(w1, 1, ph, pl);
+          rise = maxima(s_nxt, mnew, alpha);
+          __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // keys and the first values
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) stage[(4 * quarter + i) * D + 16 * e + col] = acc[rb][e][i] * inv;
+          for (int i = 0; i < 16; ++i) {                        // scores beside probabilities
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {                        // P.V beside the maxima
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+          }
+        };
+        block((tt + 1) * kPfTok + kPfTok - 1 > wpos_lo);
+      } else {
+        if (tt < w_end) {
+          bf16x8 w0[4], w1[4];
+          read_v(tt, vring[lt % kPfNbuf], 0, w0, true);
+          probs(s_cur, m_run, ph, pl, lsum);
+          pv(w0, 0, ph, pl);
+          read_v(tt, vring[lt % kPfNbuf], 1, w1, true);
+          pv(w1, 1, ph, pl);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l_lane[rb] += lsum[rb];
+      if (rise) {
+        keep_branch();
+        rescale(alpha);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_lane[rb] *= alpha[rb];
+      }
+      if (tt + 1 < w_end) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) m_run[rb] = mnew[rb];
+      }
+    };
+    for (int lt = 0; t_lo + lt < t_hi; lt += 2) {
+      step(lt, sA, sB);
+      if (t_lo + lt + 1 >= t_hi) break;
+      step(lt + 1, sB, sA);
     }
-    // (a wave's LDS accesses complete in order: the reads see these writes, and the next
-    // block's writes come after these reads)
-    if (a.out_bf16) {
+    wait_copies<0>();
+    bare_barrier();   // every wave is done with the ring, which now stages the record
+
+    // The piece's record: rows 16 rb + 4 quarter + i of the wave, each normalised by its
+    // own sum (summed across the four lanes of the row), written to the wave's 8 KiB of
+    // the ring as [row][dim] (lane n holds dims 16 e + n) and read back 16 contiguous
+    // bytes per lane, so that every store covers whole rows; m and l per row.  A row
+    // without tokens in this piece has l = 0, m = -inf and o = 0.
+    const int64_t rec0 = (2 * (int64_t)item + half) * kMqPrefillUnit;
+    // (the lane index through an empty asm: the addresses below are then formed here, per
+    // piece, instead of being hoisted out of the piece loop and held in registers)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rq = ln >> 4, rc = ln & 15;
+    if (wave_live) {
+      float* stage = reinterpret_cast<float*>(wave < 4 ? &kring[0][0] : &vring[0][0]) + (wave & 3) * 16 * D;
 #pragma unroll
-      for (int k = 0; k < 16 * (D / 8) / kWave; ++k) {
-        const int c = k * kWave + lane;
-        const int i = c / (D / 8), ch = c % (D / 8);
-        const floatx4 x = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8);
-        const floatx4 y = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8 + 4);
-        const int r = wrow0 + rb * 16 + i;
-        const int jq = j0 + r / G;
-        if (jq < qlen) {
-          uint4 v;
-          v.x = f32_to_bf16_rne(x[0]) | (uint32_t)f32_to_bf16_rne(x[1]) << 16;
-          v.y = f32_to_bf16_rne(x[2]) | (uint32_t)f32_to_bf16_rne(x[3]) << 16;
-          v.z = f32_to_bf16_rne(y[0]) | (uint32_t)f32_to_bf16_rne(y[1]) << 16;
-          v.w = f32_to_bf16_rne(y[2]) | (uint32_t)f32_to_bf16_rne(y[3]) << 16;
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) +
-                                    ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 8) = v;
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l_row = sum_xor32(sum_xor16(l_lane[rb]));   // row 16 rb + col
+        if (rq == 0) {
+          a.ws_m[rec0 + wrow0 + rb * 16 + rc] = m_run[rb];
+          a.ws_l[rec0 + wrow0 + rb * 16 + rc] = l_row;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lr = __shfl(l_row, 4 * rq + i);
+          const float inv = lr > 0.f ? 1.f / lr : 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) stage[(4 * rq + i) * D + 16 * e + rc] = acc[rb][e][i] * inv;
+        }
+        // (a wave's LDS accesses complete in order: the reads see these writes, and the next
+        // block's writes come after these reads)
+#pragma unroll
+        for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
+          const int c = k * kWave + ln;
+          const int i = c / (D / 4), ch = c % (D / 4);
+          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
+          *reinterpret_cast<floatx4*>(a.ws_o + (rec0 + wrow0 + rb * 16 + i) * D + ch * 4) = v;
         }
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
-        const int c = k * kWave + lane;
-        const int i = c / (D / 4), ch = c % (D / 4);
-        const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
-        const int r = wrow0 + rb * 16 + i;
-        const int jq = j0 + r / G;
-        if (jq < qlen)
-          *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) +
-                                      ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 4) = v;
+    }
+
+    // Count the piece in: the records are released at agent scope before the count, and
+    // the piece that counts second acquires the first one's and merges the two.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int prev = __hip_atomic_fetch_add(PL.ctr + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merge_flag = prev == 1;
+      if (prev == 1) {
+        // cleared for a later launch on the same plan
+        __hip_atomic_store(PL.ctr + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
     }
-  }
+    __syncthreads();
+    if (merge_flag) {
+      // Output rows of the unit's real rows: the two records merged in piece order (so
+      // that the result does not depend on which piece came second), NI4 row pieces of
+      // 4 dims per thread and round, their loads issued before any is used.
+      constexpr int C4 = D / 4;
+      constexpr int NI4 = 4;
+      constexpr int NT = kPfWaves * kWave;
+      static_assert(kMqPrefillUnit * C4 % (NT * NI4) == 0, "whole rounds of row pieces");
+      const int64_t ra0 = 2 * (int64_t)item * kMqPrefillUnit;   // piece 0; piece 1 follows
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+#pragma unroll 1
+      for (int c0 = tid; c0 < kMqPrefillUnit * C4; c0 += NT * NI4) {
+        float ma[NI4], la[NI4], mb[NI4], lb[NI4];
+        floatx4 oa[NI4], ob[NI4];
+#pragma unroll
+        for (int u = 0; u < NI4; ++u) {
+          const int r = (c0 + u * NT) / C4, ch = (c0 + u * NT) % C4;   // in range: 8192 = 4 * 4 * 512
+          const int64_t xa = ra0 + r, xb = ra0 + kMqPrefillUnit + r;
+          ma[u] = a.ws_m[xa];
+          la[u] = a.ws_l[xa];
+          mb[u] = a.ws_m[xb];
+          lb[u] = a.ws_l[xb];
+          oa[u] = *reinterpret_cast<const floatx4*>(a.ws_o + xa * D + ch * 4);
+          ob[u] = *reinterpret_cast<const floatx4*>(a.ws_o + xb * D + ch * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < NI4; ++u) {
+          const int r = (c0 + u * NT) / C4, ch = (c0 + u * NT) % C4;
+          const int jq = j0 + r / G;
+          if (jq >= qlen) continue;
+          const float mx = fmaxf(ma[u], mb[u]);
+          const float wa = la[u] * rel_scale(ma[u], mx), wb = lb[u] * rel_scale(mb[u], mx);
+          const float inv = seq_bad ? __builtin_nanf("") : 1.f / (wa + wb);
+          float res[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) res[e] = (wa * oa[u][e] + wb * ob[u][e]) * inv;
+          const int64_t o = ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 4;
+          if (a.out_bf16) {
+            const uint2 v = make_uint2(f32_to_bf16_rne(res[0]) | (uint32_t)f32_to_bf16_rne(res[1]) << 16,
+                                       f32_to_bf16_rne(res[2]) | (uint32_t)f32_to_bf16_rne(res[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = v;
+          } else {
+            *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + o) =
+                floatx4{res[0], res[1], res[2], res[3]};
+          }
+        }
+      }
+    }
+  }   // pieces
 }
 
 template <int G>
 static hipError_t launch_prefill_g(const AttentionArgs& a, hipStream_t stream) {
-  // one workgroup per possible (unit, kv head) item, a multiple of the XCD count
-  const int64_t items = (int64_t)a.max_units * a.num_kv_heads;
-  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  // one workgroup per compute unit (a multiple of the XCD count), each taking its XCD's
+  // pieces in snake order
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int grid = max(kXcds, cus / kXcds * kXcds);
   hipLaunchKernelGGL(paged_attention_prefill_kernel<G>, dim3((unsigned)grid), dim3(kPfWaves * kWave), 0,
                      stream, a);
   return hipGetLastError();
@@ -1159,7 +1310,8 @@ __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(Atten
   const int rows = a.unit_rows;
   cint32* hdr = (cint32*)a.tile_hdr;
   cint32* qsl = (cint32*)a.query_start_loc;
-  const int64_t unit_wgs = (int64_t)a.max_units * Hkv;
+  // prefill units merge their own pieces: only the NaN rows are left to write
+  const int64_t unit_wgs = a.unit_rows == kMqPrefillUnit ? 0 : (int64_t)a.max_units * Hkv;
   if ((int64_t)blockIdx.x >= unit_wgs) {
     const int t = (int)((int64_t)blockIdx.x - unit_wgs);
     // the sequence holding token t: the last i with qsl[i] <= t (64-way search)
@@ -1271,7 +1423,8 @@ void select_multi_mode(AttentionArgs* a) {
 }
 
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {
-  const int64_t wgs = (int64_t)a.max_units * a.num_kv_heads + a.num_tokens;
+  const int64_t wgs =
+      (a.unit_rows == kMqPrefillUnit ? 0 : (int64_t)a.max_units * a.num_kv_heads) + a.num_tokens;
   if (wgs > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)wgs);
   if (a.head_dim == 64)

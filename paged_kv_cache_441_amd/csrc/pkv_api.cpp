@@ -680,6 +680,18 @@ pkv_status check_multi_shape(int32_t num_seqs, int32_t num_tokens, int32_t num_h
   if (!mul_ok(m->max_units + pkv::kMaxStreamWgs, int64_t{num_kv_heads} * m->rows,
               INT64_MAX / 1024, &m->recs))
     return PKV_ERR_INVALID_ARG;
+  if (head_dim == 128 && m->rows == pkv::kMqRowUnit) {
+    // such a batch may take the 256-row prefill units (bf16 caches): two records of
+    // kMqPrefillUnit rows per (unit, kv head) item, the items' counters and the schedule
+    int64_t items = 0, need = 0;
+    const int64_t units = (int64_t{num_tokens} * G + pkv::kMqPrefillUnit - 1) / pkv::kMqPrefillUnit +
+                          num_seqs;
+    if (!mul_ok(units, num_kv_heads, INT64_MAX / 1024, &items) ||
+        !mul_ok(items, pkv::prefill_words_per_item(), INT64_MAX / 1024, &need))
+      return PKV_ERR_INVALID_ARG;
+    need += num_seqs + 64;
+    if (need > m->recs) m->recs = need;
+  }
   m->plan_bytes = pkv::multi_plan_bytes(num_seqs, m->max_units);
   int64_t bytes = 0;
   if (!mul_ok(m->recs, int64_t{head_dim} + 2, INT64_MAX / 8, &bytes)) return PKV_ERR_INVALID_ARG;

@@ -95,6 +95,12 @@ constexpr int kMqRowUnit = kMqRowWaves * 16 * kMqRowRB;
 // workgroup each over the unit's whole causal context (no split), when such units
 // fill the GPU at least once.
 constexpr int kMqPrefillUnit = 256;
+// Prefill units split each (unit, kv head) item's context into two pieces, which write
+// (m, l, o) records of their rows; the later one merges both.  Workspace words per
+// item in each of the m and l arrays: two records' rows, and two words of schedule (m
+// array: per-XCD prefix sums and the plan's scan, at most one word per item each) or
+// one counter (l array); the caller adds the ranked sequences and a little slack.
+constexpr int64_t prefill_words_per_item() { return 2 * kMqPrefillUnit + 2; }
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels
 // (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.
