@@ -371,8 +371,10 @@ def test_gpu_bf16_output_determinism_and_relabelling():
 # small batches take them too, so that every shape and edge can be checked here.
 # ----------------------------------------------------------------------------
 
+# (context, new tokens); contexts of one 32-token tile (the last two) leave an item's
+# first context piece empty
 PREFILL_PAIRS = [(300, 300), (1000, 257), (2049, 200), (513, 129), (64, 64), (40, 33),
-                 (777, 70)]
+                 (777, 70), (20, 20), (32, 5)]
 
 
 @pytest.mark.gpu
