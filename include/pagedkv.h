@@ -378,8 +378,9 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
  * caches, head_dim 128 and R = 128, units of 256 rows are used when they give at least
  * one (unit, kv head) item per compute unit (the environment variable
  * PKV_PREFILL_MIN_ITEMS, read at each call, sets another threshold): each item's causal
- * context is then cut into two halves, computed by different workgroups and merged by
- * log-sum-exp in a fixed order by whichever finishes second.  Where the pieces fall
+ * context is then cut into pieces (two on an even batch, up to four for the units of a
+ * history much longer than the rest), computed by different workgroups and merged by
+ * log-sum-exp in a fixed order by whichever finishes last.  Where the pieces fall
  * depends on the whole batch and the GPU, so results may differ between batches in
  * the last bits of fp32; for one batch on one GPU they are deterministic.
  * Workspace: pkv_paged_attention_multi_query_workspace_bytes() bytes, no
@@ -387,8 +388,8 @@ pkv_status pkv_paged_attention_partition_fp8(void* out, const void* query,
  * 256-byte header, the unit plan (U + 1, U and num_seqs + 1 int32, each rounded up to
  * 256 bytes) and N records of (head_dim + 2) fp32: N = (1024 + U) * num_kv_heads * R,
  * or, when the 256-row units may be taken (head_dim 128, R = 128), at least
- * 514 * U' * num_kv_heads + num_seqs + 64 with U' = ceil(num_tokens * G / 256) +
- * num_seqs (two records per item, the items' counters and the schedule).
+ * 1026 * U' * num_kv_heads + num_seqs + 64 with U' = ceil(num_tokens * G / 256) +
+ * num_seqs (four records per item, the items' counters and the schedule).
  * PKV_ERR_UNSUPPORTED when U * num_kv_heads + num_tokens exceeds 2^32 / 256 - 1.
  * Device-side contract: rows of a sequence that does not fit
  * (as for the slot mapping), or that lists a block id outside [0, num_blocks) within

@@ -148,24 +148,32 @@ __device__ int block_scan(int n, F x_of, int* __restrict__ out) {
 }
 
 // ---- prefill schedule ------------------------------------------------------------------
-// Prefill units (kMqPrefillUnit rows over the unit's whole causal context) are split in
-// two pieces along the context, so that the longest units no longer set the kernel's
-// time; the piece that finishes second merges the pair.  The pieces are dealt to the
-// XCDs by (sequence, kv head) group, group k to XCD k % kXcds with the groups ranked by
-// context length (longest first): the units of one group share their tiles in one L2,
-// and every XCD gets a similar mix.  Within an XCD the groups' pieces form one list,
-// largest first (a group's units last to first); the XCD's workgroups take it in snake
-// order (round r: workgroup j takes position rW + j, or rW + W - 1 - j on odd rounds),
-// which pairs large pieces with small ones.
+// Prefill units (kMqPrefillUnit rows over the unit's whole causal context) are split
+// into pieces along the context, so that long histories no longer set the kernel's
+// time; the piece that finishes last merges them.  With P the batch's tiles per
+// workgroup (rounded up), an item of n tiles takes k = clamp(round(2 n / P), 1,
+// kPfMaxPieces) pieces: two on an even batch (about two pieces per workgroup), up to
+// kPfMaxPieces for the items of a history much longer than the rest, and one (no
+// record, no merge) for items much shorter.  The pieces are
+// dealt to the XCDs by (sequence, kv head) group, group k to XCD k % kXcds with the
+// groups ranked by context length (longest first): the units of one group share their
+// tiles in one L2, and every XCD gets a similar mix.  Within an XCD the groups' pieces
+// form one list, largest first (a group's units last to first, an item's pieces in
+// order); the XCD's workgroups take it in snake order (round r: workgroup j takes
+// position rW + j, or rW + W - 1 - j on odd rounds), which pairs large pieces with
+// small ones.
 //
 // Workspace (words; NI = max_units * num_kv_heads items, NG = num_seqs * num_kv_heads
-// groups, J = ceil(NG / kXcds)):
-//   m array: the records' m values [2 NI * kMqPrefillUnit], then the per-XCD prefix sums
+// groups, J = ceil(NG / kXcds), K = kPfMaxPieces):
+//   m array: the records' m values [K NI * kMqPrefillUnit], then the per-XCD prefix sums
 //            of pieces over its groups [kXcds][J + 1], then the ranked sequences [B],
 //            then the plan's scan [kXcds J + 1];
-//   l array: the records' l values [2 NI * kMqPrefillUnit], then one counter per item;
-//   o array: the records' rows [2 NI * kMqPrefillUnit][head_dim].
-// Record of piece h of item i, row r: (2 i + h) * kMqPrefillUnit + r.
+//   l array: the records' l values [K NI * kMqPrefillUnit], then one counter per item;
+//   o array: the records' rows [K NI * kMqPrefillUnit][head_dim].
+// Record of piece h of item i, row r: (K i + h) * kMqPrefillUnit + r.  The tile target
+// P is tile_hdr[4].
+constexpr int kPfTok = 32;   // tokens per tile of the prefill kernel
+
 struct PrefillLayout {
   int NI, NG, J;
   int* xcum;    // [kXcds][J + 1]
@@ -176,28 +184,67 @@ struct PrefillLayout {
     NI = a.max_units * a.num_kv_heads;
     NG = a.num_seqs * a.num_kv_heads;
     J = (NG + kXcds - 1) / kXcds;
-    xcum = reinterpret_cast<int*>(a.ws_m + 2 * (int64_t)NI * kMqPrefillUnit);
+    xcum = reinterpret_cast<int*>(a.ws_m + (int64_t)kPfMaxPieces * NI * kMqPrefillUnit);
     order = xcum + kXcds * (J + 1);
     scan = order + a.num_seqs;
-    ctr = reinterpret_cast<int*>(a.ws_l + 2 * (int64_t)NI * kMqPrefillUnit);
+    ctr = reinterpret_cast<int*>(a.ws_l + (int64_t)kPfMaxPieces * NI * kMqPrefillUnit);
   }
 };
+
+// Tiles of the causal context of unit `unit` of a sequence (tpb new tokens per unit).
+__device__ __forceinline__ int pf_unit_tiles(int ctx, int qlen, int unit, int tpb) {
+  const int j1 = min(qlen, (unit + 1) * tpb);
+  return (ctx - qlen + j1 + kPfTok - 1) / kPfTok;
+}
+// Pieces of an item of n tiles, P the tile target: 2 n / P rounded to the nearest (32-bit
+// arithmetic: n is below 2^26 tiles, P below 2^30).
+__device__ __forceinline__ int pf_pieces(int n, int P) {
+  const uint32_t k = (4u * (uint32_t)n + (uint32_t)P) / (2u * (uint32_t)P);
+  return min(kPfMaxPieces, max(1, (int)k));
+}
 
 // Sequences are ranked only up to this many (beyond, they keep their index order).
 constexpr int kPfRankMax = 1024;
 
 __device__ void build_prefill_schedule(const AttentionArgs& a, int U) {
   const int B = a.num_seqs, Hkv = a.num_kv_heads;
+  const int tpb = kMqPrefillUnit / (a.num_heads / Hkv);
   const PrefillLayout L(a);
   for (int i = threadIdx.x; i < U * Hkv; i += kMqPlanThreads) L.ctr[i] = 0;
-  // rank: context length, longest first (ties by index); sequences without units last
-  __shared__ int key[kPfRankMax];
-  auto key_of = [&](int i) {
-    return a.seq_unit[i + 1] > a.seq_unit[i] ? a.context_lens[i] : -1;
+  // One pass over the sequences: the rank key (context length; -1 for a sequence
+  // without units, ranked last) and the tiles of its units, summed for the tile target
+  // (all items' tiles over the launch's workgroups).  Up to kPfRankMax sequences, their
+  // lengths, rank and pieces are kept in LDS.
+  const bool small = B <= kPfRankMax;
+  __shared__ int key[kPfRankMax], qlen_s[kPfRankMax], pcs_s[kPfRankMax], ord_s[kPfRankMax];
+  __shared__ unsigned long long tiles_all;
+  if (threadIdx.x == 0) tiles_all = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < B; i += kMqPlanThreads) {
+    const int nun = a.seq_unit[i + 1] - a.seq_unit[i];
+    const int ctx = a.context_lens[i];
+    const int qlen = a.query_start_loc[i + 1] - a.query_start_loc[i];
+    unsigned long long t = 0;
+    for (int u = 0; u < nun; ++u) t += pf_unit_tiles(ctx, qlen, u, tpb);
+    if (t) atomicAdd(&tiles_all, t);
+    if (small) {
+      key[i] = nun > 0 ? ctx : -1;
+      qlen_s[i] = nun > 0 ? qlen : 0;
+    }
+  }
+  __syncthreads();
+  const int64_t all = (int64_t)tiles_all * Hkv;
+  const int P = (int)min((int64_t)1 << 30, max((int64_t)1, (all + a.grid_wgs - 1) / a.grid_wgs));
+  if (threadIdx.x == 0) a.tile_hdr[4] = P;
+  // pieces of sequence i's units (every kv head's group of it has as many)
+  auto seq_pieces = [&](int i, int ctx, int qlen) {
+    const int nun = (qlen + tpb - 1) / tpb;
+    int n = 0;
+    for (int u = 0; u < nun; ++u) n += pf_pieces(pf_unit_tiles(ctx, qlen, u, tpb), P);
+    return n;
   };
-  if (B <= kPfRankMax) {
-    for (int i = threadIdx.x; i < B; i += kMqPlanThreads) key[i] = key_of(i);
-    __syncthreads();
+  // rank: longest first (ties by index)
+  if (small) {
     for (int i = threadIdx.x; i < B; i += kMqPlanThreads) {
       const int ki = key[i];
       int r = 0;
@@ -206,20 +253,25 @@ __device__ void build_prefill_schedule(const AttentionArgs& a, int U) {
         r += kj > ki || (kj == ki && j < i);
       }
       L.order[r] = i;
+      ord_s[r] = i;
+      pcs_s[i] = ki < 0 ? 0 : seq_pieces(i, ki, qlen_s[i]);
     }
   } else {
     for (int i = threadIdx.x; i < B; i += kMqPlanThreads) L.order[i] = i;
   }
   __syncthreads();
   // per XCD x: exclusive prefix sums over its groups k = kXcds j + x (rank k / Hkv, kv
-  // head k % Hkv) of their pieces, two per unit; entry J is the XCD's total.  One scan
-  // over t = x J + j (XCD-major), then each XCD's sums less its first.
+  // head k % Hkv) of their pieces; entry J is the XCD's total.  One scan over
+  // t = x J + j (XCD-major), then each XCD's sums less its first.
   const int J = L.J;
   auto pieces_of = [&](int t) {
     const int k = kXcds * (t % J) + t / J;
     if (k >= L.NG) return 0;
-    const int i = L.order[k / Hkv];
-    return 2 * (a.seq_unit[i + 1] - a.seq_unit[i]);
+    if (small) return pcs_s[ord_s[k / Hkv]];
+    const int i = k / Hkv;   // index order beyond kPfRankMax sequences
+    const int nun = a.seq_unit[i + 1] - a.seq_unit[i];
+    if (nun == 0) return 0;
+    return seq_pieces(i, a.context_lens[i], a.query_start_loc[i + 1] - a.query_start_loc[i]);
   };
   const int tot = block_scan<kMqPlanThreads>(kXcds * J, pieces_of, L.scan);
   if (threadIdx.x == 0) L.scan[kXcds * J] = tot;
@@ -744,7 +796,6 @@ void paged_attention_multi_kernel(AttentionArgs a) {
 // Rows of a sequence whose context lists a block id outside the pool are all NaN
 // (each piece checks the whole table row first).
 constexpr int kPfWaves = kMqPrefillUnit / 32;   // 8 waves, 32 rows each
-constexpr int kPfTok = 32;                       // tokens per tile
 #ifndef PKV_PREFILL_NBUF
 #define PKV_PREFILL_NBUF 4
 #endif
@@ -797,6 +848,7 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
   const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
   cint32* xc = (cint32*)PL.xcum + xcd * (PL.J + 1);
   const int nx = xc[PL.J];
+  const int P = ((cint32*)a.tile_hdr)[4];   // the schedule's tile target
   for (int rnd = 0;; ++rnd) {
     const int pos = rnd * W + ((rnd & 1) ? W - 1 - jw : jw);   // snake order
     if (pos >= nx) break;
@@ -809,23 +861,29 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     const int grp = kXcds * glo + xcd;
     const int seq = order[grp / Hkv];
     const int g = grp % Hkv;
-    const int in_grp = pos - xc[glo];
     const int u0 = seq_unit[seq];
     const int nun = seq_unit[seq + 1] - u0;   // > 0 for a group with pieces
-    const int unit = nun - 1 - (in_grp >> 1);  // a group's units last to first (largest first)
-    const int half = in_grp & 1;               // first or second half of the unit's context
-    const int item = u0 * Hkv + g * nun + unit;
-    const int j0 = unit * TPB;                 // first new token of the unit
     cint32* qsl = (cint32*)a.query_start_loc;
     const int q0 = qsl[seq];
     const int qlen = qsl[seq + 1] - q0;
     const int ctx = ((cint32*)a.context_lens)[seq];
+    // the group's units last to first (largest first), each an item of npc pieces
+    int in_grp = pos - xc[glo];
+    int unit = nun - 1, ntiles = 0, npc = 1;
+    for (;; --unit) {
+      ntiles = pf_unit_tiles(ctx, qlen, unit, TPB);
+      npc = pf_pieces(ntiles, P);
+      if (in_grp < npc || unit == 0) break;
+      in_grp -= npc;
+    }
+    const int piece = in_grp;                  // < npc
+    const int item = u0 * Hkv + g * nun + unit;
+    const int j0 = unit * TPB;                 // first new token of the unit
     const int j1 = min(qlen, j0 + TPB);
     const int base_pos = ctx - qlen;          // position of new token 0
-    const int ntiles = (base_pos + j1 + kPfTok - 1) / kPfTok;
     // this piece's tiles
-    const int t_lo = half ? ntiles / 2 : 0;
-    const int t_hi = half ? ntiles : ntiles / 2;
+    const int t_lo = ntiles * piece / npc;        // below 2^28: 32-bit arithmetic
+    const int t_hi = ntiles * (piece + 1) / npc;
     __syncthreads();   // the previous piece is done with the ring and merge_flag
 
     const int shift = a.block_shift;
@@ -834,9 +892,12 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     const int num_blocks = (int)a.num_blocks;
     const int32_t* table = a.block_tables + (int64_t)seq * MB;
 
-    // every block of the context must be in the pool
+    // every block of the context must be in the pool (the lane index through an empty
+    // asm keeps the lane's address part from being hoisted out of the piece loop)
+    int bl = lane;
+    asm volatile("" : "+v"(bl));
     bool bad_lane = false;
-    for (int b = lane; b < ((ctx + bs_mask) >> shift); b += kWave) {
+    for (int b = bl; b < ((ctx + bs_mask) >> shift); b += kWave) {
       const int32_t id = table[b];
       bad_lane |= id < 0 || id >= num_blocks;
     }
@@ -1162,12 +1223,14 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     wait_copies<0>();
     bare_barrier();   // every wave is done with the ring, which now stages the record
 
-    // The piece's record: rows 16 rb + 4 quarter + i of the wave, each normalised by its
-    // own sum (summed across the four lanes of the row), written to the wave's 8 KiB of
-    // the ring as [row][dim] (lane n holds dims 16 e + n) and read back 16 contiguous
-    // bytes per lane, so that every store covers whole rows; m and l per row.  A row
-    // without tokens in this piece has l = 0, m = -inf and o = 0.
-    const int64_t rec0 = (2 * (int64_t)item + half) * kMqPrefillUnit;
+    // Rows 16 rb + 4 quarter + i of the wave, each normalised by its own sum (summed
+    // across the four lanes of the row), are written to the wave's 8 KiB of the ring as
+    // [row][dim] (lane n holds dims 16 e + n) and read back 16 contiguous bytes per lane,
+    // so that every store covers whole rows: the output rows of an item of one piece,
+    // else the piece's record (with m and l per row; a row without tokens in this piece
+    // has l = 0, m = -inf and o = 0).
+    const bool direct = npc == 1;
+    const int64_t rec0 = ((int64_t)item * kPfMaxPieces + piece) * kMqPrefillUnit;
     // (the lane index through an empty asm: the addresses below are then formed here, per
     // piece, instead of being hoisted out of the piece loop and held in registers)
     int ln = lane;
@@ -1178,38 +1241,72 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float l_row = sum_xor32(sum_xor16(l_lane[rb]));   // row 16 rb + col
-        if (rq == 0) {
+        if (!direct && rq == 0) {
           a.ws_m[rec0 + wrow0 + rb * 16 + rc] = m_run[rb];
           a.ws_l[rec0 + wrow0 + rb * 16 + rc] = l_row;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float lr = __shfl(l_row, 4 * rq + i);
-          const float inv = lr > 0.f ? 1.f / lr : 0.f;
+          const float inv = direct ? (seq_bad ? __builtin_nanf("") : 1.f / lr) : (lr > 0.f ? 1.f / lr : 0.f);
 #pragma unroll
           for (int e = 0; e < CPL; ++e) stage[(4 * rq + i) * D + 16 * e + rc] = acc[rb][e][i] * inv;
         }
         // (a wave's LDS accesses complete in order: the reads see these writes, and the next
         // block's writes come after these reads)
+        if (!direct) {
 #pragma unroll
-        for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
-          const int c = k * kWave + ln;
-          const int i = c / (D / 4), ch = c % (D / 4);
-          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
-          *reinterpret_cast<floatx4*>(a.ws_o + (rec0 + wrow0 + rb * 16 + i) * D + ch * 4) = v;
+          for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
+            const int c = k * kWave + ln;
+            const int i = c / (D / 4), ch = c % (D / 4);
+            const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
+            *reinterpret_cast<floatx4*>(a.ws_o + (rec0 + wrow0 + rb * 16 + i) * D + ch * 4) = v;
+          }
+        } else if (a.out_bf16) {
+#pragma unroll
+          for (int k = 0; k < 16 * (D / 8) / kWave; ++k) {
+            const int c = k * kWave + ln;
+            const int i = c / (D / 8), ch = c % (D / 8);
+            const floatx4 x = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8);
+            const floatx4 y = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 8 + 4);
+            const int r = wrow0 + rb * 16 + i;
+            const int jq = j0 + r / G;
+            if (jq < qlen) {
+              uint4 v;
+              v.x = f32_to_bf16_rne(x[0]) | (uint32_t)f32_to_bf16_rne(x[1]) << 16;
+              v.y = f32_to_bf16_rne(x[2]) | (uint32_t)f32_to_bf16_rne(x[3]) << 16;
+              v.z = f32_to_bf16_rne(y[0]) | (uint32_t)f32_to_bf16_rne(y[1]) << 16;
+              v.w = f32_to_bf16_rne(y[2]) | (uint32_t)f32_to_bf16_rne(y[3]) << 16;
+              *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) +
+                                        ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 8) = v;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 16 * (D / 4) / kWave; ++k) {
+            const int c = k * kWave + ln;
+            const int i = c / (D / 4), ch = c % (D / 4);
+            const floatx4 v = *reinterpret_cast<const floatx4*>(stage + i * D + ch * 4);
+            const int r = wrow0 + rb * 16 + i;
+            const int jq = j0 + r / G;
+            if (jq < qlen)
+              *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) +
+                                          ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 4) = v;
+          }
         }
       }
     }
+    if (direct) continue;
 
     // Count the piece in: the records are released at agent scope before the count, and
-    // the piece that counts second acquires the first one's and merges the two.
+    // the piece that counts last acquires the others' and merges them.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const int prev = __hip_atomic_fetch_add(PL.ctr + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      merge_flag = prev == 1;
-      if (prev == 1) {
+      merge_flag = prev == npc - 1;
+      if (prev == npc - 1) {
         // cleared for a later launch on the same plan
         __hip_atomic_store(PL.ctr + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1217,42 +1314,58 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     }
     __syncthreads();
     if (merge_flag) {
-      // Output rows of the unit's real rows: the two records merged in piece order (so
-      // that the result does not depend on which piece came second), NI4 row pieces of
-      // 4 dims per thread and round, their loads issued before any is used.
+      // Output rows of the unit's real rows: the records merged in piece order (so that
+      // the result does not depend on which piece came last), NI4 row pieces of 4 dims
+      // per thread and round.
       constexpr int C4 = D / 4;
       constexpr int NI4 = 4;
       constexpr int NT = kPfWaves * kWave;
       static_assert(kMqPrefillUnit * C4 % (NT * NI4) == 0, "whole rounds of row pieces");
-      const int64_t ra0 = 2 * (int64_t)item * kMqPrefillUnit;   // piece 0; piece 1 follows
+      const int64_t rb0 = (int64_t)item * kPfMaxPieces * kMqPrefillUnit;   // piece h at + h * rows
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
 #pragma unroll 1
       for (int c0 = tid; c0 < kMqPrefillUnit * C4; c0 += NT * NI4) {
-        float ma[NI4], la[NI4], mb[NI4], lb[NI4];
-        floatx4 oa[NI4], ob[NI4];
+        float mx[NI4], wsum[NI4];
+        floatx4 osum[NI4];
 #pragma unroll
         for (int u = 0; u < NI4; ++u) {
-          const int r = (c0 + u * NT) / C4, ch = (c0 + u * NT) % C4;   // in range: 8192 = 4 * 4 * 512
-          const int64_t xa = ra0 + r, xb = ra0 + kMqPrefillUnit + r;
-          ma[u] = a.ws_m[xa];
-          la[u] = a.ws_l[xa];
-          mb[u] = a.ws_m[xb];
-          lb[u] = a.ws_l[xb];
-          oa[u] = *reinterpret_cast<const floatx4*>(a.ws_o + xa * D + ch * 4);
-          ob[u] = *reinterpret_cast<const floatx4*>(a.ws_o + xb * D + ch * 4);
+          mx[u] = -__builtin_inff();
+          wsum[u] = 0.f;
+          osum[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int h = 0; h < npc; ++h) {
+#pragma unroll
+          for (int u = 0; u < NI4; ++u)
+            mx[u] = fmaxf(mx[u], a.ws_m[rb0 + h * kMqPrefillUnit + (c0 + u * NT) / C4]);
+        }
+        for (int h = 0; h < npc; ++h) {
+          float m[NI4], l[NI4];
+          floatx4 o[NI4];
+#pragma unroll
+          for (int u = 0; u < NI4; ++u) {
+            const int64_t x = rb0 + h * kMqPrefillUnit + (c0 + u * NT) / C4;
+            m[u] = a.ws_m[x];
+            l[u] = a.ws_l[x];
+            o[u] = *reinterpret_cast<const floatx4*>(a.ws_o + x * D + ((c0 + u * NT) % C4) * 4);
+          }
+#pragma unroll
+          for (int u = 0; u < NI4; ++u) {
+            const float w = l[u] * rel_scale(m[u], mx[u]);
+            wsum[u] += w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) osum[u][e] = fmaf(w, o[u][e], osum[u][e]);
+          }
         }
 #pragma unroll
         for (int u = 0; u < NI4; ++u) {
           const int r = (c0 + u * NT) / C4, ch = (c0 + u * NT) % C4;
           const int jq = j0 + r / G;
           if (jq >= qlen) continue;
-          const float mx = fmaxf(ma[u], mb[u]);
-          const float wa = la[u] * rel_scale(ma[u], mx), wb = lb[u] * rel_scale(mb[u], mx);
-          const float inv = seq_bad ? __builtin_nanf("") : 1.f / (wa + wb);
+          const float inv = seq_bad ? __builtin_nanf("") : 1.f / wsum[u];
           float res[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) res[e] = (wa * oa[u][e] + wb * ob[u][e]) * inv;
+          for (int e = 0; e < 4; ++e) res[e] = osum[u][e] * inv;
           const int64_t o = ((int64_t)(q0 + jq) * H + g * G + r % G) * D + ch * 4;
           if (a.out_bf16) {
             const uint2 v = make_uint2(f32_to_bf16_rne(res[0]) | (uint32_t)f32_to_bf16_rne(res[1]) << 16,
@@ -1270,13 +1383,11 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
 
 template <int G>
 static hipError_t launch_prefill_g(const AttentionArgs& a, hipStream_t stream) {
-  // one workgroup per compute unit (a multiple of the XCD count), each taking its XCD's
-  // pieces in snake order
-  const int cus = device_cus();
-  if (cus <= 0) return hipErrorInvalidDevice;
-  const int grid = max(kXcds, cus / kXcds * kXcds);
-  hipLaunchKernelGGL(paged_attention_prefill_kernel<G>, dim3((unsigned)grid), dim3(kPfWaves * kWave), 0,
-                     stream, a);
+  // a.grid_wgs workgroups (one per compute unit, a multiple of the XCD count; the plan's
+  // tile target is per workgroup), each taking its XCD's pieces in snake order
+  if (a.grid_wgs < kXcds || a.grid_wgs % kXcds != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(paged_attention_prefill_kernel<G>, dim3((unsigned)a.grid_wgs),
+                     dim3(kPfWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1420,6 +1531,8 @@ void select_multi_mode(AttentionArgs* a) {
   if (units * a->num_kv_heads < min_items) return;
   a->unit_rows = kMqPrefillUnit;
   a->max_units = (int)(units + a->num_seqs);   // within the arrays sized for row-split units
+  // one workgroup per compute unit, a multiple of the XCD count
+  a->grid_wgs = max(kXcds, device_cus() / kXcds * kXcds);
 }
 
 hipError_t launch_attention_multi_reduce(const AttentionArgs& a, hipStream_t stream) {

@@ -681,8 +681,8 @@ pkv_status check_multi_shape(int32_t num_seqs, int32_t num_tokens, int32_t num_h
               INT64_MAX / 1024, &m->recs))
     return PKV_ERR_INVALID_ARG;
   if (head_dim == 128 && m->rows == pkv::kMqRowUnit) {
-    // such a batch may take the 256-row prefill units (bf16 caches): two records of
-    // kMqPrefillUnit rows per (unit, kv head) item, the items' counters and the schedule
+    // such a batch may take the 256-row prefill units (bf16 caches): kPfMaxPieces records
+    // of kMqPrefillUnit rows per (unit, kv head) item, the items' counters and the schedule
     int64_t items = 0, need = 0;
     const int64_t units = (int64_t{num_tokens} * G + pkv::kMqPrefillUnit - 1) / pkv::kMqPrefillUnit +
                           num_seqs;

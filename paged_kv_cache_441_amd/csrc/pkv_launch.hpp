@@ -76,6 +76,7 @@ struct AttentionArgs {
   int num_tokens;
   int unit_rows;            // 16, 32, kMqRowUnit or kMqPrefillUnit rows per unit
   int max_units;            // capacity of the unit arrays
+  int grid_wgs;             // prefill units: workgroups of the launch (a multiple of 8)
   int* unit_seq;            // [max_units] sequence of each unit
   int* seq_unit;            // [num_seqs + 1] first unit of each sequence
 };
@@ -95,12 +96,14 @@ constexpr int kMqRowUnit = kMqRowWaves * 16 * kMqRowRB;
 // workgroup each over the unit's whole causal context (no split), when such units
 // fill the GPU at least once.
 constexpr int kMqPrefillUnit = 256;
-// Prefill units split each (unit, kv head) item's context into two pieces, which write
-// (m, l, o) records of their rows; the later one merges both.  Workspace words per
-// item in each of the m and l arrays: two records' rows, and two words of schedule (m
-// array: per-XCD prefix sums and the plan's scan, at most one word per item each) or
-// one counter (l array); the caller adds the ranked sequences and a little slack.
-constexpr int64_t prefill_words_per_item() { return 2 * kMqPrefillUnit + 2; }
+// Prefill units split each (unit, kv head) item's context into up to kPfMaxPieces
+// pieces, which write (m, l, o) records of their rows; the last one merges them.
+// Workspace words per item in each of the m and l arrays: kPfMaxPieces records' rows,
+// and two words of schedule (m array: per-XCD prefix sums and the plan's scan, at most
+// one word per item each) or one counter (l array); the caller adds the ranked
+// sequences and a little slack.
+constexpr int kPfMaxPieces = 4;
+constexpr int64_t prefill_words_per_item() { return kPfMaxPieces * kMqPrefillUnit + 2; }
 
 // Balanced mode: at most this many workgroups per kv-head group, so segment labels
 // (workgroup + sequence) stay below kMaxStreamWgs + num_seqs.
