@@ -13,8 +13,9 @@ sequences (tokens) per second.
 
 A config named *_fp8 runs the same workload over E4M3 (8-bit float) caches: the
 prologue quantises the new rows, attention decodes the codes (balanced split only).
-The configs spec_verify and chunked_prefill run steps with several new tokens per
-sequence (slot mapping, cache write, causal multi-token attention).
+The configs spec_verify, chunked_prefill and chunked_prefill_skewed run steps with
+several new tokens per sequence (slot mapping, cache write, causal multi-token
+attention).
 
 Prints one JSON line.  The fp64 CPU oracle is timed on the same batch (all of it
 unless --cpu-sample-seqs says otherwise), split by sequence over k worker processes
@@ -704,7 +705,7 @@ def bench_multi(args) -> int:
     gbs = kv_bytes / attn_s / 1e9
     tflops = flops / attn_s / 1e12
     pv_tflops = pv_flops / attn_s / 1e12
-    hbm_bound = args.config != "chunked_prefill"
+    hbm_bound = not args.config.startswith("chunked_prefill")
     # The matrix-bound case is priced on the algorithmic causal flops (Q.K^T and P.V)
     # against the dense peak of the operand type: bf16 caches run both products on bf16
     # matrix instructions (P.V as two products, P split into bf16 hi + lo parts, not

@@ -255,7 +255,8 @@ def test_gpu_slots_and_write_exact(name):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name", ["tiny_multi", "spec_verify", "chunked_prefill"])
+@pytest.mark.parametrize("name", ["tiny_multi", "spec_verify", "chunked_prefill",
+                                  "chunked_prefill_skewed"])
 def test_gpu_attention_matches_oracle(name):
     pkv = _gpu()
     b = make_multi_config(name, device="cuda")

@@ -355,7 +355,9 @@ def build_multi_batch(spec: ConfigSpec, context_lens: Sequence[int], query_lens:
 #  - spec_verify: 256 sequences with lognormal contexts (as llama3_8b), each verifying
 #    5 speculated tokens (the draft length on the pages);
 #  - chunked_prefill: a 2048-token step budget (the pages' default) spent on 4
-#    prompts' 512-token chunks, after histories uniform in [0, 8192].
+#    prompts' 512-token chunks, after histories uniform in [0, 8192];
+#  - chunked_prefill_skewed: the same budget with one long history beside short ones
+#    (16000 and 3 x 1000 tokens), where a few long units would set the step's time.
 MULTI_CONFIGS = {
     "tiny_multi": (ConfigSpec("tiny_multi", 4, 4, 4, 64, 16, 64, "f32", 100,
                               ("fixed", (17, 33, 64, 100)), 5), ("fixed", (1, 5, 16, 40))),
@@ -364,6 +366,11 @@ MULTI_CONFIGS = {
     "chunked_prefill": (ConfigSpec("chunked_prefill", 4, 32, 8, 128, 16, 16384, "bf16",
                                    8192 + 512, ("uniform", 512, 8192 + 512), 7,
                                    partition_size=PARTITION_BALANCED), ("fixed_all", 512)),
+    "chunked_prefill_skewed": (ConfigSpec("chunked_prefill_skewed", 4, 32, 8, 128, 16, 16384,
+                                          "bf16", 16000 + 512,
+                                          ("fixed", (16512, 1512, 1512, 1512)), 7,
+                                          partition_size=PARTITION_BALANCED),
+                               ("fixed_all", 512)),
 }
 
 
