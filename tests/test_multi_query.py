@@ -404,6 +404,27 @@ def test_gpu_prefill_units_match_oracle(monkeypatch, G, Hkv, BS):
 
 
 @pytest.mark.gpu
+def test_gpu_prefill_units_many_sequences(monkeypatch):
+    # more sequences than the plan ranks (they keep their index order), each with 32-40
+    # new tokens so that the batch takes the 256-row units (at least 128 rows per sequence)
+    pkv = _gpu()
+    monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
+    rng = np.random.default_rng(11)
+    B = 1030
+    ql = rng.integers(32, 41, size=B)
+    ctx = ql + rng.integers(0, 260, size=B)
+    b = build_multi_batch(_spec(D=128, G=4, Hkv=2, BS=16, NB=16384, dtype="bf16", seed=12),
+                          ctx.tolist(), ql.tolist(), device="cuda")
+    _, _, _, out = _gpu_step(pkv, b)
+    ref = _oracle_subset(b, range(B))
+    assert len(ref) == int(ql.sum())
+    err = _max_err(out, ref)
+    print(f"prefill units, {B} sequences: max err {err:.3e} over {len(ref)} tokens")
+    assert np.isfinite(out.float().cpu().numpy()).all()
+    assert err <= ATOL
+
+
+@pytest.mark.gpu
 def test_gpu_prefill_units_invalid_inputs_give_nan_rows_only(monkeypatch):
     pkv = _gpu()
     monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
