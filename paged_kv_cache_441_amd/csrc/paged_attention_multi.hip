@@ -876,7 +876,9 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
       if (in_grp < npc || unit == 0) break;
       in_grp -= npc;
     }
-    const int piece = in_grp;                  // < npc
+    // (the plan counted the same pieces; the clamp keeps a record inside its item's
+    // kPfMaxPieces even if it had not)
+    const int piece = min(in_grp, npc - 1);
     const int item = u0 * Hkv + g * nun + unit;
     const int j0 = unit * TPB;                 // first new token of the unit
     const int j1 = min(qlen, j0 + TPB);
@@ -1120,15 +1122,16 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
         }
     };
 
-    // The tile loop, pipelined one tile deep.  Step t (tile t sits in ring slot
-    // t % kPfNbuf) starts with the scores of tile t in registers, masked, and the running
-    // maxima already raised for them.  It waits for this wave's copies of tile t + 1,
-    // passes one barrier (every wave's copies of tile t + 1 have landed; every wave is
-    // done with step t - 1 and so with tile t - 1), issues tile t + kPfNbuf - 1 into
-    // tile t - 1's slot, and then runs one block of straight-line work: the scores of
-    // tile t + 1 on the matrix cores beside the probabilities of tile t on the vector
-    // unit, then P.V of tile t on the matrix cores beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
-    // matrix instructions but not another wave's, so the block interleaves them
+    // The tile loop over the piece's tiles [t_lo, t_hi), pipelined one tile deep.  Step t
+    // (tile t sits in ring slot (t - t_lo) % kPfNbuf) starts with the scores of tile t in
+    // registers, masked, and the running maxima already raised for them.  It waits for
+    // this wave's copies of tile t + 1, passes one barrier (every wave's copies of tile
+    // t + 1 have landed; every wave is done with step t - 1 and so with tile t - 1),
+    // issues tile t + kPfNbuf - 1 into tile t - 1's slot, and then runs one block of
+    // straight-line work: the scores of tile t + 1 on the matrix cores beside the
+    // probabilities of tile t on the vector unit, then P.V of tile t on the matrix cores
+    // beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
+    // matrix instructions far better than another wave's, so the block interleaves them
     // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
     // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
     // branch).  The wave's last steps take a general path with the conditions.
