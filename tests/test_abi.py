@@ -80,6 +80,31 @@ def test_partition_size_constants():
     assert f"#define PKV_ABI_VERSION {_lib.ABI_VERSION}" in text
 
 
+def _ws_multi(B, T, H, Hkv, D):
+    # the header's formula: 256-byte header, the unit plan (U + 1, U and B + 1 int32, each
+    # rounded to 256 bytes), N records of (D + 2) fp32
+    r256 = lambda b: (b + 255) // 256 * 256
+    G = H // Hkv
+    rows_total = T * G
+    R = 128 if D == 128 and rows_total >= 128 * B else (32 if rows_total > 16 * B else 16)
+    U = -(-T // (R // G)) + B
+    N = (1024 + U) * Hkv * R
+    if D == 128 and R == 128:   # the 256-row prefill units may be taken
+        U2 = -(-T * G // 256) + B
+        N = max(N, 1026 * U2 * Hkv + B + 64)
+    return 256 + r256((U + 1) * 4) + r256(U * 4) + r256((B + 1) * 4) + N * (D + 2) * 4
+
+
+def test_multi_query_workspace_bytes_formula(lib):
+    f = lib.pkv_paged_attention_multi_query_workspace_bytes
+    # speculated tokens (32-row units), chunked prefill (128-row units, prefill sizing),
+    # one token per sequence (16-row units), fp32-sized 64-element heads
+    for B, T, H, Hkv, D in [(256, 1280, 32, 8, 128), (4, 2048, 32, 8, 128), (64, 64, 32, 8, 128),
+                            (4, 2048, 8, 2, 64), (1030, 37026, 8, 2, 128)]:
+        assert f(B, T, H, Hkv, D, 16, 1024) == _ws_multi(B, T, H, Hkv, D), (B, T, H, Hkv, D)
+    assert f(-1, 10, 32, 8, 128, 16, 64) == 0
+
+
 def test_workspace_bytes_formula(lib):
     # plan (256 + roundup256(B*NP*16)) + B * H * NP * (D + 2) * 4, NP = ceil(MB*BS/P)
     assert lib.pkv_paged_attention_workspace_bytes(256, 32, 128, 16, 512, 512) == _ws(256, 32, 128, 16)
