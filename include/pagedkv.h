@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7   /* 7: multi-token workspace sized for context pieces */
 
 /* partition_size values with a name (see above) */
 #define PKV_PARTITION_DEFAULT 0            /* fixed partitions of 512 tokens */

@@ -94,7 +94,7 @@ SIGNATURES = {
                                                    _vp, _sz, _vp]),
 }
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lock = threading.Lock()
 _lib = None
