@@ -367,9 +367,10 @@ def test_gpu_bf16_output_determinism_and_relabelling():
 
 
 # ----------------------------------------------------------------------------
-# long prompts with bf16 caches: the prefill units (256 rows, one workgroup each, no
-# split).  The library takes them when they fill the GPU; PKV_PREFILL_MIN_ITEMS=0 makes
-# small batches take them too, so that every shape and edge can be checked here.
+# long prompts with bf16 caches: the prefill units (256 rows, their causal contexts in
+# up to four pieces merged in the kernel).  The library takes them when they fill the
+# GPU; PKV_PREFILL_MIN_ITEMS=0 makes small batches take them too, so that every shape and
+# edge can be checked here.
 # ----------------------------------------------------------------------------
 
 # (context, new tokens); contexts of one 32-token tile (the last two) leave an item's
@@ -401,6 +402,31 @@ def test_gpu_prefill_units_match_oracle(monkeypatch, G, Hkv, BS):
     monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", str(1 << 40))
     rows = _gpu_step(pkv, b)[3]
     assert (rows - out).abs().max().item() <= 2e-5
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_units_reuse_one_workspace(monkeypatch):
+    # the pieces' counters live in the workspace: a garbage-filled workspace used for
+    # three calls in a row gives the same bits every time, and the same as a fresh one
+    pkv = _gpu()
+    monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
+    ctx = [c for c, _ in PREFILL_PAIRS]
+    ql = [q for _, q in PREFILL_PAIRS]
+    b = build_multi_batch(_spec(D=128, G=4, Hkv=2, BS=16, NB=1024, dtype="bf16", seed=5),
+                          ctx, ql, device="cuda")
+    _, kc, vc, fresh = _gpu_step(pkv, b)
+    bt, cl, qsl = _meta(b)
+    T = int(b.extra["query_start_loc"][-1])
+    H, Hkv, D = b.spec.num_heads, b.spec.num_kv_heads, b.spec.head_dim
+    ws = torch.full((pkv.multi_query_workspace_bytes(b.num_seqs, T, H, Hkv, D, 16, bt.shape[1]),),
+                    0xAB, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        outs.append(pkv.paged_attention_multi_query(b.query, kc, vc, bt, cl, qsl, b.scale,
+                                                    workspace=ws))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int32), fresh.view(torch.int32))
 
 
 @pytest.mark.gpu
