@@ -1417,7 +1417,7 @@ template <int D>
 __global__ __launch_bounds__(256) void paged_attention_multi_reduce_kernel(AttentionArgs a) {
   constexpr int C4 = D / 4;              // float4 pieces of a row
   constexpr int KS = 2;                  // shares whose records are loaded together
-  constexpr int NI = 4;                  // items per thread whose records are loaded together
+  constexpr int NI = 2;                  // items per thread whose records are loaded together
   const int H = a.num_heads;
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
