@@ -59,28 +59,43 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
 }
 
-// The E4M3 cache write: the codes of x / scale (the quotient rounded to fp32, then to
-// E4M3) for 16 consecutive elements of a row, read as fp32 or bfloat16; 16 bytes out.
-template <bool kBf16In>
-__device__ __forceinline__ uint4 quantize16(const void* src, int64_t group, float scale) {
-  float x[16];
-  if constexpr (kBf16In) {
-    const uint4* p = static_cast<const uint4*>(src) + 2 * group;
-    unpack_chunk<BF16>(p[0], x);
-    unpack_chunk<BF16>(p[1], x + 8);
-  } else {
-    const uint4* p = static_cast<const uint4*>(src) + 4 * group;
+// The input words behind cache piece g of a row (16 bytes of cache): one chunk for a
+// bit copy (quant 0), four fp32 chunks (quant 1) or two bfloat16 chunks (quant 2).
+__device__ __forceinline__ void load_piece(const void* src, int64_t g, int quant,
+                                           uint4 (&w)[4]) {
+  const uint4* p = static_cast<const uint4*>(src);
+  if (quant == 0) {
+    w[0] = p[g];
+  } else if (quant == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unpack_chunk<F32>(p[i], x + 4 * i);
+    for (int i = 0; i < 4; ++i) w[i] = p[4 * g + i];
+  } else {
+    w[0] = p[2 * g];
+    w[1] = p[2 * g + 1];
   }
-  uint32_t w[4];
+}
+
+// The cache piece for loaded input words: the words themselves (quant 0), else the
+// E4M3 codes of x / scale (the quotient rounded to fp32, then to E4M3) for their 16
+// elements.
+__device__ __forceinline__ uint4 encode_piece(const uint4 (&w)[4], int quant, float scale) {
+  if (quant == 0) return w[0];
+  float x[16];
+  if (quant == 2) {
+    unpack_chunk<BF16>(w[0], x);
+    unpack_chunk<BF16>(w[1], x + 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_chunk<F32>(w[i], x + 4 * i);
+  }
+  uint32_t c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    w[i] = 0;
+    c[i] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(__fdiv_rn(x[4 * i + j], scale)) << (8 * j);
+    for (int j = 0; j < 4; ++j) c[i] |= e4m3_encode(__fdiv_rn(x[4 * i + j], scale)) << (8 * j);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(c[0], c[1], c[2], c[3]);
 }
 
 // Token t's K and V rows into cache slot `slot`, each cache row `chunks` 16-byte
@@ -93,14 +108,10 @@ __device__ __forceinline__ void store_token(const void* key, const void* value, 
   for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
     const bool is_k = c < chunks;
     const int64_t cc = is_k ? c : c - chunks;
-    const void* in = is_k ? key : value;
-    uint4* out = static_cast<uint4*>(is_k ? key_cache : value_cache) + dst + cc;
-    if (quant == 0)
-      *out = static_cast<const uint4*>(in)[src + cc];
-    else if (quant == 1)
-      *out = quantize16<false>(in, src + cc, is_k ? k_scale : v_scale);
-    else
-      *out = quantize16<true>(in, src + cc, is_k ? k_scale : v_scale);
+    uint4 w[4];
+    load_piece(is_k ? key : value, src + cc, quant, w);
+    static_cast<uint4*>(is_k ? key_cache : value_cache)[dst + cc] =
+        encode_piece(w, quant, is_k ? k_scale : v_scale);
   }
 }
 
@@ -138,12 +149,30 @@ __global__ __launch_bounds__(kPrologueThreads) void decode_prologue_kernel(
     return;
   }
   const int t = blockIdx.x - 1;
+  const int chunks = chunks_per_row;
+  if (2 * chunks > kPrologueThreads) {
+    const int32_t slot = slot_of(block_tables, context_lens, t, max_blocks_per_seq, block_shift,
+                                 num_blocks);
+    if (threadIdx.x == 0) slot_mapping[t] = slot;
+    if (slot < 0) return;
+    store_token(key, value, key_cache, value_cache, t, slot, chunks, quant, k_scale, v_scale);
+    return;
+  }
+  // Both rows fit one pass: each thread loads its input piece before the slot is
+  // known (the input does not depend on it), so these loads are in flight during the
+  // two dependent reads of the slot computation.
+  const int c = threadIdx.x;
+  const bool live = c < 2 * chunks;
+  const bool is_k = c < chunks;
+  const int64_t cc = is_k ? c : c - chunks;
+  uint4 w[4];
+  if (live) load_piece(is_k ? key : value, (int64_t)t * chunks + cc, quant, w);
   const int32_t slot = slot_of(block_tables, context_lens, t, max_blocks_per_seq, block_shift,
                                num_blocks);
   if (threadIdx.x == 0) slot_mapping[t] = slot;
-  if (slot < 0) return;
-  store_token(key, value, key_cache, value_cache, t, slot, chunks_per_row, quant, k_scale,
-              v_scale);
+  if (slot < 0 || !live) return;
+  static_cast<uint4*>(is_k ? key_cache : value_cache)[(int64_t)slot * chunks + cc] =
+      encode_piece(w, quant, is_k ? k_scale : v_scale);
 }
 
 hipError_t launch_decode_prologue(const int32_t* block_tables, const int32_t* context_lens,
