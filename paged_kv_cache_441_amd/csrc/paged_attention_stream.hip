@@ -419,19 +419,42 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     } else {
       s4 = tile_scores<QT, QKC>(qa, kk);
     }
-    const bool live = col < ntok;
     float sc[4];
-    int gkey[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = live ? s4[j] * a.scale_log2 : kNegInf;
-      gkey[j] = row_max_key<TOK>(float_key(sc[j]));
+    for (int j = 0; j < 4; ++j) sc[j] = s4[j] * a.scale_log2;
+    if (TOK < 16 || !full) {
+      // columns past the context (and past TOK) take no weight: a branch taken on a
+      // sequence's last tile only
+      keep_branch();
+      const bool live = col < ntok;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[j] = live ? sc[j] : kNegInf;
     }
+    // the tile's maximum key of head h, read from lane hlane(h) of gkey[hreg(h)]
+    int gkey[4];
+    if constexpr (kValuQK) {
+      // every quarter holds the same scores: one 16-lane reduction per head
+#pragma unroll
+      for (int j = 0; j < G; ++j) gkey[j] = row_max_key<TOK>(float_key(sc[j]));
+    } else {
+      // head 4 r + j sits in quarter r of sc[j].  Two half-wave swaps and one row swap
+      // transpose the 16-lane rows against the four registers, putting head 4 r + q in
+      // quarter q of one register, so that one 16-lane reduction serves four heads
+      const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[0]),
+                                                        __float_as_uint(sc[2]), false, false);
+      const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[1]),
+                                                        __float_as_uint(sc[3]), false, false);
+      const auto t = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+      gkey[0] = row_max_key<TOK>(float_key(__uint_as_float(t[0])));
+      if constexpr (kQuarters > 1) gkey[1] = row_max_key<TOK>(float_key(__uint_as_float(t[1])));
+    }
+    auto hreg = [](int h) { return kValuQK ? h : h >> 2; };
+    auto hlane = [](int h) { return kValuQK ? 0 : 16 * (h & 3); };
     float alpha[G];
     bool rebase = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float gm = key_float(__builtin_amdgcn_readlane(gkey[h & 3], 16 * (h >> 2)));
+      const float gm = key_float(__builtin_amdgcn_readlane(gkey[hreg(h)], hlane(h)));
       const bool up = gm > m_run[h] + kRebase;   // uniform across the wave
       const float mn = up ? gm : m_run[h];
       alpha[h] = up ? fast_exp2(m_run[h] - mn) : 1.f;
@@ -449,7 +472,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         arow = quarter == 0 ? alpha[j] : alpha[(4 + j) % G];
       }
       sc[j] = fast_exp2(sc[j] - mrow);
-      l_lane[j] = rebase ? l_lane[j] * arow + sc[j] : l_lane[j] + sc[j];
+      l_lane[j] = fmaf(l_lane[j], arow, sc[j]);   // arow is 1 unless the row rebased
     }
     if (rebase) {
       if constexpr (kMfmaPV) {
@@ -483,49 +506,96 @@ void paged_attention_stream_kernel(AttentionArgs a) {
       // tokens' value columns col * 8 + e for output block e, packed from four token
       // rows (a column permutation, undone at the store).  P is split into hi + lo
       // bf16 terms, together exact to about 2^-17 of p; E4M3 values are exact in bf16.
-      floatx4 pa = {0.f, 0.f, 0.f, 0.f};
-      if (col < G) pa = *reinterpret_cast<const floatx4*>(&p_lds[wave][col % G][4 * quarter]);
+      // rows col >= G read head col % G's probabilities: finite values whose products
+      // land in padding rows of the accumulators, which are never stored
+      const floatx4 pa = *reinterpret_cast<const floatx4*>(&p_lds[wave][col % G][4 * quarter]);
       const floatx2 p01 = {pa[0], pa[1]}, p23 = {pa[2], pa[3]};
       const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
       const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
-      const bf16x2 l01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, floatx2), bf16x2);
-      const bf16x2 l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, floatx2), bf16x2);
-      const bf16x4 ahi = {h01[0], h01[1], h23[0], h23[1]};
-      const bf16x4 alo = {l01[0], l01[1], l23[0], l23[1]};
-      // bf16 caches: one k = 32 operand, the lane's four hi terms then its four lo
-      // terms, against its four value rows twice (the order of k is free); E4M3
-      // caches, whose kernel runs four waves per SIMD, keep two k = 16 products,
-      // which need fewer registers
-      const bf16x8 ahl = {h01[0], h01[1], h23[0], h23[1], l01[0], l01[1], l23[0], l23[1]};
-      uint32_t wv[4][4];   // token 4 quarter + s: value columns col * 8 .. col * 8 + 7
+      // lo = p - hi as one bf16 dot product per value, (hi0, hi1) . (-1, 0) + p0 and
+      // (hi0, hi1) . (0, -1) + p1: the products and the difference are exact in fp32.
+      // The pair (-1, 0) is the word 0x0000bf80; it is set in a scalar register because
+      // the compiler would encode it as the inline constant -1.0, i.e. 0xbf800000.
+      uint32_t kneg0;
+      asm("s_mov_b32 %0, 0xbf80" : "=s"(kneg0));
+      const bf16x2 neg0 = __builtin_bit_cast(bf16x2, kneg0);
+      const bf16x2 neg1 = __builtin_bit_cast(bf16x2, 0xbf800000u);
+      const floatx2 r01 = {__builtin_amdgcn_fdot2_f32_bf16(h01, neg0, pa[0], false),
+                           __builtin_amdgcn_fdot2_f32_bf16(h01, neg1, pa[1], false)};
+      const floatx2 r23 = {__builtin_amdgcn_fdot2_f32_bf16(h23, neg0, pa[2], false),
+                           __builtin_amdgcn_fdot2_f32_bf16(h23, neg1, pa[3], false)};
+      const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
+      const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
+      const bf16x4 ahi = __builtin_bit_cast(
+          bf16x4, make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)));
+      const bf16x4 alo = __builtin_bit_cast(
+          bf16x4, make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)));
+      if constexpr (kF8) {
+        // E4M3 caches, whose kernel runs four waves per SIMD, keep two k = 16 products,
+        // which need fewer registers.  cw[s]: the codes of token 4 quarter + s, value
+        // columns col * 8 .. col * 8 + 7 (4 per word)
+        uint32_t cw[4][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int n = 4 * quarter + s;
-        const bool dead = !full && n >= ntok;   // rows past the context may hold NaN
-        if constexpr (kF8) {
+        for (int s = 0; s < 4; ++s) {
+          const int n = 4 * quarter + s;
           const int slot = (wave * NCH + (col >> 1)) ^ St::swz(n);
           const uint2 c8 = reinterpret_cast<const uint2*>(vb)[2 * (n * St::kSlots + slot) + (col & 1)];
-          const uint2 b0 = e4m3x4_to_bf16(dead ? 0u : c8.x), b1 = e4m3x4_to_bf16(dead ? 0u : c8.y);
-          wv[s][0] = b0.x; wv[s][1] = b0.y; wv[s][2] = b1.x; wv[s][3] = b1.y;
-        } else {
-          const uint4 c = vb[n * St::kSlots + ((wave * NCH + col) ^ St::swz(n))];
-          wv[s][0] = dead ? 0u : c.x; wv[s][1] = dead ? 0u : c.y;
-          wv[s][2] = dead ? 0u : c.z; wv[s][3] = dead ? 0u : c.w;
+          cw[s][0] = c8.x;
+          cw[s][1] = c8.y;
         }
-      }
+        if (!full) {
+          // rows past the context may hold NaN codes: zero them (a sequence's last tile)
+          keep_branch();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // column col * 8 + e: the low bf16 of word e / 2 for even e, else the high
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint2 bq;
-        bq.x = __builtin_amdgcn_perm(wv[1][e >> 1], wv[0][e >> 1], sel);
-        bq.y = __builtin_amdgcn_perm(wv[3][e >> 1], wv[2][e >> 1], sel);
-        if constexpr (kF8) {
-          const bf16x4 b = __builtin_bit_cast(bf16x4, bq);
+          for (int s = 0; s < 4; ++s)
+            if (4 * quarter + s >= ntok) cw[s][0] = cw[s][1] = 0u;
+        }
+        // column pair k (columns 2k, 2k + 1): one byte permute per token pair puts the
+        // pair's codes side by side (t0 2k, t1 2k, t0 2k+1, t1 2k+1); each half of that
+        // word converts to one column's bf16 pair of those tokens
+        uint32_t xw[4][2];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t sel = (k & 1) ? 0x07030602u : 0x05010400u;
+          xw[k][0] = __builtin_amdgcn_perm(cw[1][k >> 1], cw[0][k >> 1], sel);
+          xw[k][1] = __builtin_amdgcn_perm(cw[3][k >> 1], cw[2][k >> 1], sel);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t x01 = xw[e >> 1][0], x23 = xw[e >> 1][1];
+          const bf16x2 c01 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.f, true)
+                                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.f, false);
+          const bf16x2 c23 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.f, true)
+                                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.f, false);
+          const bf16x4 b = {c01[0], c01[1], c23[0], c23[1]};
           acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, b, acc8[e], 0, 0, 0);
           acc8[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, b, acc8[e], 0, 0, 0);
-        } else {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(bq.x, bq.y, bq.x, bq.y));
+        }
+      } else {
+        // bf16 caches: one k = 32 operand, the lane's four hi terms then its four lo
+        // terms, against its four value rows twice (the order of k is free)
+        const bf16x8 ahl = {h01[0], h01[1], h23[0], h23[1], l01[0], l01[1], l23[0], l23[1]};
+        uint32_t wv[4][4];   // token 4 quarter + s: value columns col * 8 .. col * 8 + 7
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int n = 4 * quarter + s;
+          const uint4 c = vb[n * St::kSlots + ((wave * NCH + col) ^ St::swz(n))];
+          wv[s][0] = c.x; wv[s][1] = c.y; wv[s][2] = c.z; wv[s][3] = c.w;
+        }
+        if (!full) {
+          // rows past the context may hold NaN: zero them (a sequence's last tile only)
+          keep_branch();
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (4 * quarter + s >= ntok) wv[s][0] = wv[s][1] = wv[s][2] = wv[s][3] = 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // column col * 8 + e: the low bf16 of word e / 2 for even e, else the high
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t bx = __builtin_amdgcn_perm(wv[1][e >> 1], wv[0][e >> 1], sel);
+          const uint32_t by = __builtin_amdgcn_perm(wv[3][e >> 1], wv[2][e >> 1], sel);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(bx, by, bx, by));
           acc8[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahl, b, acc8[e], 0, 0, 0);
         }
       }
