@@ -1130,11 +1130,12 @@ void paged_attention_prefill_kernel(AttentionArgs a) {
     // issues tile t + kPfNbuf - 1 into tile t - 1's slot, and then runs one block of
     // straight-line work: the scores of tile t + 1 on the matrix cores beside the
     // probabilities of tile t on the vector unit, then P.V of tile t on the matrix cores
-    // beside the maxima of tile t + 1.  On gfx950 a wave's vector work overlaps its own
-    // matrix instructions far better than another wave's, so the block interleaves them
-    // (scheduling groups of one matrix instruction and a few vector ones).  A rise of a
-    // row maximum for tile t + 1 rescales the accumulators after P.V of tile t (a rare
-    // branch).  The wave's last steps take a general path with the conditions.
+    // beside the maxima of tile t + 1.  The block asks the compiler for that interleave
+    // (scheduling groups of one matrix instruction and a few vector ones); the compiled
+    // loop keeps the score products together all the same, and the order written out with
+    // scheduling fences ran slower than the compiler's.  A rise of a row maximum for tile
+    // t + 1 rescales the accumulators after P.V of tile t (a rare branch).  The wave's
+    // last steps take a general path with the conditions.
     static_assert(kPfNbuf >= 4, "tiles t and t + 1 stay staged while t + 2 lands");
     constexpr int kAhead = (kPfNbuf - 3) * 2;   // copies of later tiles left in flight
 #pragma unroll
