@@ -432,14 +432,17 @@ void paged_attention_stream_kernel(AttentionArgs a) {
     }
     // the tile's maximum key of head h, read from lane hlane(h) of gkey[hreg(h)]
     int gkey[4];
-    if constexpr (kValuQK) {
-      // every quarter holds the same scores: one 16-lane reduction per head
+    if constexpr (kValuQK || !kF8) {
+      // one 16-lane reduction per register: head j (kValuQK: every quarter holds the same
+      // scores), else head 4 r + j in quarter r of sc[j]
 #pragma unroll
-      for (int j = 0; j < G; ++j) gkey[j] = row_max_key<TOK>(float_key(sc[j]));
+      for (int j = 0; j < (kValuQK ? G : 4); ++j) gkey[j] = row_max_key<TOK>(float_key(sc[j]));
     } else {
-      // head 4 r + j sits in quarter r of sc[j].  Two half-wave swaps and one row swap
-      // transpose the 16-lane rows against the four registers, putting head 4 r + q in
-      // quarter q of one register, so that one 16-lane reduction serves four heads
+      // E4M3 caches: head 4 r + j sits in quarter r of sc[j].  Two half-wave swaps and
+      // one row swap transpose the 16-lane rows against the four registers, putting head
+      // 4 r + q in quarter q of one register, so that one 16-lane reduction serves four
+      // heads (fewer vector instructions; on bf16 caches the one longer dependent chain
+      // made the kernel 1.5 us slower, so they keep four reductions)
       const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[0]),
                                                         __float_as_uint(sc[2]), false, false);
       const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[1]),
@@ -448,8 +451,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
       gkey[0] = row_max_key<TOK>(float_key(__uint_as_float(t[0])));
       if constexpr (kQuarters > 1) gkey[1] = row_max_key<TOK>(float_key(__uint_as_float(t[1])));
     }
-    auto hreg = [](int h) { return kValuQK ? h : h >> 2; };
-    auto hlane = [](int h) { return kValuQK ? 0 : 16 * (h & 3); };
+    auto hreg = [](int h) { return kValuQK ? h : !kF8 ? (h & 3) : h >> 2; };
+    auto hlane = [](int h) { return kValuQK ? 0 : !kF8 ? 16 * (h >> 2) : 16 * (h & 3); };
     float alpha[G];
     bool rebase = false;
 #pragma unroll
