@@ -143,6 +143,39 @@ def test_boundary_contexts(D, G, BS, dtype):
         assert err <= ATOL
 
 
+def _grow_history_keys(b, per_token=1.0 / 32.0):
+    """Scale each history token's key row by 1 + j * per_token (j its position), in the
+    batch's own cache, so that the scores' running maximum keeps rising along a context."""
+    BS = b.spec.block_size
+    NB = b.key_cache.shape[0]
+    factor = torch.ones(NB * BS, dtype=torch.float32)
+    for i, ctx in enumerate(b.context_lens):
+        j = np.arange(max(int(ctx) - 1, 0))
+        rows = b.block_tables[i, j // BS].astype(np.int64) * BS + j % BS
+        factor[torch.as_tensor(rows)] = torch.as_tensor(1.0 + j * per_token, dtype=torch.float32)
+    kc = b.key_cache.view(NB * BS, -1)
+    kc.copy_((kc.float() * factor.to(kc.device)[:, None]).to(kc.dtype))
+
+
+@pytest.mark.parametrize("mode", ["fixed", "balanced", "per_head"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rising_maxima_rescale_the_earlier_terms(mode, dtype):
+    # With N(0, 1) data a row's running maximum settles on a segment's first tile, so the
+    # rescale of what was summed so far (taken when a tile's maximum exceeds the running
+    # one by more than 2^8) almost only ever scales zeros.  Here the history keys grow
+    # along each context (up to about 94 times), the maximum keeps rising, and the
+    # rescale of non-zero sums and accumulators runs on many tiles.
+    b = build_batch(spec_of(NB=2048, dtype=dtype), [40, 700, 1500, 3000], device="cuda")
+    _grow_history_keys(b)
+    P = {"fixed": 512, "balanced": BAL, "per_head": 512}[mode]
+    _, _, _, out = run_step(b, partition_size=P, per_head=mode == "per_head")
+    ref = oracle_outputs(b)
+    err = max_err(out, ref)
+    print(f"rising maxima {dtype} {mode}: max |gpu - oracle| = {err:.3e}")
+    assert np.isfinite(out.cpu().numpy()).all()
+    assert err <= ATOL
+
+
 def test_partitioned_equals_single_partition():
     b = build_batch(spec_of(NB=4096), [1, 100, 600, 1500, 5000, 9000], device="cuda")
     MB = b.max_blocks_per_seq

@@ -405,6 +405,44 @@ def test_gpu_prefill_units_match_oracle(monkeypatch, G, Hkv, BS):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("units", ["head", "prefill"])
+def test_gpu_rising_maxima_rescale_the_earlier_terms(monkeypatch, units):
+    # keys that grow along each context (history rows in the cache and the new tokens'
+    # rows alike, up to about 94 times) keep a row's running maximum rising, so the
+    # rescale of non-zero sums and accumulators runs on many tiles; every token compared
+    pkv = _gpu()
+    if units == "head":
+        ctx, ql = [300, 2100, 700], [5, 5, 3]
+    else:
+        monkeypatch.setenv("PKV_PREFILL_MIN_ITEMS", "0")
+        ctx, ql = [1500, 3000], [512, 256]
+    b = build_multi_batch(_spec(D=128, G=4, Hkv=2, BS=16, NB=1024, dtype="bf16", seed=9),
+                          ctx, ql, device="cuda")
+    BS = b.spec.block_size
+    NB = b.key_cache.shape[0]
+    qsl = b.extra["query_start_loc"]
+    factor = torch.ones(NB * BS, dtype=torch.float32)
+    new_factor = torch.ones(int(qsl[-1]), dtype=torch.float32)
+    for i, (c, q) in enumerate(zip(ctx, ql)):
+        j = np.arange(c - q)
+        rows = b.block_tables[i, j // BS].astype(np.int64) * BS + j % BS
+        factor[torch.as_tensor(rows)] = torch.as_tensor(1.0 + j / 32.0, dtype=torch.float32)
+        new_factor[qsl[i]:qsl[i + 1]] = torch.as_tensor(1.0 + np.arange(c - q, c) / 32.0,
+                                                         dtype=torch.float32)
+    kc = b.key_cache.view(NB * BS, -1)
+    kc.copy_((kc.float() * factor.to(kc.device)[:, None]).to(kc.dtype))
+    k = b.key.view(int(qsl[-1]), -1)
+    k.copy_((k.float() * new_factor.to(k.device)[:, None]).to(k.dtype))
+    _, _, _, out = _gpu_step(pkv, b)
+    ref = _oracle_subset(b, range(len(ctx)))
+    assert len(ref) == sum(ql)
+    err = _max_err(out, ref)
+    print(f"rising maxima, {units} units: max err {err:.3e} over {len(ref)} tokens")
+    assert np.isfinite(out.float().cpu().numpy()).all()
+    assert err <= ATOL
+
+
+@pytest.mark.gpu
 def test_gpu_prefill_units_reuse_one_workspace(monkeypatch):
     # the pieces' counters live in the workspace: a garbage-filled workspace used for
     # three calls in a row gives the same bits every time, and the same as a fresh one
