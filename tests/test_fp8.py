@@ -339,6 +339,37 @@ def test_gpu_fp8_boundary_contexts(D, G, Hkv, BS):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("Hkv", [2, 8, 16])
+def test_gpu_fp8_fused_prologue_fp32_inputs_equal_separate_write(Hkv):
+    # fp32 new rows (bf16 values plus a small fp32 offset, so that the quotient's
+    # rounding sees fp32 bits): the fused prologue's E4M3 codes equal the separate
+    # write's bit for bit, for code rows of 256 B, 1 KiB and 2 KiB
+    from workloads import build_fp8_batch
+    pkv = _gpu()
+    b = build_fp8_batch(_spec(D=128, G=4, Hkv=Hkv, BS=16, NB=2048), [1, 17, 600, 3000],
+                        device="cuda")
+    gen = torch.Generator(device="cpu").manual_seed(Hkv)
+    k32 = b.key.float() + 1e-3 * torch.randn(b.key.shape, generator=gen).to("cuda")
+    v32 = b.value.float() + 1e-3 * torch.randn(b.value.shape, generator=gen).to("cuda")
+    bt, cl = _meta(b)
+    ks, vs = b.extra["k_scale"], b.extra["v_scale"]
+    NB, BS = b.key_cache.shape[:2]
+    kc1, vc1 = b.key_cache.clone(), b.value_cache.clone()
+    s1 = pkv.slot_mapping(bt, cl, BS, NB)
+    pkv.kv_cache_write_fp8(k32, v32, kc1, vc1, s1, ks, vs)
+    kc2, vc2 = b.key_cache.clone(), b.value_cache.clone()
+    ws = pkv.alloc_workspace(b.query, bt, BS, pkv.PARTITION_BALANCED)
+    s2 = pkv.decode_prologue_fp8(bt, cl, k32, v32, kc2, vc2, ws, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    # and the codes are the oracle's
+    want_k = of8.quantize(k32.double().cpu().numpy(), ks)
+    got_k = kc2.view(NB * BS, -1)[s1.long()].cpu().numpy().reshape(want_k.shape)
+    assert (got_k == want_k).all()
+
+
+@pytest.mark.gpu
 def test_gpu_fp8_staged_and_fused_equal_decode_bitwise_and_bf16_output():
     from workloads import build_fp8_batch
     pkv = _gpu()

@@ -418,10 +418,13 @@ def test_plan_with_many_sequences():
 
 
 @pytest.mark.parametrize("nseq", [5, 600])
-def test_prologue_equals_separate_calls(nseq):
+@pytest.mark.parametrize("Hkv", [2, 8, 16])
+def test_prologue_equals_separate_calls(nseq, Hkv):
+    # token rows of 512 B, 2 KiB and 4 KiB: the prologue's workgroup of 256 threads
+    # stores a token's K and V rows in one pass up to 2 KiB, in several beyond
     rng = np.random.default_rng(nseq)
     ctx = rng.integers(1, 4000, size=nseq)
-    b = build_batch(spec_of(NB=nseq * 260 + 64), ctx, device="cuda")
+    b = build_batch(spec_of(Hkv=Hkv, NB=nseq * 260 + 64), ctx, device="cuda")
     bt, cl = device_meta(b)
     NB, BS = b.key_cache.shape[:2]
     P = 512
