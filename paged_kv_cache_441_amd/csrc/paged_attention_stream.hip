@@ -55,6 +55,25 @@
 
 namespace pkv {
 
+// Segment-end stores (outputs and records), non-temporal when NT: each is written once
+// while the tile copies stream, and the merge reads the records back from memory.  With
+// bf16 caches that took the Llama-3-8B-shaped batch from 260.1-261.8 to 255.7-257.4 us
+// and the long-context batch in 512-token partitions from 434-435 to 410 us; with E4M3
+// caches it cost 1-2 us, so they keep ordinary stores.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT, typename V>
+__device__ __forceinline__ void st_seg(V* p, V v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st_seg4(float* p, float x, float y, float z, float w) {
+  st_seg<NT>(reinterpret_cast<floatx4*>(p), floatx4{x, y, z, w});
+}
+
 
 #ifndef PKV_STREAM_NBUF
 #define PKV_STREAM_NBUF 2
@@ -102,6 +121,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
   constexpr int TOK = kTileTokens;
   using St = Stage<T, D, HW, TOK>;
   constexpr bool kF8 = T::kElemBytes == 1;  // E4M3 caches, bfloat16 queries
+  constexpr bool kNtSeg = !kF8;              // non-temporal segment-end stores
   using QT = typename std::conditional<kF8, BF16, T>::type;   // query and MFMA operand type
   constexpr int EB = T::kElemBytes;
   constexpr int QEB = QT::kElemBytes;
@@ -664,22 +684,22 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         if (whole) {
           const int64_t orow = ((int64_t)cc.s * H + g * G + h) * D + col * 8;
           if (a.out_bf16) {
-            uint4 v;
-            v.x = f32_to_bf16_rne(res[0]) | (uint32_t)f32_to_bf16_rne(res[1]) << 16;
-            v.y = f32_to_bf16_rne(res[2]) | (uint32_t)f32_to_bf16_rne(res[3]) << 16;
-            v.z = f32_to_bf16_rne(res[4]) | (uint32_t)f32_to_bf16_rne(res[5]) << 16;
-            v.w = f32_to_bf16_rne(res[6]) | (uint32_t)f32_to_bf16_rne(res[7]) << 16;
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = v;
+            const u32x4 v = {
+                f32_to_bf16_rne(res[0]) | (uint32_t)f32_to_bf16_rne(res[1]) << 16,
+                f32_to_bf16_rne(res[2]) | (uint32_t)f32_to_bf16_rne(res[3]) << 16,
+                f32_to_bf16_rne(res[4]) | (uint32_t)f32_to_bf16_rne(res[5]) << 16,
+                f32_to_bf16_rne(res[6]) | (uint32_t)f32_to_bf16_rne(res[7]) << 16};
+            st_seg<kNtSeg>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + orow), v);
           } else {
             float* o = static_cast<float*>(a.out) + orow;
-            *reinterpret_cast<float4*>(o) = make_float4(res[0], res[1], res[2], res[3]);
-            *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
+            st_seg4<kNtSeg>(o, res[0], res[1], res[2], res[3]);
+            st_seg4<kNtSeg>(o + 4, res[4], res[5], res[6], res[7]);
           }
         } else {
           const int64_t rec = rec_of(h);
           float* o = a.ws_o + rec * D + col * 8;
-          *reinterpret_cast<float4*>(o) = make_float4(res[0], res[1], res[2], res[3]);
-          *reinterpret_cast<float4*>(o + 4) = make_float4(res[4], res[5], res[6], res[7]);
+          st_seg4<kNtSeg>(o, res[0], res[1], res[2], res[3]);
+          st_seg4<kNtSeg>(o + 4, res[4], res[5], res[6], res[7]);
           if (col == 0) {
             a.ws_m[rec] = mh;
             a.ws_l[rec] = lh;
@@ -715,10 +735,10 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
           for (int e = 0; e < EPL; e += 4) {
-            uint2 v;
-            v.x = f32_to_bf16_rne(res[h][e]) | (uint32_t)f32_to_bf16_rne(res[h][e + 1]) << 16;
-            v.y = f32_to_bf16_rne(res[h][e + 2]) | (uint32_t)f32_to_bf16_rne(res[h][e + 3]) << 16;
-            *reinterpret_cast<uint2*>(o + h * D + e) = v;
+            const u32x2 v = {
+                f32_to_bf16_rne(res[h][e]) | (uint32_t)f32_to_bf16_rne(res[h][e + 1]) << 16,
+                f32_to_bf16_rne(res[h][e + 2]) | (uint32_t)f32_to_bf16_rne(res[h][e + 3]) << 16};
+            st_seg<kNtSeg>(reinterpret_cast<u32x2*>(o + h * D + e), v);
           }
       } else {
         float* o = static_cast<float*>(a.out) + row0 * D + li * EPL;
@@ -726,8 +746,8 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
           for (int e = 0; e < EPL; e += 4)
-            *reinterpret_cast<float4*>(o + h * D + e) =
-                make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
+            st_seg4<kNtSeg>(o + h * D + e, res[h][e], res[h][e + 1], res[h][e + 2],
+                            res[h][e + 3]);
       }
     } else {
 #pragma unroll
@@ -735,8 +755,7 @@ void paged_attention_stream_kernel(AttentionArgs a) {
         float* o = a.ws_o + rec_of(h) * D + li * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
-          *reinterpret_cast<float4*>(o + e) =
-              make_float4(res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
+          st_seg4<kNtSeg>(o + e, res[h][e], res[h][e + 1], res[h][e + 2], res[h][e + 3]);
       }
       if (lane < G) {
         // lane h < G writes head h's (m, l); m_run and l_head are uniform
