@@ -122,15 +122,22 @@ __device__ __forceinline__ int xcd_local_share(int block, int nwg) {
   return (block % kXcds) * (nwg / kXcds) + block / kXcds;
 }
 
+// floor(n / d) for 0 <= n and 0 < d < 2^31: 32-bit division when n fits (the common
+// case; a 64-bit division is a long instruction sequence on the GPU).
+__device__ __forceinline__ int64_t div_floor(int64_t n, int d) {
+  if (n <= 0xffffffffll) return (int64_t)((uint32_t)n / (uint32_t)d);
+  return n / d;
+}
+
 // Share w of the tile list is [floor(w * total / nwg), floor((w + 1) * total / nwg)).
 // The share holding tile j:
 __device__ __forceinline__ int share_of(int64_t j, int nwg, int total) {
-  return (int)(((j + 1) * nwg - 1) / total);
+  return (int)div_floor((j + 1) * nwg - 1, total);
 }
 
 // Shares are empty when there are more workgroups than tiles.
 __device__ __forceinline__ bool share_nonempty(int w, int nwg, int total) {
-  return (int64_t)w * total / nwg < (int64_t)(w + 1) * total / nwg;
+  return div_floor((int64_t)w * total, nwg) < div_floor((int64_t)(w + 1) * total, nwg);
 }
 
 // Compute units of the current device, looked up once per device.
